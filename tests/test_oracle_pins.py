@@ -1,0 +1,437 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each check is a value the
+pages print (tests/golden/), a closed form, an invariant of the method, a
+special case that reduces to a library routine, or brute force in plain
+Python integers/floats on tiny inputs.  The last block plants plausible
+mistakes into a copy of the oracle and shows that a pin catches each one.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.pdq_oracle as O
+from w8a8_int8_quantized_absmax_amd import synth
+
+F32 = np.float32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the LLM.int8() page
+# ---------------------------------------------------------------------------
+
+def check_worked_row(oracle=O):
+    g = golden("llm_int8_worked_example.json")
+    row = np.array([g["row_regular_values"]], F32)
+    q, s = oracle.quantize_rows_absmax(row)
+    # C_x = 2 (printed); S = C_x / 127
+    assert s[0] == F32(g["row_absmax_C_x"]) / F32(127)
+    # absmax formula: round(127 * x / C_x) = round(127, -63.5, 63.5)
+    expect = [round(127 * v / g["row_absmax_C_x"]) for v in g["row_regular_values"]]
+    assert expect == [127, -64, 64]
+    assert q.tolist() == [expect]
+
+
+def test_worked_example_row_scale():
+    check_worked_row()
+
+
+def test_worked_example_weight_column():
+    g = golden("llm_int8_worked_example.json")
+    col = np.array([g["weight_column_values"]], F32)  # one output channel of W
+    wq, sw, colsum = O.quantize_weight(col)
+    assert sw[0] == F32(g["weight_column_absmax"]) / F32(127)
+    assert wq.tolist() == [[-64, 0, -127, -64]]
+    assert colsum.tolist() == [-255]
+
+
+def outlier_fixture():
+    """The figure's 3-row X: 1st and 3rd columns are the printed outliers.
+
+    Row 1's regular values are the printed [2, -1, 1]; the regular values
+    of rows 2 and 3 are not printed and are filled with small numbers here.
+    """
+    g = golden("llm_int8_worked_example.json")
+    c1, c3 = g["outlier_column_magnitudes"]
+    r1 = g["row_regular_values"]
+    x = np.array([[c1[0], r1[0], c3[0], r1[1], r1[2]],
+                  [c1[1], 0.0, c3[1], 3.0, -1.0],
+                  [c1[2], -1.0, c3[2], 2.0, 0.0]], F32)
+    return x, g
+
+
+def check_outlier_example(oracle=O):
+    x, g = outlier_fixture()
+    cols = oracle.outlier_columns(x, g["threshold"])
+    assert (cols + 1).tolist() == g["outlier_column_positions_1based"]
+    q, s = oracle.quantize_rows_regular(x, cols)
+    assert s[0] == F32(g["row_absmax_C_x"]) / F32(127)
+    assert q[0].tolist() == [0, 127, 0, -64, 64]
+    assert q[:, cols].tolist() == [[0, 0]] * 3
+
+
+def test_worked_example_outlier_columns():
+    check_outlier_example()
+
+
+def check_threshold_strict(oracle=O):
+    x = np.array([[6.0, -6.0, 6.0000005, 1.0]], F32)
+    assert oracle.outlier_columns(x, 6.0).tolist() == [2]
+    x = np.array([[1.0, -7.0], [-6.5, 0.0]], F32)
+    assert oracle.outlier_columns(x, 6.0).tolist() == [0, 1]
+
+
+def test_outlier_threshold_is_strict():
+    check_threshold_strict()
+
+
+# ---------------------------------------------------------------------------
+# Library routines the oracle's primitives must agree with
+# ---------------------------------------------------------------------------
+
+def test_rint_is_round_half_even():
+    v = np.array([-3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 126.5, -127.5, 2.4999998], F32)
+    assert np.rint(v).tolist() == [float(round(float(a))) for a in v]
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal(200000).astype(F32) * F32(37)
+    # ties and near-ties: low halves 0x8000, 0x7fff, 0x8001 with both parities
+    base = rng.integers(0x3f000000, 0x42000000, 5000, dtype=np.uint32) & np.uint32(0xFFFF0000)
+    ties = np.concatenate([base | 0x8000, (base | 0x18000), base | 0x7FFF, base | 0x8001]).view(F32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 1e-40, -1e-40], F32)
+    y = np.concatenate([y, ties, special])
+    ours = O.to_bf16_bits(y)
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_rounding_matches_torch():
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal(100000) * 300.0
+    ours = O.to_f16(y.astype(F32)).view(np.uint16)
+    ref = torch.from_numpy(y.astype(F32)).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# Exact integer contraction and the zero-point (four-term) expansion
+# ---------------------------------------------------------------------------
+
+def brute_int_matmul(a, b):
+    a = a.astype(int).tolist()
+    b = b.astype(int).tolist()
+    return [[sum(x * y for x, y in zip(ra, rb)) for rb in b] for ra in a]
+
+
+def test_int_matmul_brute_force():
+    a = synth.random_int8(11, (5, 48))
+    b = synth.random_int8(12, (7, 48))
+    assert O.int_matmul(a, b).tolist() == brute_int_matmul(a, b)
+
+
+def test_int_matmul_extremes_exact():
+    k = 16384
+    a = np.full((2, k), -128, np.int8)
+    b = np.full((3, k), -128, np.int8)
+    b[1] = 127
+    acc = O.int_matmul(a, b)
+    assert acc[0, 0] == 128 * 128 * k and acc[1, 1] == -128 * 127 * k
+    # a single odd term must survive next to a large sum
+    a2 = np.full((1, k), 127, np.int8)
+    b2 = np.full((1, k), 127, np.int8)
+    b2[0, 5] = 126
+    assert O.int_matmul(a2, b2)[0, 0] == 127 * 127 * k - 127
+
+
+def check_four_term(oracle=O):
+    """[LLM.int8] part 1 section 2: sum (a - za)(b - zb) expanded in four terms."""
+    k = 40
+    a = synth.random_int8(21, (4, k))
+    b = synth.random_int8(22, (6, k), -127, 127)
+    # general four-term form with za, zb != 0, checked in plain Python ints
+    for za, zb in [(3, -5), (-128, 7), (0, 0), (127, -1)]:
+        for i in range(4):
+            for j in range(6):
+                lhs = sum((int(a[i, t]) - za) * (int(b[j, t]) - zb) for t in range(k))
+                ab = sum(int(a[i, t]) * int(b[j, t]) for t in range(k))
+                rhs = ab - zb * sum(int(v) for v in a[i]) - za * sum(int(v) for v in b[j]) + k * za * zb
+                assert lhs == rhs
+    # the oracle's specialisation to a symmetric weight (zb = 0)
+    colsum = b.astype(np.int64).sum(axis=1)
+    for z in (-3, 0, 11, -128, 127):
+        got = oracle.zero_point_correct(oracle.int_matmul(a, b), colsum, z)
+        want = [[sum((int(a[i, t]) - z) * int(b[j, t]) for t in range(k)) for j in range(6)]
+                for i in range(4)]
+        assert got.tolist() == want
+
+
+def test_four_term_zero_point_expansion():
+    check_four_term()
+
+
+def test_weight_colsum_is_code_sum():
+    w = synth.weights(31, 9, 64, "f32")
+    wq, sw, colsum = O.quantize_weight(w)
+    assert colsum.tolist() == [sum(int(v) for v in r) for r in wq]
+
+
+# ---------------------------------------------------------------------------
+# Quantizer bounds and extremes
+# ---------------------------------------------------------------------------
+
+def test_symmetric_dequant_error_bound():
+    x = synth.activations(41, 64, 512, [3, 100], 100.0, dtype="f32")
+    q, s = O.quantize_rows_absmax(x)
+    err = np.abs(x.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None].astype(np.float64) / 2 * (1 + 2.0**-20))
+    # the absmax element of every row reaches +-127 with the sign of x
+    idx = np.argmax(np.abs(x), axis=1)
+    r = np.arange(x.shape[0])
+    assert np.all(q[r, idx] == np.where(x[r, idx] > 0, 127, -127))
+    assert q.min() >= -127
+
+
+def test_asymmetric_calibration_extremes():
+    batches = [synth.activations(50 + b, 32, 256, [5], 100.0, offset=0.1, dtype="f32") for b in range(4)]
+    (lo, hi), s, z = O.calibrate(batches)
+    assert lo < 0 < hi
+    assert s == F32(F32(hi - lo) / F32(255))
+    xall = np.concatenate(batches)
+    q, sat = O.quantize_static(xall, s, z)
+    # the range minimum lands exactly on -128; the maximum on 127
+    assert q.flat[np.argmin(xall)] == -128
+    assert q.flat[np.argmax(xall)] == 127
+    # unclamped code of the maximum is 127 or 128 (rounding of both ends)
+    r_max = int(np.rint(F32(F32(hi) / s))) + z
+    assert r_max in (127, 128)
+    assert sat == int(r_max == 128) * int(np.count_nonzero(xall == hi))
+    # dequant error bound for every unclamped value
+    r = np.rint(xall / s).astype(np.int64) + z
+    ok = (r >= -128) & (r <= 127)
+    err = np.abs(xall.astype(np.float64) - float(s) * (q.astype(np.float64) - z))
+    assert np.all(err[ok] <= float(s) / 2 * (1 + 2.0**-20))
+
+
+def test_calibration_range_contains_zero():
+    pos = [np.full((2, 16), 3.0, F32), np.full((2, 16), 5.0, F32)]
+    (lo, hi), s, z = O.calibrate(pos)
+    assert (lo, hi) == (3.0, 5.0)
+    assert s == F32(F32(5.0) / F32(255)) and z == -128
+    q, _ = O.quantize_static(np.zeros((1, 16), F32), s, z)
+    assert np.all(q == z)  # 0 is exactly representable
+    assert O.minmax_finalize((F32(0), F32(0))) == (1.0, 0)
+
+
+def test_static_saturation_counting():
+    s, z = F32(0.5), -3
+    x = np.array([[0.0, 63.0, 64.0, 65.25, -62.0, -63.0, 1e30, -np.inf]], F32)
+    q, sat = O.quantize_static(x, s, z)
+    # codes: rne(x/S) + Z = -3, 123, 125, 127(130.5->130+(-3)=127), -127, -129, huge, -inf
+    assert q.tolist() == [[-3, 123, 125, 127, -127, -128, 127, -128]]
+    assert sat == 3
+
+
+def test_static_round_then_add_zero_point():
+    # x/S = 2.5 exactly: rne(2.5) = 2, then + Z (odd) = 3 ; rne(2.5 + 1) would be 4
+    q, _ = O.quantize_static(np.array([[1.25]], F32), F32(0.5), 1)
+    assert q[0, 0] == 3
+
+
+def test_identity_quantization_special_case():
+    xi = synth.random_int8(61, (3, 32), -127, 127).astype(F32)
+    q, sat = O.quantize_static(xi, F32(1), 0)
+    assert sat == 0 and np.array_equal(q.astype(F32), xi)
+    w = synth.random_int8(62, (5, 32), -127, 127)
+    res = O.linear_decode(xi, F32(1), 0, w, np.ones(5, F32), w.astype(np.int64).sum(1))
+    assert np.array_equal(res["y32"].astype(np.float64), xi.astype(np.float64) @ w.astype(np.float64).T)
+
+
+# ---------------------------------------------------------------------------
+# Invariances
+# ---------------------------------------------------------------------------
+
+def test_sign_and_power_of_two_invariance():
+    x = synth.activations(71, 8, 128, [1], 100.0, dtype="f32")
+    q, s = O.quantize_rows_absmax(x)
+    qn, sn = O.quantize_rows_absmax(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for e in (-3, 5):
+        q2, s2 = O.quantize_rows_absmax(x * F32(2.0**e))
+        assert np.array_equal(q2, q) and np.array_equal(s2, s * F32(2.0**e))
+
+
+def test_joint_k_permutation_invariance():
+    x = synth.activations(72, 6, 96, [4], 100.0, dtype="f32")
+    w = synth.weights(73, 10, 96, "f32")
+    wq, sw, _ = O.quantize_weight(w)
+    perm = np.random.default_rng(5).permutation(96)
+    a = O.linear_prefill(x, wq, sw)
+    b = O.linear_prefill(x[:, perm], wq[:, perm], sw)
+    assert np.array_equal(a["acc"], b["acc"]) and np.array_equal(a["y32"], b["y32"])
+
+
+def test_single_token_per_token_equals_per_tensor():
+    x = synth.activations(74, 1, 64, [2], 100.0, dtype="f32")
+    q, s = O.quantize_rows_absmax(x)
+    s_t = O.absmax_scale(np.max(np.abs(x)))
+    assert s[0] == s_t and np.array_equal(q, O.quantize_symmetric(x, np.array([s_t], F32)))
+
+
+def test_calibration_resume_is_exact():
+    batches = [synth.activations(80 + b, 16, 64, [7], 100.0, offset=0.1, dtype="f32") for b in range(10)]
+    state_all, s_all, z_all = O.calibrate(batches)
+    st = None
+    for b in batches[:5]:
+        st = O.minmax_update(st, b)
+    saved = (F32(st[0]), F32(st[1]))
+    for b in batches[5:]:
+        saved = O.minmax_update(saved, b)
+    assert saved == state_all and O.minmax_finalize(saved) == (s_all, z_all)
+
+
+# ---------------------------------------------------------------------------
+# Brute force of whole layers on tiny shapes
+# ---------------------------------------------------------------------------
+
+def test_prefill_brute_force_error_bound():
+    x = synth.activations(91, 3, 16, [2], 50.0, dtype="f32")
+    w = synth.weights(92, 4, 16, "f32")
+    wq, sw, _ = O.quantize_weight(w)
+    res = O.linear_prefill(x, wq, sw)
+    sx = res["x_scale"]
+    for m in range(3):
+        for n in range(4):
+            exact = sum(float(x[m, k]) * float(w[n, k]) for k in range(16))
+            bound = sum(abs(float(x[m, k])) * float(sw[n]) / 2 + abs(float(w[n, k])) * float(sx[m]) / 2
+                        + float(sx[m]) * float(sw[n]) / 4 for k in range(16))
+            assert abs(float(res["y32"][m, n]) - exact) <= bound * (1 + 1e-5) + 1e-6 * abs(exact)
+
+
+def test_decode_brute_force_error_bound():
+    cal = [synth.activations(93 + b, 8, 32, [1], 20.0, offset=0.1, dtype="f32") for b in range(3)]
+    _, s, z = O.calibrate(cal)
+    x = synth.activations(96, 2, 32, [1], 20.0, offset=0.1, dtype="f32")
+    w = synth.weights(97, 5, 32, "f32")
+    wq, sw, colsum = O.quantize_weight(w)
+    res = O.linear_decode(x, s, z, wq, sw, colsum)
+    assert res["sat"] == 0
+    for m in range(2):
+        for n in range(5):
+            exact = sum(float(x[m, k]) * float(w[n, k]) for k in range(32))
+            bound = sum(abs(float(x[m, k])) * float(sw[n]) / 2 + abs(float(w[n, k])) * float(s) / 2
+                        + float(s) * float(sw[n]) / 4 for k in range(32))
+            assert abs(float(res["y32"][m, n]) - exact) <= bound * (1 + 1e-5) + 1e-6 * abs(exact)
+
+
+def test_epilogue_matches_binary64_evaluation():
+    x = synth.activations(98, 32, 256, [9], 100.0, dtype="f32")
+    w = synth.weights(99, 48, 256, "f32")
+    b = synth.bias(100, 48)
+    wq, sw, _ = O.quantize_weight(w)
+    res = O.linear_prefill(x, wq, sw, b)
+    y64 = (res["x_scale"].astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]) * res["acc"] + b
+    scale = np.abs(res["x_scale"][:, None].astype(np.float64) * sw[None, :] * res["acc"]) + np.abs(b)
+    assert np.all(np.abs(res["y32"] - y64) <= 4 * 2.0**-24 * scale + 1e-30)
+
+
+def test_outlier_infinite_threshold_is_vector_wise():
+    x = synth.activations(111, 12, 64, [3, 40], 100.0, dtype="f16")
+    w = synth.weights(112, 20, 64, "f16")
+    wq, sw, _ = O.quantize_weight(w)
+    a = O.linear_int8_outlier(x, w, wq, sw, np.inf)
+    b = O.linear_prefill(x, wq, sw)
+    assert a["cols"].size == 0
+    assert np.array_equal(a["xq"], b["xq"]) and np.array_equal(a["acc"], b["acc"])
+    assert np.array_equal(a["y64"], b["y32"].astype(np.float64))
+
+
+def test_outlier_all_columns_is_plain_16bit_matmul():
+    x = synth.activations(113, 5, 32, [], dtype="f16")
+    w = synth.weights(114, 7, 32, "f16")
+    wq, sw, _ = O.quantize_weight(w)
+    a = O.linear_int8_outlier(x, w, wq, sw, -1.0)
+    assert a["cols"].tolist() == list(range(32))
+    assert not a["xq"].any() and not a["acc"].any()
+    ref = [[sum(float(x[m, k]) * float(w[n, k]) for k in range(32)) for n in range(7)] for m in range(5)]
+    assert np.allclose(a["y64"], np.array(ref), rtol=1e-12, atol=1e-12)
+
+
+def test_outlier_decomposition_reconstructs_matmul():
+    """INT8 part + 16-bit part approximates X W^T within the INT8 error bound."""
+    x = synth.activations(115, 6, 48, [7, 30], 100.0, dtype="f16")
+    w = synth.weights(116, 9, 48, "f16")
+    wq, sw, _ = O.quantize_weight(w)
+    a = O.linear_int8_outlier(x, w, wq, sw, 6.0)
+    assert a["cols"].tolist() == [7, 30]
+    xr = x.astype(np.float64).copy()
+    xr[:, a["cols"]] = 0
+    sx = a["x_scale"].astype(np.float64)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = (np.abs(xr) @ np.abs(w.astype(np.float64)).T) * 0  # filled below
+    for m in range(6):
+        for n in range(9):
+            bound[m, n] = sum(abs(xr[m, k]) * float(sw[n]) / 2 + abs(float(w[n, k])) * sx[m] / 2
+                              + sx[m] * float(sw[n]) / 4 for k in range(48) if k not in (7, 30))
+    assert np.all(np.abs(a["y64"] - exact) <= bound * (1 + 1e-5) + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: a copy of the oracle with one plausible error each
+# ---------------------------------------------------------------------------
+
+class _Mutant:
+    def __init__(self, **over):
+        self.__dict__.update({k: getattr(O, k) for k in dir(O) if not k.startswith("__")})
+        self.__dict__.update(over)
+
+
+def _half_up_rows(x):
+    x = np.asarray(x, F32)
+    s = O.absmax_scale(np.max(np.abs(x), axis=1))
+    return np.clip(np.floor(x / s[:, None] + F32(0.5)), -127, 127).astype(np.int8), s
+
+
+def _truncating_rows(x):
+    x = np.asarray(x, F32)
+    c = np.max(np.abs(x), axis=1)
+    s = O.absmax_scale(c)
+    return np.clip(np.trunc(x * (F32(127) / c)[:, None]), -127, 127).astype(np.int8), s
+
+
+def _plus_zero_point(acc, colsum, z):
+    return np.asarray(acc, np.int64) + np.int64(z) * np.asarray(colsum, np.int64)[None, :]
+
+
+def _nonstrict_outliers(x, thr):
+    return np.nonzero(np.max(np.abs(np.asarray(x, F32)), axis=0) >= F32(thr))[0]
+
+
+def _rowwise_over_all_columns(x, cols):
+    q, s = O.quantize_rows_absmax(x)
+    q = q.copy()
+    q[:, cols] = 0
+    return q, s
+
+
+@pytest.mark.parametrize("mutant,check", [
+    (_Mutant(quantize_rows_absmax=_half_up_rows), check_worked_row),
+    (_Mutant(quantize_rows_absmax=_truncating_rows), check_worked_row),
+    (_Mutant(zero_point_correct=_plus_zero_point), check_four_term),
+    (_Mutant(quantize_rows_regular=_rowwise_over_all_columns), check_outlier_example),
+    (_Mutant(outlier_columns=_nonstrict_outliers), check_threshold_strict),
+])
+def test_planted_mistake_is_caught(mutant, check):
+    with pytest.raises(AssertionError):
+        check(mutant)
+
