@@ -1,0 +1,205 @@
+/*
+ * pdq.h -- W8A8 INT8 quantized linear layer for AMD MI355X (gfx950).
+ *
+ * C ABI of libpdq.so.  The operations are those of two sources:
+ *
+ *   [PDMIX-term]  "PDMIX inter-phase mixed quantization" terminology entry
+ *                 (msModelSlim knowledge base): section 2.1 core idea,
+ *                 section 2.3 mathematical description, section 2.4 key
+ *                 properties.
+ *   [PDMIX-guide] "PDMIX Parameter Configuration Workflow Guide": section 3
+ *                 process overview; section 4 step 2 (recommended qconfig:
+ *                 act scope pd_mix / int8 / symmetric false / minmax; weight
+ *                 per_channel / int8 / symmetric true / minmax) and step 3
+ *                 (configuration item table).
+ *   [LLM.int8]    "LLM.int8(): 8-bit Matrix Multiplication for Transformers at
+ *                 Scale" reading notes (blog.rainlin.top): part 1 section 1
+ *                 absmax quantization, section 2 zero-point quantization and
+ *                 its four-term expansion, section 3 granularity; part 2
+ *                 vector-wise quantization, the four-step INT8 flow, the 16-bit
+ *                 decomposition and the mixed-precision decomposition.
+ *
+ * Arithmetic (identical on every entry point):
+ *   rne(v)            round to nearest integer, ties to even
+ *   symmetric scale   S = C / 127 (binary32, correctly rounded division) for
+ *                     an absmax C; S = 1 when C == 0
+ *   symmetric code    q = clamp(rne(x / S), -127, 127)       (x / S correctly rounded)
+ *   asymmetric code   q = clamp(rne(x / S) + Z, -128, 127)
+ *   dequant epilogue  y = (S_x * S_w) * (float)acc' [+ bias], every operation
+ *                     rounded to binary32, no fused multiply-add; 16-bit
+ *                     outputs are rounded to nearest even.
+ *
+ * Conventions:
+ *   - Every pointer argument is DEVICE memory owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after returning, and
+ *     never synchronises: all work is enqueued on `stream` (a hipStream_t;
+ *     NULL means the null stream), and buffers must stay valid until that
+ *     work has completed.
+ *   - Matrices are row-major.  Leading dimensions (ld*) are in elements.
+ *     Inner dimension K must be a multiple of 16; every base pointer and
+ *     every row pitch (ld * element size) of a K-wide operand must be a
+ *     multiple of 16 bytes.  Sizes may be 0 (nothing is written then).
+ *   - Every argument check runs on the host before anything is enqueued; on
+ *     error nothing is launched and no output is touched.  After the
+ *     launches, a HIP launch error is reported as PDQ_ERR_HIP.
+ *   - The library holds no mutable global state; calls are reentrant.
+ *     Outputs of one call must not alias its inputs.
+ */
+#ifndef PDQ_H_
+#define PDQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PDQ_OK = 0,
+    PDQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    PDQ_ERR_SHAPE = 2,       /* negative size, K % 16 != 0, ld too small        */
+    PDQ_ERR_DTYPE = 3,       /* dtype not accepted by this entry point          */
+    PDQ_ERR_ALIGN = 4,       /* pointer or row pitch not 16-byte aligned        */
+    PDQ_ERR_UNSUPPORTED = 5, /* value out of range (scale, zero point, ...)     */
+    PDQ_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required         */
+    PDQ_ERR_HIP = 8          /* the HIP runtime reported a launch error         */
+} pdq_status;
+
+typedef enum {
+    PDQ_F32 = 0,  /* IEEE binary32                */
+    PDQ_BF16 = 1, /* bfloat16 (upper half of f32) */
+    PDQ_F16 = 2   /* IEEE binary16                */
+} pdq_dtype;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* pdq_status_string(pdq_status s);
+
+/*
+ * Offline weight quantization, per output channel, symmetric, MinMax
+ * (= absmax for a symmetric grid).  [PDMIX-guide] step 2 weight qconfig;
+ * [PDMIX-term] 2.1/2.4: one INT8 copy serves both phases; [LLM.int8] part 1
+ * section 1 absmax formula.
+ *
+ *   w        [N, K] of w_dt (F32, BF16 or F16), row pitch ldw >= K
+ *   wq       [N, K] int8 out, dense (row pitch K)
+ *   w_scale  [N] float out: S_w[n] = max_k |w[n,k]| / 127
+ *   w_colsum [N] int32 out, or NULL: sum_k wq[n,k] (needed by decode's
+ *            zero-point correction, [LLM.int8] part 1 section 2)
+ */
+pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
+                               int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream);
+
+/*
+ * Static calibration for the decode phase: MinMax observer over calibration
+ * batches, then the per-tensor asymmetric scale and zero point.
+ * [PDMIX-term] 2.3 decode formula and section 3 (MinMax); [PDMIX-guide]
+ * section 3: decode measures and exports per-tensor asymmetric parameters.
+ *
+ *   x        [M, K] batch of x_dt, row pitch ldx; may be NULL when M == 0
+ *   minmax   float[2] in/out running {min, max}; initialise to {+INF, -INF}
+ *            before the first batch.  min/max are exact and order-free, so
+ *            a saved state resumes calibration bit-exactly.
+ *   a_scale  float[1] out or NULL; a_zp int32[1] out or NULL.  When both are
+ *            non-NULL the updated state is finalised (after this batch):
+ *            range [lo, hi] = [min(min, 0), max(max, 0)];
+ *            S = (hi - lo) / 255 (S = 1 if hi == lo);
+ *            Z = clamp(-128 - rne(lo / S), -128, 127).
+ *            Passing only one of them is PDQ_ERR_NULL.
+ */
+pdq_status pdq_calibrate_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                float* minmax, float* a_scale, int32_t* a_zp, void* stream);
+
+/*
+ * Prefill linear: per-token dynamic symmetric activation quantization, INT8
+ * GEMM with INT32 accumulation, fused dequantizing epilogue, bf16 output.
+ * [PDMIX-term] 2.3 prefill formula with Z_token = 0 ([PDMIX-guide] step 3:
+ * prefill is per-token symmetric); [LLM.int8] part 2 steps (2)-(4) and the
+ * vector-wise outer product of scales.
+ *
+ *   x        [M, K] of x_dt (F32, BF16, F16), row pitch ldx
+ *   wq       [N, K] int8 from pdq_quantize_weight; w_scale [N] float
+ *   bias     [N] float or NULL
+ *   xq       [M, K] int8 out (dense), x_scale [M] float out: the quantized
+ *            activations and their per-token scales (also the GEMM operand)
+ *   y        [M, N] bfloat16 out (uint16 bit patterns), row pitch ldy >= N
+ *            y = bf16((S_x[m] * S_w[n]) * (float)acc[m,n] [+ bias[n]])
+ *   acc_out  [M, N] int32 out (dense) or NULL: acc = sum_k xq[m,k] wq[n,k]
+ */
+pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                              const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
+                              int8_t* xq, float* x_scale, uint16_t* y, int64_t ldy,
+                              int32_t* acc_out, void* stream);
+
+/*
+ * Decode linear: per-tensor static asymmetric activation quantization with
+ * the offline (S, Z), INT8 GEMM, zero-point correction through the weight
+ * code sums, fused epilogue, bf16 output.  [PDMIX-term] 2.3 decode formula
+ * (round, then add Z); 2.4: static scales may saturate on inputs the
+ * calibration did not cover; [LLM.int8] part 1 section 2 four-term expansion
+ * reduced to a symmetric weight: acc' = acc - Z * colsum[n].
+ *
+ *   x          [M, K] of x_dt, row pitch ldx (any M; built for M <= 64)
+ *   a_scale    S > 0 and finite; a_zp Z in [-128, 127] (host values, from
+ *              pdq_calibrate_static)
+ *   wq, w_scale, w_colsum  from pdq_quantize_weight (w_colsum required)
+ *   bias       [N] float or NULL
+ *   xq         [M, K] int8 out (dense): q = clamp(rne(x / S) + Z, -128, 127)
+ *   y          [M, N] bfloat16 out, row pitch ldy:
+ *              y = bf16((S * S_w[n]) * (float)(acc - Z * colsum[n]) [+ bias[n]])
+ *   acc_out    [M, N] int32 out or NULL: raw acc = sum_k xq wq (before the
+ *              zero-point term)
+ *   sat_count  uint32[1] or NULL: INCREMENTED by the number of values whose
+ *              unclamped code rne(x / S) + Z lies outside [-128, 127]; the
+ *              caller resets it when it wants a fresh count.
+ */
+pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                             float a_scale, int32_t a_zp, const int8_t* wq, const float* w_scale,
+                             const int32_t* w_colsum, const float* bias, int64_t N, int8_t* xq,
+                             uint16_t* y, int64_t ldy, int32_t* acc_out, uint32_t* sat_count,
+                             void* stream);
+
+/*
+ * LLM.int8() vector-wise quantization with the 16-bit outlier decomposition.
+ * [LLM.int8] part 2: outlier columns are the hidden dimensions whose
+ * magnitude exceeds the threshold (6.0 in the text); the regular part is
+ * quantized per row (absmax over the regular columns) against the
+ * per-output-channel INT8 weight and multiplied in INT8; the outlier columns
+ * of x and of the 16-bit weight are multiplied in 16-bit floating point
+ * (binary32 accumulation); the two results are summed into a 16-bit output.
+ *
+ *   x            [M, K] of dt (F16 or BF16), row pitch ldx
+ *   threshold    column k is an outlier iff max_m |x[m,k]| > threshold
+ *                (strict; +INF gives no outliers; NaN is rejected)
+ *   wq, w_scale  the shared INT8 weight (pdq_quantize_weight over full K)
+ *   w16          [N, K] of dt: the original 16-bit weight, row pitch ldw
+ *   bias         [N] float or NULL
+ *   y            [M, N] of dt out, row pitch ldy
+ *   xq           [M, K] int8 out: regular columns quantized, outliers 0
+ *   x_scale      [M] float out: absmax over regular columns / 127
+ *   outlier_idx  int32[max_outliers] out: ascending outlier columns (the
+ *                first max_outliers of them)
+ *   n_outlier    int32[1] out: the number of outlier columns found
+ *   max_outliers capacity for the 16-bit part, >= 0.  If more columns than
+ *                this exceed the threshold, every element of y is set to
+ *                NaN (n_outlier still reports the true count).
+ *   workspace    device scratch of at least
+ *                pdq_linear_int8_outlier_workspace(M, N, K, max_outliers)
+ *                bytes, 256-byte aligned; its contents on entry do not matter
+ *   acc_out      [M, N] int32 out or NULL: the INT8 part's accumulator
+ */
+size_t pdq_linear_int8_outlier_workspace(int64_t M, int64_t N, int64_t K, int64_t max_outliers);
+
+pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx,
+                                   float threshold, const int8_t* wq, const float* w_scale,
+                                   const void* w16, int64_t ldw, const float* bias, int64_t N,
+                                   void* y, int64_t ldy, int8_t* xq, float* x_scale,
+                                   int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers,
+                                   void* workspace, size_t workspace_bytes, int32_t* acc_out,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDQ_H_ */

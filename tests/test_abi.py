@@ -1,0 +1,132 @@
+"""The C ABI of libpdq on the host: symbols and argument validation.
+
+Every call here is rejected by the host-side checks before anything is
+enqueued (the pointers are never dereferenced), so these run without a GPU.
+"""
+import ctypes
+import os
+
+import pytest
+
+from w8a8_int8_quantized_absmax_amd import pdq
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000  # 64 KiB-aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pdq.LIB_PATH):
+        pytest.skip("libpdq.so not built")
+    return pdq.lib()
+
+
+def test_header_functions_all_exported(L):
+    names = pdq.header_functions()
+    assert set(names) == set(pdq.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, 8):
+        assert L.pdq_status_string(s)
+    assert L.pdq_status_string(SHAPE).startswith(b"invalid shape")
+
+
+def qw(L, w=P, dt=1, N=4, K=32, ldw=32, wq=P, ws=P, cs=P):
+    return L.pdq_quantize_weight(w, dt, N, K, ldw, wq, ws, cs, None)
+
+
+def test_quantize_weight_validation(L):
+    assert qw(L, dt=7) == DTYPE
+    assert qw(L, K=17, ldw=17) == SHAPE
+    assert qw(L, K=32, ldw=16) == SHAPE
+    assert qw(L, N=-1) == SHAPE
+    assert qw(L, K=65536 + 16, ldw=65536 + 16) == SHAPE
+    assert qw(L, w=None) == NULL
+    assert qw(L, wq=None) == NULL
+    assert qw(L, ws=None) == NULL
+    assert qw(L, w=P + 8) == ALIGN
+    assert qw(L, dt=1, ldw=36) == ALIGN     # bf16 pitch 72 bytes
+    assert qw(L, wq=P + 4) == ALIGN
+    assert qw(L, N=0) == OK                # nothing to do, nothing launched
+
+
+def pre(L, x=P, dt=1, M=8, K=64, ldx=64, wq=P, ws=P, bias=None, N=16, xq=P, xs=P, y=P, ldy=16, acc=None):
+    return L.pdq_linear_prefill(x, dt, M, K, ldx, wq, ws, bias, N, xq, xs, y, ldy, acc, None)
+
+
+def test_prefill_validation(L):
+    assert pre(L, dt=3) == DTYPE
+    assert pre(L, K=40, ldx=40) == SHAPE
+    assert pre(L, ldy=15) == SHAPE
+    assert pre(L, N=-2) == SHAPE
+    assert pre(L, x=None) == NULL
+    assert pre(L, xq=None) == NULL
+    assert pre(L, xs=None) == NULL
+    assert pre(L, y=None) == NULL
+    assert pre(L, ws=None) == NULL
+    assert pre(L, wq=P + 1) == ALIGN
+    assert pre(L, y=P + 1) == ALIGN
+    assert pre(L, bias=P + 2) == ALIGN
+    assert pre(L, M=0) == OK
+
+
+def dec(L, x=P, dt=1, M=4, K=64, ldx=64, s=0.5, z=-3, wq=P, ws=P, cs=P, bias=None, N=16, xq=P, y=P,
+        ldy=16, acc=None, sat=None):
+    return L.pdq_linear_decode(x, dt, M, K, ldx, s, z, wq, ws, cs, bias, N, xq, y, ldy, acc, sat, None)
+
+
+def test_decode_validation(L):
+    assert dec(L, dt=-1) == DTYPE
+    assert dec(L, K=8, ldx=8) == SHAPE
+    assert dec(L, s=0.0) == UNSUP
+    assert dec(L, s=-1.0) == UNSUP
+    assert dec(L, s=float("inf")) == UNSUP
+    assert dec(L, s=float("nan")) == UNSUP
+    assert dec(L, z=128) == UNSUP
+    assert dec(L, z=-129) == UNSUP
+    assert dec(L, cs=None) == NULL
+    assert dec(L, xq=None) == NULL
+    assert dec(L, sat=P + 2) == ALIGN
+    assert dec(L, M=0) == OK
+
+
+def test_calibrate_validation(L):
+    f = L.pdq_calibrate_static
+    assert f(P, 1, 4, 64, 64, None, None, None, None) == NULL     # no state
+    assert f(P, 1, 4, 64, 64, P, P, None, None) == NULL          # scale without zero point
+    assert f(P, 5, 4, 64, 64, P, None, None, None) == DTYPE
+    assert f(P, 1, 4, 60, 64, P, None, None, None) == SHAPE
+    assert f(P, 1, 4, 64, 64, P + 2, None, None, None) == ALIGN
+
+
+def test_outlier_workspace_size(L):
+    ws = L.pdq_linear_int8_outlier_workspace
+    # flags (K u32) + X_out (M x P f16) + W_out (N x P f16), each 256-aligned, P = ceil16(max)
+    assert ws(2048, 28672, 8192, 64) == 8192 * 4 + 2048 * 64 * 2 + 28672 * 64 * 2
+    assert ws(3, 5, 16, 1) == 256 + 256 + 256
+    assert ws(3, 5, 16, 0) == 256
+    assert ws(-1, 5, 16, 1) == 0
+
+
+def out8(L, x=P, dt=2, M=8, K=64, ldx=64, thr=6.0, wq=P, ws=P, w16=P, ldw=64, bias=None, N=16, y=P,
+         ldy=16, xq=P, xs=P, idx=P, cnt=P, maxo=8, work=P, work_bytes=1 << 20, acc=None):
+    return L.pdq_linear_int8_outlier(x, dt, M, K, ldx, thr, wq, ws, w16, ldw, bias, N, y, ldy, xq, xs,
+                                     idx, cnt, maxo, work, work_bytes, acc, None)
+
+
+def test_outlier_validation(L):
+    assert out8(L, dt=0) == DTYPE      # the 16-bit path takes F16 or BF16 only
+    assert out8(L, thr=float("nan")) == UNSUP
+    assert out8(L, maxo=65) == SHAPE
+    assert out8(L, maxo=-1) == SHAPE
+    assert out8(L, cnt=None) == NULL
+    assert out8(L, idx=None) == NULL
+    assert out8(L, w16=None) == NULL
+    assert out8(L, work=None) == WS
+    need = L.pdq_linear_int8_outlier_workspace(8, 16, 64, 8)
+    assert out8(L, work_bytes=need - 1) == WS
+    assert out8(L, work=P + 16) == ALIGN
+    assert out8(L, w16=P + 1) == ALIGN

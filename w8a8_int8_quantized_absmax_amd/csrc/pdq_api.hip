@@ -1,0 +1,231 @@
+// The C entry points of libpdq: host-side argument checks, then the kernel
+// launches of each operation on the caller's stream.  Declared and
+// documented in include/pdq.h.
+
+#include <math.h>
+
+#include "pdq.h"
+#include "pdq_kernels.h"
+
+using namespace pdq;
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;        // |sum_k (q_x - Z) q_w| < 255 * 127 * K stays in int32
+constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
+
+int elem_bytes(int dt) { return dt == PDQ_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == PDQ_F32 || dt == PDQ_BF16 || dt == PDQ_F16; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape rules shared by every K-wide operand.
+pdq_status check_mk(int64_t M, int64_t K, int64_t ld) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxK || K % 16 != 0) return PDQ_ERR_SHAPE;
+    if (ld < K || ld < 0) return PDQ_ERR_SHAPE;
+    return PDQ_OK;
+}
+
+// A [rows, K] operand with `ebytes`-byte elements and row pitch `ld`.
+pdq_status check_operand(const void* p, int ebytes, int64_t rows, int64_t K, int64_t ld) {
+    pdq_status s = check_mk(rows, K, ld);
+    if (s != PDQ_OK) return s;
+    if (rows > 0 && K > 0 && !p) return PDQ_ERR_NULL;
+    if (!aligned(p, 16) || (ld * ebytes) % 16 != 0) return PDQ_ERR_ALIGN;
+    return PDQ_OK;
+}
+
+pdq_status launched() { return hipGetLastError() == hipSuccess ? PDQ_OK : PDQ_ERR_HIP; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int64_t side_pitch(int64_t max_out) { return (max_out + 15) / 16 * 16; }
+
+}  // namespace
+
+#define PDQ_TRY(expr)                         \
+    do {                                      \
+        const pdq_status s_ = (expr);         \
+        if (s_ != PDQ_OK) return s_;          \
+    } while (0)
+
+extern "C" {
+
+const char* pdq_status_string(pdq_status s) {
+    switch (s) {
+        case PDQ_OK: return "ok";
+        case PDQ_ERR_NULL: return "required pointer is NULL";
+        case PDQ_ERR_SHAPE: return "invalid shape (negative size, K % 16 != 0, K > 65536, or ld too small)";
+        case PDQ_ERR_DTYPE: return "dtype not accepted by this entry point";
+        case PDQ_ERR_ALIGN: return "pointer or row pitch not 16-byte aligned";
+        case PDQ_ERR_UNSUPPORTED: return "argument value out of range";
+        case PDQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case PDQ_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
+                               int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream) {
+    if (!dtype_ok(w_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(w, elem_bytes(w_dt), N, K, ldw));
+    if (N > 0 && ((K > 0 && !wq) || !w_scale)) return PDQ_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4)) return PDQ_ERR_ALIGN;
+    if (N == 0) return PDQ_OK;
+    launch_quant_rows(w, w_dt, N, K, ldw, wq, w_scale, w_colsum, nullptr,
+                      static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_calibrate_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                float* minmax, float* a_scale, int32_t* a_zp, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!minmax) return PDQ_ERR_NULL;
+    if ((a_scale == nullptr) != (a_zp == nullptr)) return PDQ_ERR_NULL;
+    if (!aligned(minmax, 4) || !aligned(a_scale, 4) || !aligned(a_zp, 4)) return PDQ_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    launch_minmax(x, x_dt, M, K, ldx, minmax, st);
+    if (a_scale) launch_minmax_finalize(minmax, a_scale, a_zp, st);
+    return launched();
+}
+
+pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                              const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
+                              int8_t* xq, float* x_scale, uint16_t* y, int64_t ldy,
+                              int32_t* acc_out, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N > 0 && !w_scale) return PDQ_ERR_NULL;
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr, st);
+    GemmArgs g{};
+    g.A = xq;
+    g.B = wq;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.sa = x_scale;
+    g.sb = w_scale;
+    g.bias = bias;
+    g.y = y;
+    g.ldy = ldy;
+    g.acc_out = acc_out;
+    launch_gemm_i8(g, PDQ_BF16, false, st);
+    return launched();
+}
+
+pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                             float a_scale, int32_t a_zp, const int8_t* wq, const float* w_scale,
+                             const int32_t* w_colsum, const float* bias, int64_t N, int8_t* xq,
+                             uint16_t* y, int64_t ldy, int32_t* acc_out, uint32_t* sat_count,
+                             void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
+        return PDQ_ERR_UNSUPPORTED;
+    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(acc_out, 4) || !aligned(sat_count, 4))
+        return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    launch_quant_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, st);
+    DecodeArgs d{};
+    d.xq = xq;
+    d.wq = wq;
+    d.M = (int)M;
+    d.N = (int)N;
+    d.K = (int)K;
+    d.s = a_scale;
+    d.z = a_zp;
+    d.sw = w_scale;
+    d.colsum = w_colsum;
+    d.bias = bias;
+    d.y = y;
+    d.ldy = ldy;
+    d.acc_out = acc_out;
+    launch_decode_gemv(d, st);
+    return launched();
+}
+
+size_t pdq_linear_int8_outlier_workspace(int64_t M, int64_t N, int64_t K, int64_t max_outliers) {
+    if (M < 0 || N < 0 || K < 0 || max_outliers < 0) return 0;
+    const int64_t P = side_pitch(max_outliers);
+    return align256((size_t)K * 4) + align256((size_t)(M * P * 2)) + align256((size_t)(N * P * 2));
+}
+
+pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx,
+                                   float threshold, const int8_t* wq, const float* w_scale,
+                                   const void* w16, int64_t ldw, const float* bias, int64_t N,
+                                   void* y, int64_t ldy, int8_t* xq, float* x_scale,
+                                   int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers,
+                                   void* workspace, size_t workspace_bytes, int32_t* acc_out,
+                                   void* stream) {
+    if (dt != PDQ_F16 && dt != PDQ_BF16) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N || ldw < K) return PDQ_ERR_SHAPE;
+    if (max_outliers < 0 || max_outliers > K) return PDQ_ERR_SHAPE;
+    if (isnan(threshold)) return PDQ_ERR_UNSUPPORTED;
+    if (!n_outlier || (max_outliers > 0 && !outlier_idx)) return PDQ_ERR_NULL;
+    if (N > 0 && (!w_scale || (K > 0 && !w16))) return PDQ_ERR_NULL;
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(w16, 2) || !aligned(acc_out, 4) || !aligned(outlier_idx, 4) ||
+        !aligned(n_outlier, 4))
+        return PDQ_ERR_ALIGN;
+    const size_t need = pdq_linear_int8_outlier_workspace(M, N, K, max_outliers);
+    if (!workspace || workspace_bytes < need) return PDQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PDQ_ERR_ALIGN;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t P = side_pitch(max_outliers);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + align256((size_t)K * 4));
+    uint16_t* wo = reinterpret_cast<uint16_t*>(ws + align256((size_t)K * 4) +
+                                               align256((size_t)(M * P * 2)));
+
+    launch_fill_zero_u32(flags, K, st);
+    launch_outlier_flags(x, dt, M, K, ldx, threshold, flags, st);
+    launch_outlier_compact(flags, K, outlier_idx, n_outlier, max_outliers, st);
+    if (M > 0) {
+        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, flags, st);
+        launch_gather_cols(x, M, ldx, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P, st);
+    }
+    launch_gather_cols(w16, N, ldw, outlier_idx, n_outlier, (int)max_outliers, wo, (int)P, st);
+    GemmArgs g{};
+    g.A = xq;
+    g.B = wq;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.sa = x_scale;
+    g.sb = w_scale;
+    g.bias = bias;
+    g.y = y;
+    g.ldy = ldy;
+    g.acc_out = acc_out;
+    g.xo = xo;
+    g.wo = wo;
+    g.P = (int)P;
+    g.count = n_outlier;
+    g.max_count = (int)max_outliers;
+    launch_gemm_i8(g, dt, true, st);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Device-side helpers shared by the HIP kernels of libpdq (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdq {
+
+enum DType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<kF32> {
+    static constexpr int bytes = 4;
+};
+template <>
+struct Elem<kBF16> {
+    static constexpr int bytes = 2;
+};
+template <>
+struct Elem<kF16> {
+    static constexpr int bytes = 2;
+};
+
+// One 8-element chunk of a K-contiguous row in its storage format: 16 bytes
+// for the 16-bit types, 32 bytes for binary32.
+template <int DT>
+struct Raw8 {
+    uint4 w[DT == kF32 ? 2 : 1];
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// binary32 -> bfloat16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// binary32 -> binary16, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load_raw8(const void* row, int chunk) {
+    Raw8<DT> r;
+    const uint4* p = reinterpret_cast<const uint4*>(row) + chunk * (DT == kF32 ? 2 : 1);
+    r.w[0] = p[0];
+    if constexpr (DT == kF32) r.w[1] = p[1];
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> zero_raw8() {
+    Raw8<DT> r;
+    r.w[0] = make_uint4(0, 0, 0, 0);
+    if constexpr (DT == kF32) r.w[1] = make_uint4(0, 0, 0, 0);
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void widen8(const Raw8<DT>& r, float (&v)[8]) {
+    if constexpr (DT == kF32) {
+        v[0] = __uint_as_float(r.w[0].x);
+        v[1] = __uint_as_float(r.w[0].y);
+        v[2] = __uint_as_float(r.w[0].z);
+        v[3] = __uint_as_float(r.w[0].w);
+        v[4] = __uint_as_float(r.w[1].x);
+        v[5] = __uint_as_float(r.w[1].y);
+        v[6] = __uint_as_float(r.w[1].z);
+        v[7] = __uint_as_float(r.w[1].w);
+    } else {
+        const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == kBF16) {
+                v[2 * i] = bf16_to_f32(u[i] & 0xffffu);
+                v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+            } else {
+                v[2 * i] = f16_to_f32(u[i] & 0xffffu);
+                v[2 * i + 1] = f16_to_f32(u[i] >> 16);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Symmetric step size from an absmax: S = C / 127 (correctly rounded), 1 if C == 0.
+__device__ __forceinline__ float absmax_step(float c) { return c == 0.0f ? 1.0f : c / 127.0f; }
+
+// Symmetric code: clamp(rne(x / S), -127, 127) with a correctly rounded quotient.
+__device__ __forceinline__ int sym_code(float x, float s) {
+    float r = __builtin_rintf(x / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// Float max / min through integer atomics (valid for every non-NaN value,
+// including +-INF and the {+INF, -INF} starting state).  -0 is taken as +0 so
+// that the sign test below routes it through the signed-integer branch.
+__device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
+    if (v == 0.0f) v = 0.0f;
+    if (v >= 0.0f)
+        atomicMax(reinterpret_cast<int*>(addr), __float_as_int(v));
+    else
+        atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+__device__ __forceinline__ void atomic_min_f32(float* addr, float v) {
+    if (v == 0.0f) v = 0.0f;
+    if (v >= 0.0f)
+        atomicMin(reinterpret_cast<int*>(addr), __float_as_int(v));
+    else
+        atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace pdq

@@ -1,0 +1,292 @@
+// Activation and weight quantizers of libpdq (gfx950).
+//
+//  * k_quant_rows   per-row absmax symmetric INT8 -- per output channel for
+//                   weights, per token for prefill activations (PDMIX
+//                   terminology entry, section 2.3 prefill formula with a zero
+//                   zero point; LLM.int8() notes, part 1 "Absmax
+//                   quantization"), optionally skipping the outlier columns of
+//                   the LLM.int8() decomposition (part 2, vector-wise step (1)
+//                   on X_normal).  One wavefront per row: the row is read from
+//                   HBM once with 16-byte loads, kept in registers in its
+//                   storage format, reduced with cross-lane shuffles, then
+//                   quantized and written as packed INT8.
+//  * k_quant_static per-tensor static asymmetric INT8 of the decode phase
+//                   (PDMIX terminology entry, section 2.3 decode formula),
+//                   with the saturation count of section 2.4.
+//  * k_minmax       the MinMax observer of the static calibration, and
+//    k_minmax_finalize its (S, Z) (PDMIX usage guide, section 3).
+//
+// Every division is the correctly rounded binary32 division and every
+// rounding to an integer is round-half-to-even (v_rndne_f32), so the codes
+// and scales match a host evaluation of the same formulas bit for bit.
+
+#include "pdq_device.h"
+#include "pdq_kernels.h"
+
+namespace pdq {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wavefront per row, four per workgroup
+
+template <bool SKIP>
+__device__ __forceinline__ uint32_t skip_mask(const uint32_t* __restrict__ flags, int chunk) {
+    if constexpr (!SKIP) {
+        return 0u;
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(flags + chunk * 8);
+        const uint4 a = p[0], b = p[1];
+        return (uint32_t)(a.x != 0) | ((uint32_t)(a.y != 0) << 1) | ((uint32_t)(a.z != 0) << 2) |
+               ((uint32_t)(a.w != 0) << 3) | ((uint32_t)(b.x != 0) << 4) |
+               ((uint32_t)(b.y != 0) << 5) | ((uint32_t)(b.z != 0) << 6) |
+               ((uint32_t)(b.w != 0) << 7);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float chunk_absmax(const Raw8<DT>& r, uint32_t skipm, float amax) {
+    float v[8];
+    widen8<DT>(r, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (!((skipm >> j) & 1u)) amax = fmaxf(amax, fabsf(v[j]));
+    return amax;
+}
+
+template <int DT>
+__device__ __forceinline__ uint2 chunk_codes(const Raw8<DT>& r, uint32_t skipm, float s, int& csum) {
+    float v[8];
+    widen8<DT>(r, v);
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        c[j] = ((skipm >> j) & 1u) ? 0 : sym_code(v[j], s);
+        csum += c[j];
+    }
+    return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+}
+
+// CPL > 0: each lane keeps CPL chunks of 8 elements in registers (one HBM
+// read).  CPL == 0: rows too long for registers are streamed twice (the
+// second pass hits the L2).
+template <int DT, int CPL, bool SKIP, bool COLSUM>
+__global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
+                                                    int64_t rows, int nch, int8_t* __restrict__ q,
+                                                    float* __restrict__ scale,
+                                                    int32_t* __restrict__ colsum,
+                                                    const uint32_t* __restrict__ skip) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wavefront leaves together
+    const char* xr = static_cast<const char*>(x) + row * ld_bytes;
+    uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+
+    float amax = 0.0f;
+    int csum = 0;
+    float s;
+    if constexpr (CPL > 0) {
+        Raw8<DT> raw[CPL];
+        uint32_t sk[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            raw[i] = c < nch ? load_raw8<DT>(xr, c) : zero_raw8<DT>();
+            sk[i] = c < nch ? skip_mask<SKIP>(skip, c) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+        amax = wave_max(amax);
+        s = absmax_step(amax);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nch) qr[c] = chunk_codes<DT>(raw[i], sk[i], s, csum);
+        }
+    } else {
+        for (int c = lane; c < nch; c += 64)
+            amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
+        amax = wave_max(amax);
+        s = absmax_step(amax);
+        for (int c = lane; c < nch; c += 64)
+            qr[c] = chunk_codes<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), s, csum);
+    }
+    if (lane == 0) scale[row] = s;
+    if constexpr (COLSUM) {
+        csum = wave_sum(csum);
+        if (lane == 0) colsum[row] = csum;
+    }
+}
+
+template <int DT, int CPL>
+void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
+                    int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    const int64_t ldb = ldx * Elem<DT>::bytes;
+    const int nch = (int)(K / 8);
+    if (skip) {
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, true, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
+    } else if (colsum) {
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, false, true>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
+    } else {
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, false, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
+    }
+}
+
+template <int DT>
+void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
+                   int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+    const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
+    constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
+    if (per_lane <= 1)
+        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else if (per_lane <= 2)
+        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else if (per_lane <= 4)
+        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else if (per_lane <= 8)
+        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else if (per_lane <= 16)
+        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else if (per_lane <= kMaxCpl)
+        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, st);
+    else
+        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, st);
+}
+
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x, int64_t ld_bytes,
+                                                      int64_t total, int nch,
+                                                      int8_t* __restrict__ q, float s, int z,
+                                                      uint32_t* __restrict__ sat) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int nsat = 0;
+    if (c < total) {
+        const int64_t row = c / nch;
+        const int col = (int)(c - row * nch);
+        float v[8];
+        widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
+        int code[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float r = __builtin_rintf(v[j] / s);
+            r = fminf(fmaxf(r, -512.0f), 512.0f);  // keeps the int conversion in range
+            const int ri = (int)r + z;
+            nsat += (ri < -128) | (ri > 127);
+            code[j] = min(max(ri, -128), 127);
+        }
+        reinterpret_cast<uint2*>(q)[c] = make_uint2(pack4_i8(code[0], code[1], code[2], code[3]),
+                                                    pack4_i8(code[4], code[5], code[6], code[7]));
+    }
+    if (sat) {
+        nsat = wave_sum(nsat);
+        if ((threadIdx.x & 63) == 0 && nsat) atomicAdd(sat, (uint32_t)nsat);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_minmax(const void* __restrict__ x, int64_t ld_bytes,
+                                                int64_t total, int nch, float* __restrict__ mm) {
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * 256) {
+        const int64_t row = c / nch;
+        const int col = (int)(c - row * nch);
+        float v[8];
+        widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo = fminf(lo, v[j]);
+            hi = fmaxf(hi, v[j]);
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((threadIdx.x & 63) == 0 && lo <= hi) {
+        atomic_min_f32(mm, lo);
+        atomic_max_f32(mm + 1, hi);
+    }
+}
+
+__global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restrict__ s_out,
+                                  int32_t* __restrict__ z_out) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const float lo = fminf(mm[0], 0.0f);
+    const float hi = fmaxf(mm[1], 0.0f);
+    float s = 1.0f;
+    int z = 0;
+    if (hi != lo) {
+        s = (hi - lo) / 255.0f;
+        z = -128 - (int)__builtin_rintf(lo / s);
+        z = min(max(z, -128), 127);
+    }
+    *s_out = s;
+    *z_out = z;
+}
+
+}  // namespace
+
+void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
+                       float* scale, int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+    if (rows <= 0) return;
+    switch (dt) {
+        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+    }
+}
+
+void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
+                         int8_t* q, uint32_t* sat, hipStream_t st) {
+    const int64_t total = M * (K / 8);
+    if (total <= 0) return;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    const int nch = (int)(K / 8);
+    switch (dt) {
+        case kF32:
+            hipLaunchKernelGGL(k_quant_static<kF32>, grid, dim3(256), 0, st, x, ldx * 4, total, nch,
+                               q, s, z, sat);
+            break;
+        case kBF16:
+            hipLaunchKernelGGL(k_quant_static<kBF16>, grid, dim3(256), 0, st, x, ldx * 2, total,
+                               nch, q, s, z, sat);
+            break;
+        default:
+            hipLaunchKernelGGL(k_quant_static<kF16>, grid, dim3(256), 0, st, x, ldx * 2, total, nch,
+                               q, s, z, sat);
+            break;
+    }
+}
+
+void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float* mm,
+                   hipStream_t st) {
+    const int64_t total = M * (K / 8);
+    if (total <= 0) return;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    const int nch = (int)(K / 8);
+    switch (dt) {
+        case kF32:
+            hipLaunchKernelGGL(k_minmax<kF32>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx * 4,
+                               total, nch, mm);
+            break;
+        case kBF16:
+            hipLaunchKernelGGL(k_minmax<kBF16>, dim3((unsigned)blocks), dim3(256), 0, st, x,
+                               ldx * 2, total, nch, mm);
+            break;
+        default:
+            hipLaunchKernelGGL(k_minmax<kF16>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx * 2,
+                               total, nch, mm);
+            break;
+    }
+}
+
+void launch_minmax_finalize(const float* mm, float* a_scale, int32_t* a_zp, hipStream_t st) {
+    hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, a_zp);
+}
+
+}  // namespace pdq
