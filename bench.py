@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the W8A8 INT8 linear layer on one MI355X.
+
+Headline (the JSON `value`): the prefill linear of a 7B-like MLP up-projection,
+4096 tokens x (4096 -> 11008), bf16 activations quantized per token on the
+fly, INT8 MFMA GEMM, fused dequant epilogue to bf16 -- one step is one whole
+prefill linear (quantize + GEMM + epilogue) and `value` is 2*M*N*K / step
+time in TOPS.  `roofline` is the INT8 GEMM kernel alone, timed with HIP
+events on the stream it is launched on, against the chip's dense INT8 peak.
+
+Also measured in the same run and reported under "decode" and "llm_int8":
+the static per-tensor decode linear 4096 -> 4096 at M in {1, 8, 32, 64}
+(HBM GB/s of the skinny GEMM against 8 TB/s, weights rotated over >= 1 GiB of
+copies so that no cache serves them), and the LLM.int8() decomposition
+2048 x (8192 -> 28672) in fp16 with threshold 6.0.
+
+cpu_baseline: the CPU oracle timed on the host on the same prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill W8A8 GEMM TOPS + decode GB/s, as % of MI355X INT8/HBM roofline"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, published (5.0 POP/s)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published (8 TB/s)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_prefill_4096x4096x11008_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "w8a8_int8_quantized_absmax_amd", "csrc", "gemm_i8.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, iters: int, warmup: int, stream) -> float:
+    """Average milliseconds per call of fn(i) over `iters` calls, HIP events on `stream`."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def kernel_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(per_launch_bytes_expected: float):
+    """HBM bytes per GEMM launch from the committed PMC summary, if it is for this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def bench_prefill(args, torch, pdq, synth):
+    c = synth.Prefill7B()
+    M, K, N = c.M, c.K, c.N
+    log(f"[prefill] generating X[{M},{K}] and W[{N},{K}] ({c.dtype})")
+    x_host, w_host = c.x(), c.w()
+    x = torch.from_numpy(x_host).to(torch.bfloat16).cuda()
+    wq0, ws, _ = pdq.quantize_weight(torch.from_numpy(w_host).to(torch.bfloat16).cuda())
+    nrot = 8  # 8 x 45 MB of INT8 weights + 8 x 34 MB of activations: more than the 256 MB MALL
+    wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
+    xs = [x] + [x.clone() for _ in range(nrot - 1)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xsc = torch.empty(M, dtype=torch.float32, device="cuda")
+    xqs = [xq] + [xq.clone() for _ in range(nrot - 1)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = i % nrot
+        pdq._call("pdq_linear_prefill", pdq._p(xs[r]), pdq.BF16, M, K, K, pdq._p(wqs[r]), pdq._p(ws),
+                  None, N, pdq._p(xqs[r]), pdq._p(xsc), pdq._p(y), N, None, pdq._stream(x.device))
+
+    ms_step = timed(step, args.steps, args.warmup, stream)
+
+    # the INT8 GEMM kernel alone (same launch configuration as inside the step)
+    for r in range(nrot):
+        pdq.quantize_per_token(xs[r], xq=xqs[r], x_scale=xsc)
+
+    def gemm(i):
+        r = i % nrot
+        pdq._call("pdq_gemm_per_token", pdq._p(xqs[r]), pdq._p(xsc), M, K, pdq._p(wqs[r]), pdq._p(ws),
+                  None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+    ms_gemm = timed(gemm, args.steps, args.warmup, stream)
+
+    def quant(i):
+        r = i % nrot
+        pdq._call("pdq_quantize_per_token", pdq._p(xs[r]), pdq.BF16, M, K, K, pdq._p(xqs[r]),
+                  pdq._p(xsc), pdq._stream(x.device))
+
+    ms_quant = timed(quant, args.steps, args.warmup, stream)
+    ops = 2.0 * M * N * K
+    gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+    gemm_bytes = M * K + N * K + 4 * (M + N) + 2 * M * N  # xq, wq, scales, bf16 y
+    quant_bytes = 2 * M * K + M * K + 4 * M
+    del wqs, xs, xqs
+    return dict(M=M, K=K, N=N, ms_step=ms_step, ms_gemm=ms_gemm, ms_quant=ms_quant, ops=ops,
+                gemm_tops=gemm_tops, gemm_bytes=gemm_bytes, quant_bytes=quant_bytes,
+                x_host=x_host, w_host=w_host)
+
+
+def bench_decode(args, torch, pdq, synth):
+    c = synth.Decode()
+    K, N = c.K, c.N
+    log(f"[decode] calibrating on {c.n_calib} batches of [{c.calib_tokens},{K}]")
+    mm = pdq.minmax_state("cuda")
+    for b in range(c.n_calib):
+        out = pdq.calibrate_static(torch.from_numpy(c.calib(b)).to(torch.bfloat16).cuda(), mm,
+                                   finalize=b == c.n_calib - 1)
+    s_t, z_t = out
+    s, z = float(s_t.item()), int(z_t.item())
+    wq0, ws, cs = pdq.quantize_weight(torch.from_numpy(c.w()).to(torch.bfloat16).cuda())
+    nrot = 64  # 64 x 16.8 MB = 1.07 GB of INT8 weights
+    wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
+    stream = torch.cuda.current_stream()
+    res = {}
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for m in c.batches:
+        x = torch.from_numpy(c.x(m)).to(torch.bfloat16).cuda()
+        xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+        sat.zero_()
+        pdq.linear_decode(x, s, z, wq0, ws, cs, sat_count=sat, out=y, xq=xq)
+        torch.cuda.synchronize()
+        nsat = int(sat.item())
+
+        def call(i):
+            pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(wqs[i % nrot]),
+                      pdq._p(ws), pdq._p(cs), None, N, pdq._p(xq), pdq._p(y), N, None, None,
+                      pdq._stream(x.device))
+
+        def gemv(i):
+            pdq._call("pdq_gemm_static", pdq._p(xq), m, K, s, z, pdq._p(wqs[i % nrot]), pdq._p(ws),
+                      pdq._p(cs), None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+        iters = max(args.steps * 10, 200)
+        ms_call = timed(call, iters, args.warmup * 4, stream)
+        ms_gemv = timed(gemv, iters, args.warmup * 4, stream)
+        # algorithmic bytes: int8 W once, bf16 X, bf16 Y, w_scale + colsum
+        call_bytes = N * K + 2 * m * K + 2 * m * N + 8 * N
+        gemv_bytes = N * K + m * K + 2 * m * N + 8 * N
+        res[str(m)] = dict(us_call=ms_call * 1e3, us_gemv=ms_gemv * 1e3,
+                           call_GBps=call_bytes / (ms_call * 1e-3) / 1e9,
+                           gemv_GBps=gemv_bytes / (ms_gemv * 1e-3) / 1e9,
+                           gemv_frac=gemv_bytes / (ms_gemv * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           saturated=nsat, saturated_frac=nsat / (m * K))
+    del wqs
+    return dict(S=s, Z=z, K=K, N=N, per_batch=res)
+
+
+def bench_llm_int8(args, torch, pdq, synth):
+    c = synth.LlmInt8()
+    M, K, N = c.M, c.K, c.N
+    log(f"[llm.int8] generating X[{M},{K}] and W[{N},{K}] ({c.dtype})")
+    x = torch.from_numpy(c.x()).half().cuda()
+    w16 = torch.from_numpy(c.w()).half().cuda()
+    wq0, ws, _ = pdq.quantize_weight(w16)
+    nrot = 2
+    wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
+    max_out = 64
+    ws_bytes = pdq.int8_outlier_workspace_bytes(M, N, K, max_out)
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    idx = torch.empty(max_out, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        pdq._call("pdq_linear_int8_outlier", pdq._p(x), pdq.F16, M, K, K, c.threshold,
+                  pdq._p(wqs[i % nrot]), pdq._p(ws), pdq._p(w16), K, None, N, pdq._p(y), N, pdq._p(xq),
+                  pdq._p(xs), pdq._p(idx), pdq._p(cnt), max_out, pdq._p(work), ws_bytes, None,
+                  pdq._stream(x.device))
+
+    ms = timed(call, args.steps, args.warmup, stream)
+    n_out = int(cnt.item())
+    ops = 2.0 * M * N * K
+    return dict(M=M, K=K, N=N, ms=ms, n_outlier=n_out, int8_tops=ops / (ms * 1e-3) / 1e12,
+                side_flops=2.0 * M * N * n_out)
+
+
+def cpu_baseline(pre):
+    import oracle.pdq_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x, w = pre["x_host"], pre["w_host"]
+    wq, sw, _ = O.quantize_weight(w)  # offline, not timed
+    t0 = time.perf_counter()
+    O.linear_prefill(x, wq, sw)
+    dt = time.perf_counter() - t0
+    return {"value": pre["ops"] / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full prefill linear {pre['M']}x{pre['K']}->{pre['N']} (per-token quant, "
+                      f"exact integer GEMM via a binary64 BLAS product, binary32 epilogue) in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill"], default="all")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (known HBM traffic, for "
+                         "scaling hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from w8a8_int8_quantized_absmax_amd import pdq, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pdq.lib()
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    pre = bench_prefill(args, torch, pdq, synth)
+    log(f"[prefill] step {pre['ms_step']*1e3:.1f} us (quant {pre['ms_quant']*1e3:.1f} us, "
+        f"GEMM {pre['ms_gemm']*1e3:.1f} us = {pre['gemm_tops']:.0f} TOPS)")
+    dec = llm = None
+    if args.only == "all":
+        dec = bench_decode(args, torch, pdq, synth)
+        for m, r in dec["per_batch"].items():
+            log(f"[decode] M={m}: call {r['us_call']:.2f} us, GEMV {r['us_gemv']:.2f} us = "
+                f"{r['gemv_GBps']:.0f} GB/s; saturated {r['saturated']}")
+        llm = bench_llm_int8(args, torch, pdq, synth)
+        log(f"[llm.int8] {llm['ms']*1e3:.1f} us, {llm['int8_tops']:.0f} TOPS, |O|={llm['n_outlier']}")
+
+    value = pre["ops"] / (pre["ms_step"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "prefill linear, 4096 tokens x (4096 -> 11008), bf16 in/out, per-token "
+                               "dynamic symmetric INT8 activations, per-channel INT8 weights",
+                   "M": pre["M"], "K": pre["K"], "N": pre["N"], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tops"], 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic_for(pre["gemm_bytes"]),
+                     "kernel": "k_gemm_i8 (INT8 MFMA GEMM + bf16 epilogue)",
+                     "us_per_launch": round(pre["ms_gemm"] * 1e3, 2)},
+        "prefill_quant": {"us": round(pre["ms_quant"] * 1e3, 2),
+                          "GBps": round(pre["quant_bytes"] / (pre["ms_quant"] * 1e-3) / 1e9, 1)},
+    }
+    if dec:
+        out["decode"] = {"unit": "GB/s", "peak": PEAK_HBM_GBS, "S": dec["S"], "Z": dec["Z"],
+                         "per_batch": {m: {k: round(v, 5) if isinstance(v, float) else v
+                                           for k, v in r.items()} for m, r in dec["per_batch"].items()}}
+    if llm:
+        out["llm_int8"] = {"us": round(llm["ms"] * 1e3, 1), "int8_TOPS": round(llm["int8_tops"], 1),
+                           "frac": round(llm["int8_tops"] / PEAK_INT8_TOPS, 4),
+                           "n_outlier": llm["n_outlier"], "side_GFLOP": round(llm["side_flops"] / 1e9, 3)}
+    if not args.no_cpu_baseline:
+        log("[cpu] timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(pre)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,6 +160,36 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
                              void* stream);
 
 /*
+ * Building blocks of the two PDMIX phases.  pdq_linear_prefill is
+ * pdq_quantize_per_token followed by pdq_gemm_per_token; pdq_linear_decode is
+ * pdq_quantize_static followed by pdq_gemm_static.  They are exposed for
+ * callers that quantize an activation once and feed several weight matrices
+ * with it (e.g. separate Q, K and V projections of one hidden state), or that
+ * produce the INT8 activations themselves.  Arguments as in the composite
+ * calls above; xq is dense [M, K] int8.
+ */
+/* Per-token quantizer: S_x[m] = max_k |x[m,k]| / 127, xq = clamp(rne(x / S_x), -127, 127). */
+pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                  int8_t* xq, float* x_scale, void* stream);
+
+/* INT8 GEMM + per-token epilogue: y = bf16((S_x[m] * S_w[n]) * (float)(sum_k xq wq) [+ bias[n]]). */
+pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M, int64_t K,
+                              const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
+                              uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream);
+
+/* Static quantizer: xq = clamp(rne(x / S) + Z, -128, 127); sat_count (nullable) incremented. */
+pdq_status pdq_quantize_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                               float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count,
+                               void* stream);
+
+/* Skinny INT8 GEMM + zero-point epilogue:
+ * y = bf16((S * S_w[n]) * (float)(sum_k xq wq - Z * colsum[n]) [+ bias[n]]). */
+pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale, int32_t a_zp,
+                           const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                           const float* bias, int64_t N, uint16_t* y, int64_t ldy, int32_t* acc_out,
+                           void* stream);
+
+/*
  * LLM.int8() vector-wise quantization with the 16-bit outlier decomposition.
  * [LLM.int8] part 2: outlier columns are the hidden dimensions whose
  * magnitude exceeds the threshold (6.0 in the text); the regular part is

@@ -283,3 +283,38 @@ def test_outlier_llm_int8_full_sampled():
     res, cnt = outlier_case(x, w, c.dtype, c.threshold, rows=rows)
     print(f"LLM.int8 full: {cnt} outlier columns: {host(res['idx'])[:cnt].tolist()}")
     assert cnt >= c.n_outlier_cols
+
+
+# ---------------------------------------------------------------------------
+# building blocks: quantize once, GEMM against several weights
+# ---------------------------------------------------------------------------
+
+def test_per_token_blocks_shared_activation():
+    x = synth.activations(6000, 200, 1024, [7, 900], 100.0, dtype="bf16")
+    xq, xs = pdq.quantize_per_token(dev(x, "bf16"))
+    xq_ref, sx_ref = O.quantize_rows_absmax(x)
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(xs), sx_ref)
+    for n in (96, 300):  # e.g. two projections of one hidden state
+        w = synth.weights(6001 + n, n, 1024, "bf16")
+        wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
+        rq, rs, _ = O.quantize_weight(w)
+        res = pdq.gemm_per_token(xq, xs, wq, ws, want_acc=True)
+        acc = O.int_matmul(xq_ref, rq)
+        assert np.array_equal(host(res["acc"]), acc)
+        check_16bit(host(res["y"]), O.dequantize(acc, sx_ref, rs), "bf16", exact=True)
+
+
+def test_static_blocks():
+    x = synth.activations(6100, 24, 512, [3], 100.0, offset=0.1, dtype="f16")
+    s, z = F32(1.7), -5
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xq = pdq.quantize_static(dev(x, "f16"), s, z, sat_count=sat)
+    ref_q, ref_sat = O.quantize_static(x, s, z)
+    assert np.array_equal(host(xq), ref_q) and int(host(sat)[0]) == ref_sat
+    w = synth.weights(6101, 130, 512, "f16")
+    wq, ws, cs = pdq.quantize_weight(dev(w, "f16"))
+    rq, rs, rc = O.quantize_weight(w)
+    res = pdq.gemm_static(xq, s, z, wq, ws, cs, want_acc=True)
+    acc = O.int_matmul(ref_q, rq)
+    assert np.array_equal(host(res["acc"]), acc)
+    check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc, rc, z), s, rs), "bf16", exact=True)

@@ -89,6 +89,47 @@ pdq_status pdq_calibrate_static(const void* x, pdq_dtype x_dt, int64_t M, int64_
     return launched();
 }
 
+pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                  int8_t* xq, float* x_scale, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4)) return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr,
+                      static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M, int64_t K,
+                              const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
+                              uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream) {
+    PDQ_TRY(check_operand(xq, 1, M, K, K));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N > 0 && !w_scale) return PDQ_ERR_NULL;
+    if (M > 0 && !x_scale) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) || !aligned(y, 2) ||
+        !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    if (M == 0 || N == 0) return PDQ_OK;
+    GemmArgs g{};
+    g.A = xq;
+    g.B = wq;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.sa = x_scale;
+    g.sb = w_scale;
+    g.bias = bias;
+    g.y = y;
+    g.ldy = ldy;
+    g.acc_out = acc_out;
+    launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
 pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
                               const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
                               int8_t* xq, float* x_scale, uint16_t* y, int64_t ldy,
@@ -103,22 +144,55 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
     if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
         !aligned(y, 2) || !aligned(acc_out, 4))
         return PDQ_ERR_ALIGN;
+    PDQ_TRY(pdq_quantize_per_token(x, x_dt, M, K, ldx, xq, x_scale, stream));
+    return pdq_gemm_per_token(xq, x_scale, M, K, wq, w_scale, bias, N, y, ldy, acc_out, stream);
+}
+
+pdq_status pdq_quantize_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                               float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count,
+                               void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
+        return PDQ_ERR_UNSUPPORTED;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(sat_count, 4)) return PDQ_ERR_ALIGN;
     if (M == 0) return PDQ_OK;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr, st);
-    GemmArgs g{};
-    g.A = xq;
-    g.B = wq;
-    g.M = (int)M;
-    g.N = (int)N;
-    g.K = (int)K;
-    g.sa = x_scale;
-    g.sb = w_scale;
-    g.bias = bias;
-    g.y = y;
-    g.ldy = ldy;
-    g.acc_out = acc_out;
-    launch_gemm_i8(g, PDQ_BF16, false, st);
+    launch_quant_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count,
+                        static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale, int32_t a_zp,
+                           const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                           const float* bias, int64_t N, uint16_t* y, int64_t ldy, int32_t* acc_out,
+                           void* stream) {
+    PDQ_TRY(check_operand(xq, 1, M, K, K));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
+        return PDQ_ERR_UNSUPPORTED;
+    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) || !aligned(y, 2) ||
+        !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    if (M == 0 || N == 0) return PDQ_OK;
+    DecodeArgs d{};
+    d.xq = xq;
+    d.wq = wq;
+    d.M = (int)M;
+    d.N = (int)N;
+    d.K = (int)K;
+    d.s = a_scale;
+    d.z = a_zp;
+    d.sw = w_scale;
+    d.colsum = w_colsum;
+    d.bias = bias;
+    d.y = y;
+    d.ldy = ldy;
+    d.acc_out = acc_out;
+    launch_decode_gemv(d, static_cast<hipStream_t>(stream));
     return launched();
 }
 
@@ -139,25 +213,9 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
     if (!aligned(xq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) ||
         !aligned(y, 2) || !aligned(acc_out, 4) || !aligned(sat_count, 4))
         return PDQ_ERR_ALIGN;
-    if (M == 0) return PDQ_OK;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    launch_quant_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, st);
-    DecodeArgs d{};
-    d.xq = xq;
-    d.wq = wq;
-    d.M = (int)M;
-    d.N = (int)N;
-    d.K = (int)K;
-    d.s = a_scale;
-    d.z = a_zp;
-    d.sw = w_scale;
-    d.colsum = w_colsum;
-    d.bias = bias;
-    d.y = y;
-    d.ldy = ldy;
-    d.acc_out = acc_out;
-    launch_decode_gemv(d, st);
-    return launched();
+    PDQ_TRY(pdq_quantize_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, stream));
+    return pdq_gemm_static(xq, M, K, a_scale, a_zp, wq, w_scale, w_colsum, bias, N, y, ldy, acc_out,
+                           stream);
 }
 
 size_t pdq_linear_int8_outlier_workspace(int64_t M, int64_t N, int64_t K, int64_t max_outliers) {

@@ -31,6 +31,13 @@ SIGNATURES = {
                                           _vp, _vp, _vp, _i64, _vp, _vp]),
     "pdq_linear_decode": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp,
                                          _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "pdq_quantize_per_token": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "pdq_gemm_per_token": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                          _vp]),
+    "pdq_quantize_static": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp,
+                                           _vp]),
+    "pdq_gemm_static": (ctypes.c_int, [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _vp,
+                                       _i64, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
@@ -85,13 +92,18 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_mat(t: torch.Tensor, name: str):
+def _check_mat(t: torch.Tensor, name: str, dtypes=_DT):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit stride in the last dimension")
-    if t.dtype not in _DT:
+    if t.dtype not in dtypes:
         raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row pitch in elements (a single or empty row has no meaningful stride)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 # ---------------------------------------------------------------------------
@@ -103,7 +115,7 @@ def quantize_weight(w: torch.Tensor):
     wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
     ws = torch.empty(n, dtype=torch.float32, device=w.device)
     cs = torch.empty(n, dtype=torch.int32, device=w.device)
-    _call("pdq_quantize_weight", _p(w), _DT[w.dtype], n, k, w.stride(0), _p(wq), _p(ws), _p(cs),
+    _call("pdq_quantize_weight", _p(w), _DT[w.dtype], n, k, _ld(w), _p(wq), _p(ws), _p(cs),
           _stream(w.device))
     return wq, ws, cs
 
@@ -121,7 +133,7 @@ def calibrate_static(x: torch.Tensor, minmax: torch.Tensor, finalize: bool = Fal
     if finalize:
         s = torch.empty(1, dtype=torch.float32, device=x.device)
         z = torch.empty(1, dtype=torch.int32, device=x.device)
-    _call("pdq_calibrate_static", _p(x), _DT[x.dtype], m, k, x.stride(0), _p(minmax), _p(s), _p(z),
+    _call("pdq_calibrate_static", _p(x), _DT[x.dtype], m, k, _ld(x), _p(minmax), _p(s), _p(z),
           _stream(x.device))
     return (s, z) if finalize else None
 
@@ -135,8 +147,8 @@ def linear_prefill(x, wq, w_scale, bias=None, want_acc: bool = False, out=None):
     xs = torch.empty(m, dtype=torch.float32, device=x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
-    _call("pdq_linear_prefill", _p(x), _DT[x.dtype], m, k, x.stride(0), _p(wq), _p(w_scale), _p(bias),
-          n, _p(xq), _p(xs), _p(y), y.stride(0), _p(acc), _stream(x.device))
+    _call("pdq_linear_prefill", _p(x), _DT[x.dtype], m, k, _ld(x), _p(wq), _p(w_scale), _p(bias),
+          n, _p(xq), _p(xs), _p(y), _ld(y), _p(acc), _stream(x.device))
     return dict(y=y, xq=xq, x_scale=xs, acc=acc)
 
 
@@ -149,8 +161,8 @@ def linear_decode(x, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None,
     xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
-    _call("pdq_linear_decode", _p(x), _DT[x.dtype], m, k, x.stride(0), float(a_scale), int(a_zp),
-          _p(wq), _p(w_scale), _p(colsum), _p(bias), n, _p(xq), _p(y), y.stride(0), _p(acc),
+    _call("pdq_linear_decode", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp),
+          _p(wq), _p(w_scale), _p(colsum), _p(bias), n, _p(xq), _p(y), _ld(y), _p(acc),
           _p(sat_count), _stream(x.device))
     return dict(y=y, xq=xq, acc=acc)
 
@@ -167,6 +179,7 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
     m, k = x.shape
     n = wq.shape[0]
     dev = x.device
+    max_outliers = min(max_outliers, k)
     xq = torch.empty((m, k), dtype=torch.int8, device=dev)
     xs = torch.empty(m, dtype=torch.float32, device=dev)
     idx = torch.empty(max(max_outliers, 1), dtype=torch.int32, device=dev)
@@ -176,7 +189,52 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
     need = int8_outlier_workspace_bytes(m, n, k, max_outliers)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _call("pdq_linear_int8_outlier", _p(x), _DT[x.dtype], m, k, x.stride(0), float(threshold), _p(wq),
-          _p(w_scale), _p(w16), w16.stride(0), _p(bias), n, _p(y), y.stride(0), _p(xq), _p(xs), _p(idx),
+    _call("pdq_linear_int8_outlier", _p(x), _DT[x.dtype], m, k, _ld(x), float(threshold), _p(wq),
+          _p(w_scale), _p(w16), _ld(w16), _p(bias), n, _p(y), _ld(y), _p(xq), _p(xs), _p(idx),
           _p(cnt), max_outliers, _p(workspace), workspace.numel(), _p(acc), _stream(dev))
     return dict(y=y, xq=xq, x_scale=xs, idx=idx, count=cnt, acc=acc)
+
+
+def quantize_per_token(x, xq=None, x_scale=None):
+    """Per-token dynamic symmetric INT8 -> (xq int8 [M,K], x_scale f32 [M])."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    _call("pdq_quantize_per_token", _p(x), _DT[x.dtype], m, k, _ld(x), _p(xq), _p(xs), _stream(x.device))
+    return xq, xs
+
+
+def gemm_per_token(xq, x_scale, wq, w_scale, bias=None, want_acc: bool = False, out=None):
+    """INT8 GEMM + per-token/per-channel dequant epilogue -> dict(y bf16[, acc])."""
+    _check_mat(xq, "xq", (torch.int8,))
+    m, k = xq.shape
+    n = wq.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    _call("pdq_gemm_per_token", _p(xq), _p(x_scale), m, k, _p(wq), _p(w_scale), _p(bias), n, _p(y),
+          _ld(y), _p(acc), _stream(xq.device))
+    return dict(y=y, acc=acc)
+
+
+def quantize_static(x, a_scale: float, a_zp: int, xq=None, sat_count=None):
+    """Per-tensor static asymmetric INT8 -> xq int8 [M,K]."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    _call("pdq_quantize_static", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp), _p(xq),
+          _p(sat_count), _stream(x.device))
+    return xq
+
+
+def gemm_static(xq, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None, want_acc: bool = False,
+                out=None):
+    """Skinny INT8 GEMM + zero-point correction + dequant epilogue -> dict(y bf16[, acc])."""
+    _check_mat(xq, "xq", (torch.int8,))
+    m, k = xq.shape
+    n = wq.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    _call("pdq_gemm_static", _p(xq), m, k, float(a_scale), int(a_zp), _p(wq), _p(w_scale), _p(colsum),
+          _p(bias), n, _p(y), _ld(y), _p(acc), _stream(xq.device))
+    return dict(y=y, acc=acc)
