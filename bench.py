@@ -233,8 +233,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill"], default="all")
     ap.add_argument("--copy-probe", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (known HBM traffic, for "
-                         "scaling hardware byte counters)")
+                    help="also run a fill and a plain device copy of this many MiB (known HBM "
+                         "traffic, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -248,11 +248,13 @@ def main():
     torch.cuda.set_device(0)
     pdq.lib()
     if args.copy_probe:
+        # known traffic: the fill kernel writes size bytes, the copy kernel
+        # reads size bytes and writes size bytes (far more than the 256 MB MALL)
         n = args.copy_probe * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        a = torch.empty(n, dtype=torch.float32, device="cuda")
+        a.fill_(1.0)
         b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
+        b.copy_(a)
         torch.cuda.synchronize()
         del a, b
 

@@ -12,13 +12,14 @@
 //
 // Tiling: 256x256 output tile per 256-thread workgroup (4 wavefronts in a
 // 2x2 arrangement, 128x128 each = 4x4 v_mfma_i32_32x32x32_i8 tiles with
-// their INT32 accumulators in registers), K staged through LDS 128 bytes at
-// a time.  A and B are both K-contiguous, so a K tile of 256 rows is 256
-// lines of 128 bytes; the 16-byte chunk c of row r sits at chunk c ^ (r & 7)
-// so that the 128-bit fragment reads of 8 consecutive rows hit 8 distinct
-// chunk positions.  Tiles move global -> LDS directly (global_load_lds, no
-// register staging) into two LDS buffers: tile k+1 is in flight while tile k
-// feeds the MFMAs.
+// their INT32 accumulators in registers, W rows as the MFMA row operand so
+// that each lane ends up with runs of 4 consecutive outputs), K staged through
+// LDS 64 bytes at a time.  A and B are both K-contiguous, so a K tile of 256
+// rows is 256 lines of 64 bytes, XOR-swizzled in 16-byte chunks so that the
+// 128-bit fragment reads are free of bank conflicts (see swz).  Tiles move
+// global -> LDS directly (global_load_lds, no register staging) through a
+// ring of four LDS buffers: three K tiles are in flight while one feeds the
+// MFMAs.
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -29,22 +30,64 @@ namespace pdq {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256, BK = 64;  // BK in bytes = K values per LDS stage
+constexpr int kStages = 4;                   // LDS ring: 4 x 32 KB, three K tiles in flight
+static_assert((kStages & (kStages - 1)) == 0, "ring index uses a mask");
+constexpr int kStageBytes = (BM + BN) * BK;
+// Output tile in LDS after the K loop: 256 rows of 256 16-bit values, padded
+// to 520 bytes so that the 8-byte writes of 32 lanes (32 rows, 4 values each)
+// hit 32 distinct bank pairs.
+constexpr int kYPitch = BN * 2 + 8;
+constexpr int kLdsBytes = kStages * kStageBytes > BM * kYPitch ? kStages * kStageBytes : BM * kYPitch;
 
-__device__ __forceinline__ int swz(int r, int kc) { return r * BK + ((kc ^ (r & 7)) << 4); }
+// LDS image of a K tile: row r (64 bytes) holds its 16-byte chunk kc at
+// position kc ^ ((r >> 2) & 3).  A 128-bit read instruction is served 16
+// lanes at a time over 64 four-byte banks (256 bytes = 4 rows): the 16 lanes
+// read rows r..r+15 at one logical chunk; rows r, r+1, r+2, r+3 fall in the
+// four bank quarters and, within a quarter, the 4 rows land on 4 distinct
+// chunk positions.
+__device__ __forceinline__ int swz_pos(int r, int kc) { return kc ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r, int kc) { return r * BK + (swz_pos(r, kc) << 4); }
+
+constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kGroupM = 4;   // tile rows per group of the grouped order
+
+// Tile of workgroup `bid`.  Consecutive workgroup ids land on different XCDs,
+// each with its own L2; renumber so that every XCD works through a contiguous
+// run of tiles, and walk tiles in groups of kGroupM tile rows (column by
+// column inside a group) so that the tiles resident on one XCD at a time share
+// a few A and B panels.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int num = tiles_m * tiles_n;
+    const int q = num / kXcds, r = num % kXcds;
+    const int xcd = bid % kXcds, local = bid / kXcds;
+    const int id = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    const int per_group = kGroupM * tiles_n;
+    const int g = id / per_group;
+    const int first_m = g * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int in = id - g * per_group;
+    tm = first_m + in % gsize;
+    tn = in / gsize;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int OUT, bool SIDE>
 __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
-    // Two K-tile buffers, each A[256][128] followed by B[256][128].
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2][(BM + BN) * BK];
+    // kStages K-tile buffers, each A[256][64] followed by B[256][64]; after
+    // the K loop the same memory holds the 16-bit output tile (row pitch
+    // kYPitch bytes).  The tile's row scales, column scales and bias are
+    // staged once at the start.
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) float s_sa[BM], s_sb[BN], s_bias[BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int M = a.M, N = a.N, K = a.K;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nkt = (K + BK - 1) / BK;
 
@@ -54,33 +97,43 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
+    {
+        const int m = m0 + tid, n = n0 + tid;  // 256 threads = BM = BN
+        s_sa[tid] = m < M ? a.sa[m] : 0.0f;
+        s_sb[tid] = n < N ? a.sb[n] : 0.0f;
+        s_bias[tid] = (a.bias && n < N) ? a.bias[n] : 0.0f;
+    }
+    __syncthreads();
+
+
     // Global -> LDS without registers: one global_load_lds_dwordx4 moves 64
-    // lanes x 16 bytes into 1 KB of LDS (8 rows of the tile), lane l landing in
-    // row l/8, chunk position l%8.  The lane therefore fetches logical chunk
-    // (l%8) ^ (row & 7) so that the LDS image is the swizzled layout.  Wave w
-    // fills rows [64w, 64w + 64) of both the A and the B tile.  Rows past M
-    // (N) are clamped onto the last row: they only feed outputs that are never
-    // stored.  Chunks past K are clamped onto the last chunk and zeroed in the
-    // A fragments of the last K tile, which zeroes their products.
-    const int lr = lane >> 3;
-    const int kc_ld = (lane & 7) ^ lr;
-    const int rbase = wave * 64 + lr;
-    auto issue = [&](int kt, int buf) {
-        const int gk = min(kt * BK + kc_ld * 16, K - 16);
-        uint8_t* la = &smem[buf][wave * 64 * BK];
-        uint8_t* lb = &smem[buf][BM * BK + wave * 64 * BK];
+    // lanes x 16 bytes into 1 KB of LDS (16 rows of 64 bytes), lane l landing
+    // in row l/4, chunk position l%4.  The lane fetches the logical chunk that
+    // the swizzle puts at its position (the swizzle is an involution in kc).
+    // Wave w fills rows [64w, 64w + 64) of both the A and the B tile: 4 + 4
+    // instructions per K tile.  Rows past M (N) are clamped onto the last row:
+    // they only feed outputs that are never stored.  Chunks past K are clamped
+    // onto the last chunk and zeroed in the A fragments of the last K tile,
+    // which zeroes their products.
+    const int rbase = wave * 64 + (lane >> 2);
+    // row r = rbase + 16 i has (r >> 2) & 3 == (lane >> 4) & 3 for every i
+    const int koff = swz_pos(rbase, lane & 3) * 16;
+    const int8_t* pa[4];
+    const int8_t* pb[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int gm = min(m0 + rbase + 8 * i, M - 1);
-            __builtin_amdgcn_global_load_lds(a.A + (size_t)gm * K + gk, (lds_ptr_t)(la + i * 8 * BK),
+    for (int i = 0; i < 4; ++i) {
+        pa[i] = a.A + (size_t)min(m0 + rbase + 16 * i, M - 1) * K;
+        pb[i] = a.B + (size_t)min(n0 + rbase + 16 * i, N - 1) * K;
+    }
+    // Load number `i` (0..7: A rows, then B rows) of K tile kt.
+    auto issue_one = [&](int kt, bool partial, int i) {
+        uint8_t* la = smem + (kt & (kStages - 1)) * kStageBytes + wave * 64 * BK;
+        const int gk = partial ? min(kt * BK + koff, K - 16) : kt * BK + koff;
+        if (i < 4)
+            __builtin_amdgcn_global_load_lds(pa[i] + gk, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(pb[i - 4] + gk, (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK),
                                              16, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int gn = min(n0 + rbase + 8 * i, N - 1);
-            __builtin_amdgcn_global_load_lds(a.B + (size_t)gn * K + gk, (lds_ptr_t)(lb + i * 8 * BK),
-                                             16, 0, 0);
-        }
     };
     // Fragments of one 32-wide K step: lane l reads row (l%32) of each 32-row
     // block, chunk 2*s + l/32 (16 bytes = 16 K values).
@@ -94,11 +147,13 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             fb[j] = *reinterpret_cast<const v4i*>(sbase + BM * BK +
                                                   swz(wn * 128 + j * 32 + (lane & 31), kc));
     };
-
-    // One K tile from LDS buffer `sb`: 4 steps of 32, each 16 MFMAs, with the
-    // next step's fragments read while the current step's MFMAs run.  MASK
-    // (last tile only, when K % 128 != 0) zeroes A past K.
-    auto compute = [&](const uint8_t* sb, int kvalid, auto mask) {
+    // One K tile: 2 steps of 32, each 16 MFMAs, with the next step's
+    // fragments read while the current step's MFMAs run.  When `next` >= 0
+    // the eight loads of K tile `next` are spread over the 32 MFMAs (one after
+    // every four) instead of being issued in a burst, so the wavefront keeps
+    // the matrix core fed while its memory requests trickle out.  MASK (last
+    // tile only, when K % 64 != 0) zeroes A past K.
+    auto compute = [&](const uint8_t* sb, int kvalid, auto mask, int next, bool next_partial) {
         v4i fa[2][4], fb[2][4];
         read_frags(sb, 0, fa[0], fb[0]);
 #pragma unroll
@@ -113,97 +168,122 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     if (dead) fa[cur][i] = v4i{};
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cur][i], fb[cur][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i],
                                                                       acc[i][j], 0, 0, 0);
+                if (next >= 0) issue_one(next, next_partial, 4 * s + i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
-    if (nkt > 0) issue(0, 0);
-    for (int kt = 0; kt + 1 < nkt; ++kt) {
-        const int buf = kt & 1;
-        issue(kt + 1, buf ^ 1);
-        // this wave's 16 loads of tile kt have landed; then all waves'.
-        // (__syncthreads() would also wait for tile kt+1's loads.)
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-        compute(smem[buf], BK, std::false_type{});
-        // every wave is done reading `buf` before the next iteration refills it
-        asm volatile("s_barrier" ::: "memory");
-    }
-    if (nkt > 0) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        const int kvalid = K - (nkt - 1) * BK;
-        if (kvalid >= BK)
-            compute(smem[(nkt - 1) & 1], kvalid, std::false_type{});
+    // Ring schedule: tiles 0..kStages-2 are in flight before the loop; at the
+    // top of iteration kt this wave waits for its own loads of tile kt (the
+    // loads of the tiles issued after it may stay outstanding), the barrier
+    // makes every wave's loads of tile kt visible and guarantees that every
+    // wave has finished computing tile kt-1, whose buffer then receives tile
+    // kt+kStages-1 during compute(kt).  A partial last tile (K % 64 != 0) is
+    // computed after the loop.
+    const int nfull = K / BK;
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t)
+        if (t < nkt)
+            for (int i = 0; i < 8; ++i) issue_one(t, t >= nfull, i);
+    for (int kt = 0; kt < nfull; ++kt) {
+        const int after = min(kStages - 2, nkt - 1 - kt);  // tiles issued after kt
+        if (after >= 2)
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        else if (after == 1)
+            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
         else
-            compute(smem[(nkt - 1) & 1], kvalid, std::true_type{});
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        const int next = kt + kStages - 1 < nkt ? kt + kStages - 1 : -1;
+        compute(smem + (kt & (kStages - 1)) * kStageBytes, BK, std::false_type{}, next, next >= nfull);
+    }
+    if (nkt > nfull) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        compute(smem + (nfull & (kStages - 1)) * kStageBytes, K - nfull * BK, std::true_type{}, -1, false);
     }
 
-    // Epilogue.  32x32 accumulator layout: lane l, register r holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the sub-tile.  The 16-bit
-    // results go to LDS (the 256x256 tile is exactly the 128 KB of the two
-    // K buffers) and leave in 16-byte row chunks.
-    bool poison = false;
+    // Epilogue.  acc[i][j] is the 32x32 block (W rows n, X rows m) of the
+    // wave's 128x128 tile: lane l, register r holds n = 8*(r/4) + 4*(l/32) +
+    // r%4 and m = l%32, i.e. 4 consecutive outputs of one row of y per
+    // register quad.  They are rounded, packed and written to the LDS output
+    // tile with one 8-byte write; the tile then leaves in 16-byte row chunks.
     int side_steps = 0;
+    bool poison = false;
     if constexpr (SIDE) {
         const int cnt = *a.count;
         poison = cnt > a.max_count;
         side_steps = poison ? 0 : (cnt + 15) / 16;
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    uint16_t* sY = reinterpret_cast<uint16_t*>(&smem[0][0]);
-    const int ml0 = wm * 128 + 4 * (lane >> 5), nl0 = wn * 128 + (lane & 31);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring no longer read
+    const bool has_bias = a.bias != nullptr;
+    const int ml0 = wm * 128 + (lane & 31);
+    const int nl0 = wn * 128 + 4 * (lane >> 5);
+    float sam[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float sam[16];
+    for (int i = 0; i < 4; ++i) sam[i] = s_sa[ml0 + 32 * i];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = m0 + ml0 + i * 32 + 8 * (r >> 2) + (r & 3);
-            sam[r] = m < M ? a.sa[m] : 0.0f;
-        }
+    for (int j = 0; j < 4; ++j) {
+        float sbv[4][4], bv[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int nl = nl0 + j * 32;
-            const int n = n0 + nl;
-            const bool nvalid = n < N;
-            const float sbn = nvalid ? a.sb[n] : 0.0f;
-            const float bn = (a.bias && nvalid) ? a.bias[n] : 0.0f;
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
+                bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ml = ml0 + 32 * i;
             v16f side = v16f{};
             if constexpr (SIDE) {
-                const int xm = m0 + wm * 128 + i * 32 + (lane & 31);
+                // 16-bit product of the outlier columns for this 32x32 block,
+                // in the same (n, m) orientation: W_out rows x X_out rows.
+                const int m = m0 + ml;
+                const int wr = n0 + wn * 128 + 32 * j + (lane & 31);
                 for (int ks = 0; ks < side_steps; ++ks) {
                     const int koff = ks * 16 + 8 * (lane >> 5);
                     uint4 xv = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
-                    if (xm < M) xv = *reinterpret_cast<const uint4*>(a.xo + (size_t)xm * a.P + koff);
-                    if (nvalid) wv = *reinterpret_cast<const uint4*>(a.wo + (size_t)n * a.P + koff);
+                    if (m < M) xv = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
+                    if (wr < N) wv = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
                     if constexpr (OUT == kF16)
-                        side = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, xv),
-                                                                      __builtin_bit_cast(v8h, wv),
+                        side = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wv),
+                                                                      __builtin_bit_cast(v8h, xv),
                                                                       side, 0, 0, 0);
                     else
-                        side = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xv),
-                                                                       __builtin_bit_cast(v8bf, wv),
+                        side = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, wv),
+                                                                       __builtin_bit_cast(v8bf, xv),
                                                                        side, 0, 0, 0);
                 }
             }
-            if (a.acc_out && nvalid) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + ml0 + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (m < M) a.acc_out[(size_t)m * N + n] = acc[i][j][r];
+            for (int g = 0; g < 4; ++g) {
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = __fmul_rn(sam[i], sbv[g][e]);
+                    float v = __fmul_rn(t, (float)acc[i][j][4 * g + e]);
+                    if constexpr (SIDE) v = __fadd_rn(v, side[4 * g + e]);
+                    if (has_bias) v = __fadd_rn(v, bv[g][e]);
+                    if (poison) v = __builtin_nanf("");
+                    o[e] = OUT == kF16 ? f32_to_f16(v) : f32_to_bf16(v);
                 }
-            }
+                const int nl = nl0 + 32 * j + 8 * g;
+                *reinterpret_cast<uint2*>(smem + ml * kYPitch + nl * 2) =
+                    make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+                if (a.acc_out) {
+                    const int m = m0 + ml, n = n0 + nl;
+                    if (m < M) {
+                        int32_t* ap = a.acc_out + (size_t)m * N + n;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ml = ml0 + i * 32 + 8 * (r >> 2) + (r & 3);
-                const float t = __fmul_rn(sam[r], sbn);
-                float y = __fmul_rn(t, (float)acc[i][j][r]);
-                if constexpr (SIDE) y = __fadd_rn(y, side[r]);
-                if (a.bias) y = __fadd_rn(y, bn);
-                if (poison) y = __builtin_nanf("");
-                sY[ml * BN + nl] = OUT == kF16 ? f32_to_f16(y) : f32_to_bf16(y);
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) ap[e] = acc[i][j][4 * g + e];
+                    }
+                }
             }
         }
     }
@@ -212,16 +292,21 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // chunks of a row.
     uint16_t* y = static_cast<uint16_t*>(a.y);
     const bool vec = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (a.ldy % 8 == 0);
+#pragma unroll 4
     for (int c = tid; c < BM * (BN / 8); c += 256) {
         const int ml = c >> 5, nl = (c & 31) * 8;
         const int m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
+        const uint2* src = reinterpret_cast<const uint2*>(smem + ml * kYPitch + nl * 2);
+        const uint2 lo = src[0], hi = src[1];
         uint16_t* dst = y + (size_t)m * a.ldy + n;
-        const uint16_t* src = sY + ml * BN + nl;
         if (vec && n + 8 <= N) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
-            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = src[e];
+            const uint16_t v[8] = {(uint16_t)lo.x, (uint16_t)(lo.x >> 16), (uint16_t)lo.y,
+                                   (uint16_t)(lo.y >> 16), (uint16_t)hi.x, (uint16_t)(hi.x >> 16),
+                                   (uint16_t)hi.y, (uint16_t)(hi.y >> 16)};
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = v[e];
         }
     }
 }

@@ -42,12 +42,10 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// binary32 -> bfloat16, round to nearest, ties to even (NaN stays NaN).
+// binary32 -> bfloat16, round to nearest, ties to even (NaN stays NaN): the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // binary32 -> binary16, round to nearest even (the hardware conversion).
