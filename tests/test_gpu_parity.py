@@ -318,3 +318,49 @@ def test_static_blocks():
     acc = O.int_matmul(ref_q, rq)
     assert np.array_equal(host(res["acc"]), acc)
     check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc, rc, z), s, rs), "bf16", exact=True)
+
+
+# ---------------------------------------------------------------------------
+# rounding at and around the ties: inputs at (k + 1/2) S and a few ulps away
+# ---------------------------------------------------------------------------
+
+def _near_ties(s, kmax, ulps=3):
+    k = np.arange(-kmax, kmax, dtype=np.float64)
+    base = ((k + 0.5) * np.float64(s)).astype(F32)
+    vals = [base]
+    up, down = base.copy(), base.copy()
+    for _ in range(ulps):
+        up = np.nextafter(up, F32(np.inf))
+        down = np.nextafter(down, F32(-np.inf))
+        vals += [up, down]
+    return np.concatenate(vals).astype(F32)
+
+
+def test_per_token_rounding_near_ties():
+    rows = []
+    for c in (127.0, 1.0, 3.3, 0.021, 5e4, 2.0):
+        s = F32(F32(c) / F32(127))
+        v = _near_ties(s, 127)
+        v = v[np.abs(v) < F32(c)]
+        row = np.zeros(4096, F32)
+        row[: v.size] = v
+        row[-1] = F32(c)  # the row absmax is exactly c
+        rows.append(row)
+    x = np.stack(rows)
+    xq, xs = pdq.quantize_per_token(dev(x, "f32"))
+    q_ref, s_ref = O.quantize_rows_absmax(x)
+    assert np.array_equal(host(xs), s_ref)
+    assert np.array_equal(host(xq), q_ref)
+
+
+@pytest.mark.parametrize("s", [0.5, 3.3963, 0.0078125, 17.25, 1e-3])
+def test_static_rounding_near_ties(s):
+    s = F32(s)
+    v = _near_ties(s, 700)  # reaches well past the clamp on both sides
+    v = v[: (v.size // 16) * 16].reshape(-1, 16)
+    for z in (0, -3, 100, -128):
+        sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+        xq = pdq.quantize_static(dev(v, "f32"), s, z, sat_count=sat)
+        q_ref, sat_ref = O.quantize_static(v, s, z)
+        assert np.array_equal(host(xq), q_ref)
+        assert int(host(sat)[0]) == sat_ref

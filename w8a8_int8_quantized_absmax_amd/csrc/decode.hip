@@ -10,10 +10,11 @@
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
 // bandwidth-bound).  Each 256-thread workgroup owns 16 weight rows and up to 64
 // activation rows; its four wavefronts interleave over the K dimension in
-// 64-byte steps and issue all of a batch's weight loads before the first
-// v_mfma_i32_16x16x64_i8, so that the whole 16 x K weight panel is in flight
-// at once.  The activations (already quantized, a few hundred KB at most) come
-// from the L2.  The four partial accumulators are summed through LDS.
+// 64-byte steps.  Weight and activation fragments (the activations are already
+// quantized, a few hundred KB at most, and come from the L2) are loaded a
+// batch at a time, all before the batch's first v_mfma_i32_16x16x64_i8, with
+// the next batch in flight during the current one's MFMAs.  The four partial
+// accumulators are summed through LDS.
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -24,48 +25,79 @@ namespace {
 
 constexpr int kRows = 16;   // weight rows per workgroup
 constexpr int kMRows = 64;  // activation rows per workgroup
-constexpr int kBatch = 16;  // 64-byte K steps per wavefront per batch of loads
+
+// 64-byte K steps per batch: a batch's weight and activation fragments are all
+// loaded before its first MFMA, and the next batch's loads are in flight while
+// this batch computes (two register sets).  (1 + NMB) * KB fragments of 16
+// bytes per lane per set.
+template <int NMB>
+struct DecodeBatch {
+    static constexpr int KB = NMB == 1 ? 8 : (NMB == 2 ? 6 : 4);
+};
 
 template <int NMB>
 __global__ __launch_bounds__(256) void k_decode_gemv(DecodeArgs a) {
+    constexpr int KB = DecodeBatch<NMB>::KB;
     __shared__ v4i red[4][NMB][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = a.M, N = a.N, K = a.K;
     const int n0 = blockIdx.x * kRows;
     const int mbase = blockIdx.y * kMRows;
     const int nsteps = (K + 63) / 64;
-    const int wrow = n0 + (lane & 15);
     const int kl = 16 * (lane >> 4);
+    const int wrow = n0 + (lane & 15);
     const bool wvalid = wrow < N;
     const int8_t* wp = a.wq + (size_t)(wvalid ? wrow : 0) * K + kl;
+    const int8_t* xp[NMB];
+    bool xvalid[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        const int xm = mbase + mb * 16 + (lane & 15);
+        xvalid[mb] = xm < M;
+        xp[mb] = a.xq + (size_t)(xvalid[mb] ? xm : 0) * K + kl;
+    }
+    // wave w takes the steps s = w + 4 t, t = 0, 1, ...; batch b holds t in
+    // [b KB, b KB + KB)
+    const int tsteps = (nsteps - wave + 3) / 4;
+    const int nbatch = (tsteps + KB - 1) / KB;
 
+    struct Frags {
+        uint4 w[KB];
+        uint4 x[NMB][KB];
+    };
+    auto load = [&](int b, Frags& f) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const int s = wave + 4 * (b * KB + i);
+            const bool kin = s < nsteps && s * 64 + kl < K;
+            f.w[i] = (wvalid && kin) ? *reinterpret_cast<const uint4*>(wp + (size_t)s * 64)
+                                     : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+                f.x[mb][i] = (xvalid[mb] && kin) ? *reinterpret_cast<const uint4*>(xp[mb] + (size_t)s * 64)
+                                                 : make_uint4(0, 0, 0, 0);
+        }
+    };
     v4i acc[NMB];
 #pragma unroll
-    for (int b = 0; b < NMB; ++b) acc[b] = v4i{};
-
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * kBatch) {
-        uint4 wv[kBatch];
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] = v4i{};
+    auto compute = [&](const Frags& f) {
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int s = s0 + 4 * b;
-            wv[b] = (wvalid && s < nsteps && s * 64 + kl < K)
-                        ? *reinterpret_cast<const uint4*>(wp + (size_t)s * 64)
-                        : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < KB; ++i)
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int s = s0 + 4 * b;
-            const int k = s * 64 + kl;
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                const int xm = mbase + mb * 16 + (lane & 15);
-                const uint4 xv = (xm < M && s < nsteps && k < K)
-                                     ? *reinterpret_cast<const uint4*>(a.xq + (size_t)xm * K + k)
-                                     : make_uint4(0, 0, 0, 0);
-                acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, wv[b]),
-                                                                __builtin_bit_cast(v4i, xv),
+            for (int mb = 0; mb < NMB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, f.w[i]),
+                                                                __builtin_bit_cast(v4i, f.x[mb][i]),
                                                                 acc[mb], 0, 0, 0);
-            }
+    };
+    Frags f0, f1;
+    if (nbatch > 0) load(0, f0);
+    for (int b = 0; b < nbatch; b += 2) {
+        if (b + 1 < nbatch) load(b + 1, f1);
+        compute(f0);
+        if (b + 1 < nbatch) {
+            if (b + 2 < nbatch) load(b + 2, f0);
+            compute(f1);
         }
     }
 

@@ -117,11 +117,32 @@ __device__ __forceinline__ int wave_sum(int v) {
 // Symmetric step size from an absmax: S = C / 127 (correctly rounded), 1 if C == 0.
 __device__ __forceinline__ float absmax_step(float c) { return c == 0.0f ? 1.0f : c / 127.0f; }
 
-// Symmetric code: clamp(rne(x / S), -127, 127) with a correctly rounded quotient.
-__device__ __forceinline__ int sym_code(float x, float s) {
-    float r = __builtin_rintf(x / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+// rne(fl(x[j] / s)) for 8 values, bit-identical to rounding the correctly
+// rounded quotients, given inv = fl(1 / s) (itself correctly rounded).
+// a = fl(x * inv) differs from x / s by at most (2^-23 + 2^-48) |x / s|
+// (reciprocal error plus one rounding) and fl(x / s) from x / s by at most
+// 2^-24 |x / s|, so |a - fl(x / s)| <= 3 * 2^-24 * |x / s| < 2^-12 for
+// |x / s| <= 1365.  Unless a lies within 2^-12 of a half-integer, a and
+// fl(x / s) round to the same integer (and neither is a tie).  When any value
+// of any lane of the wavefront is that close, the whole chunk takes the exact
+// division instead (a wavefront-uniform branch, rarely taken).  Beyond
+// |x / s| = 1365 every caller clamps the code, and a and fl(x / s) have the
+// same sign and both exceed 512 in magnitude.  A multiply, a floor and a
+// compare per value replace the ~10-instruction division sequence.
+__device__ __forceinline__ void rne_quotient8(const float (&x)[8], float s, float inv, float (&r)[8]) {
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        r[j] = x[j] * inv;
+        const float h = r[j] - __builtin_floorf(r[j]);  // fractional part, error <= 2^-24
+        near |= fabsf(h - 0.5f) <= 0x1p-12f;
+    }
+    if (__builtin_expect(__any(near), 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = x[j] / s;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = __builtin_rintf(r[j]);
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {

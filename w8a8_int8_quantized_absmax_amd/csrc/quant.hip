@@ -28,6 +28,7 @@ namespace pdq {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, four per workgroup
+constexpr int64_t kQuantBlocks = 512;  // 2 per CU on 256 CUs
 
 template <bool SKIP>
 __device__ __forceinline__ uint32_t skip_mask(const uint32_t* __restrict__ flags, int chunk) {
@@ -54,21 +55,25 @@ __device__ __forceinline__ float chunk_absmax(const Raw8<DT>& r, uint32_t skipm,
 }
 
 template <int DT>
-__device__ __forceinline__ uint2 chunk_codes(const Raw8<DT>& r, uint32_t skipm, float s, int& csum) {
-    float v[8];
+__device__ __forceinline__ uint2 chunk_codes(const Raw8<DT>& r, uint32_t skipm, float s, float inv,
+                                             int& csum) {
+    float v[8], q[8];
     widen8<DT>(r, v);
+    rne_quotient8(v, s, inv, q);
     int c[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        c[j] = ((skipm >> j) & 1u) ? 0 : sym_code(v[j], s);
+        c[j] = ((skipm >> j) & 1u) ? 0 : (int)fminf(fmaxf(q[j], -127.0f), 127.0f);
         csum += c[j];
     }
     return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
 }
 
 // CPL > 0: each lane keeps CPL chunks of 8 elements in registers (one HBM
-// read).  CPL == 0: rows too long for registers are streamed twice (the
-// second pass hits the L2).
+// read).  Wavefronts stride over the rows and load row r + stride while they
+// quantize row r, so reads, arithmetic and writes of different rows overlap.
+// CPL == 0: rows too long for registers are streamed twice (the second pass
+// hits the L2).
 template <int DT, int CPL, bool SKIP, bool COLSUM>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
@@ -76,51 +81,77 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                                                     int32_t* __restrict__ colsum,
                                                     const uint32_t* __restrict__ skip) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+    int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;  // whole wavefront leaves together
-    const char* xr = static_cast<const char*>(x) + row * ld_bytes;
-    uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+    auto row_ptr = [&](int64_t r) { return static_cast<const char*>(x) + r * ld_bytes; };
 
-    float amax = 0.0f;
-    int csum = 0;
-    float s;
     if constexpr (CPL > 0) {
-        Raw8<DT> raw[CPL];
+        Raw8<DT> raw[CPL], nxt[CPL];
         uint32_t sk[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            raw[i] = c < nch ? load_raw8<DT>(xr, c) : zero_raw8<DT>();
+            raw[i] = c < nch ? load_raw8<DT>(row_ptr(row), c) : zero_raw8<DT>();
             sk[i] = c < nch ? skip_mask<SKIP>(skip, c) : 0u;
         }
+        for (; row < rows; row += stride) {
+            const bool more = row + stride < rows;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
-        amax = wave_max(amax);
-        s = absmax_step(amax);
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + 64 * i;
+                nxt[i] = (more && c < nch) ? load_raw8<DT>(row_ptr(row + stride), c) : zero_raw8<DT>();
+            }
+            float amax = 0.0f;
+            int csum = 0;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
-            if (c < nch) qr[c] = chunk_codes<DT>(raw[i], sk[i], s, csum);
+            for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+            amax = wave_max(amax);
+            const float s = absmax_step(amax);
+            const float inv = 1.0f / s;
+            uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + 64 * i;
+                if (c < nch) qr[c] = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
+            }
+            if (lane == 0) scale[row] = s;
+            if constexpr (COLSUM) {
+                csum = wave_sum(csum);
+                if (lane == 0) colsum[row] = csum;
+            }
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) raw[i] = nxt[i];
         }
     } else {
-        for (int c = lane; c < nch; c += 64)
-            amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
-        amax = wave_max(amax);
-        s = absmax_step(amax);
-        for (int c = lane; c < nch; c += 64)
-            qr[c] = chunk_codes<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), s, csum);
-    }
-    if (lane == 0) scale[row] = s;
-    if constexpr (COLSUM) {
-        csum = wave_sum(csum);
-        if (lane == 0) colsum[row] = csum;
+        for (; row < rows; row += stride) {
+            const char* xr = row_ptr(row);
+            float amax = 0.0f;
+            int csum = 0;
+            for (int c = lane; c < nch; c += 64)
+                amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
+            amax = wave_max(amax);
+            const float s = absmax_step(amax);
+            const float inv = 1.0f / s;
+            uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+            for (int c = lane; c < nch; c += 64)
+                qr[c] = chunk_codes<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), s, inv, csum);
+            if (lane == 0) scale[row] = s;
+            if constexpr (COLSUM) {
+                csum = wave_sum(csum);
+                if (lane == 0) colsum[row] = csum;
+            }
+        }
     }
 }
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                     int32_t* colsum, const uint32_t* skip, hipStream_t st) {
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    // two workgroups (eight wavefronts) per CU, each wavefront striding over rows
+    int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (blocks > kQuantBlocks) blocks = kQuantBlocks;
+    const dim3 grid((unsigned)blocks);
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
     if (skip) {
@@ -164,17 +195,18 @@ __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x
                                                       int8_t* __restrict__ q, float s, int z,
                                                       uint32_t* __restrict__ sat) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const float inv = 1.0f / s;
     int nsat = 0;
     if (c < total) {
         const int64_t row = c / nch;
         const int col = (int)(c - row * nch);
-        float v[8];
+        float v[8], rq[8];
         widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
+        rne_quotient8(v, s, inv, rq);
         int code[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float r = __builtin_rintf(v[j] / s);
-            r = fminf(fmaxf(r, -512.0f), 512.0f);  // keeps the int conversion in range
+            const float r = fminf(fmaxf(rq[j], -512.0f), 512.0f);  // keeps the int conversion in range
             const int ri = (int)r + z;
             nsat += (ri < -128) | (ri > 127);
             code[j] = min(max(ri, -128), 127);
