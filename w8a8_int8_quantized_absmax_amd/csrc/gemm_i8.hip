@@ -36,9 +36,9 @@ static_assert((kStages & (kStages - 1)) == 0, "ring index uses a mask");
 constexpr int kStageBytes = (BM + BN) * BK;
 // Output tile in LDS after the K loop: 256 rows of 256 16-bit values, padded
 // to 520 bytes so that the 8-byte writes of 32 lanes (32 rows, 4 values each)
-// hit 32 distinct bank pairs.
+// hit 32 distinct bank pairs; rows [64 s, 64 s + 64) live in stage buffer s.
 constexpr int kYPitch = BN * 2 + 8;
-constexpr int kLdsBytes = kStages * kStageBytes > BM * kYPitch ? kStages * kStageBytes : BM * kYPitch;
+constexpr int kStageAlloc = kStageBytes > 64 * kYPitch ? kStageBytes : 64 * kYPitch;
 
 // LDS image of a K tile: row r (64 bytes) holds its 16-byte chunk kc at
 // position kc ^ ((r >> 2) & 3).  A 128-bit read instruction is served 16
@@ -73,14 +73,48 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// s_waitcnt immediate (gfx9 layout): at most `vm` vector-memory loads and
+// `lgkm` LDS operations of this wave still outstanding, export count untouched.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Wait until at most VM of this wave's K-tile loads are in flight and all its
+// LDS reads have returned, then join the workgroup barrier.  Written with the
+// builtins rather than assembly so that the compiler sees the wait: its own
+// waits before the LDS reads that follow then only cover loads that are really
+// still outstanding (with an opaque wait it assumes every earlier
+// global -> LDS load may still be writing and drains them all).  The empty
+// asm statements keep the compiler from moving memory accesses across.
+template <int VM>
+__device__ __forceinline__ void wait_loads_and_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int OUT, bool SIDE>
 __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
-    // kStages K-tile buffers, each A[256][64] followed by B[256][64]; after
-    // the K loop the same memory holds the 16-bit output tile (row pitch
-    // kYPitch bytes).  The tile's row scales, column scales and bias are
-    // staged once at the start.
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+    // The four K-tile buffers (each A[256][64] followed by B[256][64]) are
+    // four separate LDS objects, and every access below names its buffer
+    // statically (the K loop is unrolled by four).  The compiler then knows
+    // that fragment reads of one buffer do not alias the global->LDS loads in
+    // flight into the others and waits only for the loads of the buffer it
+    // reads; with one array it has to drain every load in flight first.
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageAlloc];
+    // the tile's row scales, column scales and bias, staged once at the start
     __shared__ __attribute__((aligned(16))) float s_sa[BM], s_sb[BN], s_bias[BN];
+    auto stage = [&](auto idx) -> uint8_t* {
+        constexpr int i = decltype(idx)::value & (kStages - 1);
+        if constexpr (i == 0) return st0;
+        else if constexpr (i == 1) return st1;
+        else if constexpr (i == 2) return st2;
+        else return st3;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -125,9 +159,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         pa[i] = a.A + (size_t)min(m0 + rbase + 16 * i, M - 1) * K;
         pb[i] = a.B + (size_t)min(n0 + rbase + 16 * i, N - 1) * K;
     }
-    // Load number `i` (0..7: A rows, then B rows) of K tile kt.
-    auto issue_one = [&](int kt, bool partial, int i) {
-        uint8_t* la = smem + (kt & (kStages - 1)) * kStageBytes + wave * 64 * BK;
+    // Load number `i` (0..7: A rows, then B rows) of K tile kt into `buf`.
+    auto issue_one = [&](uint8_t* buf, int kt, bool partial, int i) {
+        uint8_t* la = buf + wave * 64 * BK;
         const int gk = partial ? min(kt * BK + koff, K - 16) : kt * BK + koff;
         if (i < 4)
             __builtin_amdgcn_global_load_lds(pa[i] + gk, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
@@ -147,65 +181,93 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             fb[j] = *reinterpret_cast<const v4i*>(sbase + BM * BK +
                                                   swz(wn * 128 + j * 32 + (lane & 31), kc));
     };
-    // One K tile: 2 steps of 32, each 16 MFMAs, with the next step's
-    // fragments read while the current step's MFMAs run.  When `next` >= 0
-    // the eight loads of K tile `next` are spread over the 32 MFMAs (one after
-    // every four) instead of being issued in a burst, so the wavefront keeps
-    // the matrix core fed while its memory requests trickle out.  MASK (last
-    // tile only, when K % 64 != 0) zeroes A past K.
-    auto compute = [&](const uint8_t* sb, int kvalid, auto mask, int next, bool next_partial) {
-        v4i fa[2][4], fb[2][4];
-        read_frags(sb, 0, fa[0], fb[0]);
+    auto mfma = [&](const v4i (&fa)[4], const v4i (&fb)[4], int i, int j) {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    };
+    // A past K (last tile only, when K % 64 != 0): zeroed fragments give zero
+    // products whatever B holds there.
+    auto mask_a = [&](v4i (&fa)[4], int s, int kvalid) {
+        if ((2 * s + (lane >> 5)) * 16 >= kvalid)
 #pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < BK / 32) read_frags(sb, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
-            __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
-            if constexpr (decltype(mask)::value) {
-                const bool dead = (2 * s + (lane >> 5)) * 16 >= kvalid;
+            for (int i = 0; i < 4; ++i) fa[i] = v4i{};
+    };
+    // K loop.  Each 64-byte K tile is two steps of 16 MFMAs on register set
+    // f0 (step 0) and f1 (step 1).  Step 0 reads step 1's fragments and spreads
+    // the 8 loads of tile kt+3 (into the buffer tile kt-1 used) over its MFMAs.
+    // Step 1 runs one MFMA, then this wave waits for its loads of tile kt+1 and
+    // joins the barrier: past it every wave holds tile kt's step-1 fragments in
+    // registers (so buffer kt may be refilled) and every wave's loads of tile
+    // kt+1 have landed, so step 0 of tile kt+1 is read during the remaining 15
+    // MFMAs.  One barrier per tile, and no LDS latency exposed between tiles.
+    //
+    // Every tile issues exactly 8 loads per wave, also past the last tile
+    // (those re-load the last tile into a buffer nobody reads again), so the
+    // number of loads in flight is the same on every path and each wait below
+    // -- and each wait the compiler derives for the LDS reads -- is exact.
+    const int nfull = K / BK;
+    v4i f0a[4], f0b[4], f1a[4], f1b[4];
+    auto issue_tile = [&](uint8_t* buf, int t, int i) {
+        const int te = min(t, nkt - 1);
+        issue_one(buf, te, te >= nfull, i);
+    };
+    if (nkt > 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (dead) fa[cur][i] = v4i{};
-            }
+        for (int i = 0; i < 8; ++i) issue_tile(st0, 0, i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) issue_tile(st1, 1, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue_tile(st2, 2, i);
+        wait_loads_and_sync<16>();
+        read_frags(st0, 0, f0a, f0b);
+        auto body = [&](auto S, int kt) {
+            constexpr int s0 = decltype(S)::value;
+            const uint8_t* sb = stage(std::integral_constant<int, s0>{});
+            const uint8_t* sn = stage(std::integral_constant<int, s0 + 1>{});
+            uint8_t* sd = stage(std::integral_constant<int, s0 + kStages - 1>{});
+            const int kvalid = K - kt * BK;
+            const int next = kt + kStages - 1;
+            read_frags(sb, 1, f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kvalid < BK) mask_a(f0a, 0, kvalid);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    mfma(f0a, f0b, i, j);
+                    if (j & 1) issue_tile(sd, next, 2 * i + (j >> 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            if (kvalid < BK) mask_a(f1a, 1, kvalid);
+            mfma(f1a, f1b, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // Loads issued after tile kt+1's: tiles kt+2 and kt+3.  Also after
+            // the last tile (tile kt+1 then re-loads the last one), so that the
+            // wait is on every path and the compiler's count stays exact.
+            wait_loads_and_sync<16>();
+            read_frags(sn, 0, f0a, f0b);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i],
-                                                                      acc[i][j], 0, 0, 0);
-                if (next >= 0) issue_one(next, next_partial, 4 * s + i);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                    if (i | j) mfma(f1a, f1b, i, j);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        int kt = 0;
+        for (; kt + 4 <= nkt; kt += 4) {
+            body(I0{}, kt);
+            body(I1{}, kt + 1);
+            body(I2{}, kt + 2);
+            body(I3{}, kt + 3);
         }
-    };
-
-    // Ring schedule: tiles 0..kStages-2 are in flight before the loop; at the
-    // top of iteration kt this wave waits for its own loads of tile kt (the
-    // loads of the tiles issued after it may stay outstanding), the barrier
-    // makes every wave's loads of tile kt visible and guarantees that every
-    // wave has finished computing tile kt-1, whose buffer then receives tile
-    // kt+kStages-1 during compute(kt).  A partial last tile (K % 64 != 0) is
-    // computed after the loop.
-    const int nfull = K / BK;
-#pragma unroll
-    for (int t = 0; t < kStages - 1; ++t)
-        if (t < nkt)
-            for (int i = 0; i < 8; ++i) issue_one(t, t >= nfull, i);
-    for (int kt = 0; kt < nfull; ++kt) {
-        const int after = min(kStages - 2, nkt - 1 - kt);  // tiles issued after kt
-        if (after >= 2)
-            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-        else if (after == 1)
-            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        const int next = kt + kStages - 1 < nkt ? kt + kStages - 1 : -1;
-        compute(smem + (kt & (kStages - 1)) * kStageBytes, BK, std::false_type{}, next, next >= nfull);
-    }
-    if (nkt > nfull) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        compute(smem + (nfull & (kStages - 1)) * kStageBytes, K - nfull * BK, std::true_type{}, -1, false);
-    }
+        const int rem = nkt - kt;  // tile kt sits in buffer 0
+        if (rem > 0) body(I0{}, kt);
+        if (rem > 1) body(I1{}, kt + 1);
+        if (rem > 2) body(I2{}, kt + 2);
+    }  // nkt > 0
 
     // Epilogue.  acc[i][j] is the 32x32 block (W rows n, X rows m) of the
     // wave's 128x128 tile: lane l, register r holds n = 8*(r/4) + 4*(l/32) +
@@ -219,7 +281,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         poison = cnt > a.max_count;
         side_steps = poison ? 0 : (cnt + 15) / 16;
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring no longer read
+    wait_loads_and_sync<0>();  // the ring is no longer read or written
+    auto yrow = [&](int ml) -> uint8_t* {
+        uint8_t* b = ml < 128 ? (ml < 64 ? st0 : st1) : (ml < 192 ? st2 : st3);
+        return b + (ml & 63) * kYPitch;
+    };
     const bool has_bias = a.bias != nullptr;
     const int ml0 = wm * 128 + (lane & 31);
     const int nl0 = wn * 128 + 4 * (lane >> 5);
@@ -273,7 +339,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     o[e] = OUT == kF16 ? f32_to_f16(v) : f32_to_bf16(v);
                 }
                 const int nl = nl0 + 32 * j + 8 * g;
-                *reinterpret_cast<uint2*>(smem + ml * kYPitch + nl * 2) =
+                *reinterpret_cast<uint2*>(yrow(ml) + nl * 2) =
                     make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
                 if (a.acc_out) {
                     const int m = m0 + ml, n = n0 + nl;
@@ -297,7 +363,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         const int ml = c >> 5, nl = (c & 31) * 8;
         const int m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
-        const uint2* src = reinterpret_cast<const uint2*>(smem + ml * kYPitch + nl * 2);
+        const uint2* src = reinterpret_cast<const uint2*>(yrow(ml) + nl * 2);
         const uint2 lo = src[0], hi = src[1];
         uint16_t* dst = y + (size_t)m * a.ldy + n;
         if (vec && n + 8 <= N) {
