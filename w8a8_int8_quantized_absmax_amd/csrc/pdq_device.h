@@ -102,6 +102,27 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Maximum over all 64 lanes through DPP row permutations (quad swaps, then
+// the half-row and row mirrors leave every lane of a 16-lane row holding the
+// row maximum) and four lane reads, instead of a chain of LDS-routed
+// shuffles.  Every lane of the wavefront must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_max_full(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
@@ -121,28 +142,31 @@ __device__ __forceinline__ float absmax_step(float c) { return c == 0.0f ? 1.0f 
 // rounded quotients, given inv = fl(1 / s) (itself correctly rounded).
 // a = fl(x * inv) differs from x / s by at most (2^-23 + 2^-48) |x / s|
 // (reciprocal error plus one rounding) and fl(x / s) from x / s by at most
-// 2^-24 |x / s|, so |a - fl(x / s)| <= 3 * 2^-24 * |x / s| < 2^-12 for
-// |x / s| <= 1365.  Unless a lies within 2^-12 of a half-integer, a and
-// fl(x / s) round to the same integer (and neither is a tie).  When any value
-// of any lane of the wavefront is that close, the whole chunk takes the exact
-// division instead (a wavefront-uniform branch, rarely taken).  Beyond
-// |x / s| = 1365 every caller clamps the code, and a and fl(x / s) have the
-// same sign and both exceed 512 in magnitude.  A multiply, a floor and a
-// compare per value replace the ~10-instruction division sequence.
+// 2^-24 |x / s|, so |a - fl(x / s)| <= 3 * 2^-24 * |x / s|, which is below the
+// window w = 2^-15 when |x / s| <= 128 (kSmall: every absmax-scaled value) and
+// below w = 2^-12 when |x / s| <= 1365.  Unless a lies within w of a
+// half-integer -- i.e. unless |a - rint(a)| >= 1/2 - w, a subtraction that is
+// exact -- a and fl(x / s) round to the same integer (and neither is a tie).
+// When any value of any lane of the wavefront is that close, the whole chunk
+// takes the exact division instead (a wavefront-uniform branch, rarely
+// taken).  Without kSmall, beyond |x / s| = 1365 every caller clamps the code,
+// and a and fl(x / s) have the same sign and both exceed 512 in magnitude.  A
+// multiply, a subtraction and half a max per value replace the ~10-instruction
+// division sequence.
+template <bool kSmall>
 __device__ __forceinline__ void rne_quotient8(const float (&x)[8], float s, float inv, float (&r)[8]) {
-    bool near = false;
+    constexpr float kEdge = 0.5f - (kSmall ? 0x1p-15f : 0x1p-12f);
+    float dmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        r[j] = x[j] * inv;
-        const float h = r[j] - __builtin_floorf(r[j]);  // fractional part, error <= 2^-24
-        near |= fabsf(h - 0.5f) <= 0x1p-12f;
+        const float a = x[j] * inv;
+        r[j] = __builtin_rintf(a);
+        dmax = fmaxf(dmax, fabsf(a - r[j]));
     }
-    if (__builtin_expect(__any(near), 0)) {
+    if (__builtin_expect(__any(dmax >= kEdge), 0)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = x[j] / s;
+        for (int j = 0; j < 8; ++j) r[j] = __builtin_rintf(x[j] / s);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = __builtin_rintf(r[j]);
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {

@@ -28,7 +28,6 @@ namespace pdq {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, four per workgroup
-constexpr int64_t kQuantBlocks = 512;  // 2 per CU on 256 CUs
 
 template <bool SKIP>
 __device__ __forceinline__ uint32_t skip_mask(const uint32_t* __restrict__ flags, int chunk) {
@@ -59,7 +58,7 @@ __device__ __forceinline__ uint2 chunk_codes(const Raw8<DT>& r, uint32_t skipm, 
                                              int& csum) {
     float v[8], q[8];
     widen8<DT>(r, v);
-    rne_quotient8(v, s, inv, q);
+    rne_quotient8<true>(v, s, inv, q);  // |x / s| <= 127 (1 + 2^-22): absmax scale
     int c[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -69,101 +68,141 @@ __device__ __forceinline__ uint2 chunk_codes(const Raw8<DT>& r, uint32_t skipm, 
     return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
 }
 
-// CPL > 0: each lane keeps CPL chunks of 8 elements in registers (one HBM
-// read).  Wavefronts stride over the rows and load row r + stride while they
-// quantize row r, so reads, arithmetic and writes of different rows overlap.
-// CPL == 0: rows too long for registers are streamed twice (the second pass
-// hits the L2).
-template <int DT, int CPL, bool SKIP, bool COLSUM>
+// Codes of one chunk of an absmax-scaled row (|x / s| <= 127 (1 + 2^-22)),
+// skipped elements 0.  b = fma(x, inv, 1.5 * 2^23) rounds the exact product
+// x * inv to the nearest integer, ties to even, and leaves that integer (two's
+// complement) in the low byte of b's encoding, so one FMA does the scaling,
+// the rounding and the conversion.  x * inv is within 2^-24 |x / s| of x / s,
+// and fl(x / s) within 2^-24 |x / s| as well, so both lie within 2^-16 of each
+// other: unless x * inv is within 2^-15 of a half-integer, rounding it gives
+// the same integer as rounding the correctly rounded quotient (and neither is
+// a tie).  The residual d = fma(x, inv, -(b - 1.5 * 2^23)) = x * inv - rint(x *
+// inv), rounded once, tells: when any |d| of the wavefront reaches 1/2 - 2^-15
+// the whole chunk is recomputed with the correctly rounded division.
+template <int DT, bool SKIP>
+__device__ __forceinline__ uint2 chunk_codes_absmax(const Raw8<DT>& r, uint32_t skipm, float s, float inv) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    float v[8], b[8];
+    widen8<DT>(r, v);
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        b[j] = __builtin_fmaf(v[j], inv, kMagic);
+        const float d = fabsf(__builtin_fmaf(v[j], inv, -(b[j] - kMagic)));
+        if (!SKIP || !((skipm >> j) & 1u)) dmax = fmaxf(dmax, d);
+    }
+    if (__builtin_expect(__any(dmax >= 0.5f - 0x1p-15f), 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = v[j] / s + kMagic;  // exact: |v / s| < 2^22 for kept elements
+    }
+    uint32_t u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = (SKIP && ((skipm >> j) & 1u)) ? 0u : __float_as_uint(b[j]);
+    // low bytes of u[0..7] -> two words of packed codes
+    const uint32_t t0 = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u);
+    const uint32_t t2 = __builtin_amdgcn_perm(u[5], u[4], 0x0c0c0400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(u[7], u[6], 0x0c0c0400u);
+    return make_uint2(__builtin_amdgcn_perm(t1, t0, 0x05040100u), __builtin_amdgcn_perm(t3, t2, 0x05040100u));
+}
+
+// One wavefront per row.  CPL > 0: each lane keeps CPL chunks of 8 elements
+// in registers (one HBM read), issued together and unconditionally (FULL: the
+// row is exactly CPL wavefront-wide chunks; otherwise lanes past the row
+// re-read its last chunk and zero it), so the compiler's waits count them
+// exactly.  CPL == 0: rows too long for registers are streamed twice (the
+// second pass hits the L2).
+template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
                                                     float* __restrict__ scale,
                                                     int32_t* __restrict__ colsum,
                                                     const uint32_t* __restrict__ skip) {
     const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
-    int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;  // whole wavefront leaves together
-    auto row_ptr = [&](int64_t r) { return static_cast<const char*>(x) + r * ld_bytes; };
+    const char* xr = static_cast<const char*>(x) + row * ld_bytes;
+    uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+    int csum = 0;
+    float s;
 
     if constexpr (CPL > 0) {
-        Raw8<DT> raw[CPL], nxt[CPL];
+        Raw8<DT> raw[CPL];
         uint32_t sk[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            raw[i] = c < nch ? load_raw8<DT>(row_ptr(row), c) : zero_raw8<DT>();
-            sk[i] = c < nch ? skip_mask<SKIP>(skip, c) : 0u;
+            if constexpr (FULL) {
+                raw[i] = load_raw8<DT>(xr, c);
+            } else {
+                raw[i] = load_raw8<DT>(xr, min(c, nch - 1));
+                if (c >= nch) raw[i] = zero_raw8<DT>();
+            }
+            sk[i] = (FULL || c < nch) ? skip_mask<SKIP>(skip, min(c, nch - 1)) : 0u;
         }
-        for (; row < rows; row += stride) {
-            const bool more = row + stride < rows;
+        float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = lane + 64 * i;
-                nxt[i] = (more && c < nch) ? load_raw8<DT>(row_ptr(row + stride), c) : zero_raw8<DT>();
-            }
-            float amax = 0.0f;
-            int csum = 0;
+        for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+        amax = wave_max_full(amax);
+        s = absmax_step(amax);
+        const float inv = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
-            amax = wave_max(amax);
-            const float s = absmax_step(amax);
-            const float inv = 1.0f / s;
-            uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = lane + 64 * i;
-                if (c < nch) qr[c] = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
-            }
-            if (lane == 0) scale[row] = s;
-            if constexpr (COLSUM) {
-                csum = wave_sum(csum);
-                if (lane == 0) colsum[row] = csum;
-            }
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) raw[i] = nxt[i];
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            uint2 code;
+            if constexpr (COLSUM)
+                code = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
+            else
+                code = chunk_codes_absmax<DT, SKIP>(raw[i], sk[i], s, inv);
+            if (FULL || c < nch) qr[c] = code;
         }
     } else {
-        for (; row < rows; row += stride) {
-            const char* xr = row_ptr(row);
-            float amax = 0.0f;
-            int csum = 0;
-            for (int c = lane; c < nch; c += 64)
-                amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
-            amax = wave_max(amax);
-            const float s = absmax_step(amax);
-            const float inv = 1.0f / s;
-            uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
-            for (int c = lane; c < nch; c += 64)
-                qr[c] = chunk_codes<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), s, inv, csum);
-            if (lane == 0) scale[row] = s;
-            if constexpr (COLSUM) {
-                csum = wave_sum(csum);
-                if (lane == 0) colsum[row] = csum;
-            }
+        float amax = 0.0f;
+        for (int c = lane; c < nch; c += 64)
+            amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
+        amax = wave_max_full(amax);
+        s = absmax_step(amax);
+        const float inv = 1.0f / s;
+        for (int c = lane; c < nch; c += 64) {
+            const Raw8<DT> r = load_raw8<DT>(xr, c);
+            const uint32_t m = skip_mask<SKIP>(skip, c);
+            if constexpr (COLSUM)
+                qr[c] = chunk_codes<DT>(r, m, s, inv, csum);
+            else
+                qr[c] = chunk_codes_absmax<DT, SKIP>(r, m, s, inv);
         }
     }
+    if (lane == 0) scale[row] = s;
+    if constexpr (COLSUM) {
+        csum = wave_sum(csum);
+        if (lane == 0) colsum[row] = csum;
+    }
+}
+
+template <int DT, int CPL, bool FULL>
+void launch_rows(dim3 grid, const void* x, int64_t ldb, int64_t rows, int nch, int8_t* q, float* scale,
+                 int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+    if (skip)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
+    else if (colsum)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
+    else
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, skip);
 }
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                     int32_t* colsum, const uint32_t* skip, hipStream_t st) {
-    // two workgroups (eight wavefronts) per CU, each wavefront striding over rows
-    int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (blocks > kQuantBlocks) blocks = kQuantBlocks;
-    const dim3 grid((unsigned)blocks);
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
-    if (skip) {
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, true, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
-    } else if (colsum) {
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, false, true>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
-    } else {
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, false, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
-    }
+    if (CPL > 0 && nch == 64 * CPL)
+        launch_rows<DT, CPL, true>(grid, x, ldb, rows, nch, q, scale, colsum, skip, st);
+    else
+        launch_rows<DT, CPL, false>(grid, x, ldb, rows, nch, q, scale, colsum, skip, st);
 }
 
 template <int DT>
@@ -202,7 +241,7 @@ __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x
         const int col = (int)(c - row * nch);
         float v[8], rq[8];
         widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
-        rne_quotient8(v, s, inv, rq);
+        rne_quotient8<false>(v, s, inv, rq);
         int code[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
