@@ -191,6 +191,34 @@ def test_decode_ragged(dtype, m, n, k):
     decode_case(x, synth.weights(4200 + n, n, k, dtype), dtype, s, z, bias=synth.bias(4300, n))
 
 
+# One-launch path (static quantization inside the GEMM): M <= 16 and M * K <=
+# 32768; (9, 100, 4096) and (17, 50, 64) sit just past the limits and take the
+# two-kernel path.
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (5, 17, 80), (16, 1000, 1040), (16, 300, 2048),
+                                   (2, 64, 14336), (8, 4096, 4096), (9, 100, 4096), (17, 50, 64)])
+def test_decode_fused_shapes(dtype, m, n, k):
+    cal = [synth.activations(4500 + b, 64, k, [1, k - 2], 100.0, offset=0.1, dtype=dtype) for b in range(3)]
+    _, s, z = O.calibrate(cal)
+    x = synth.activations(4600 + m, m, k, [1, k - 2], 100.0, offset=0.1, dtype=dtype)
+    decode_case(x, synth.weights(4700 + n, n, k, dtype), dtype, s, z, bias=synth.bias(4800, n))
+
+
+def test_decode_fused_strided_rows():
+    m, n, k = 6, 300, 1024
+    wide = synth.activations(4900, m, k + 48, [5], 100.0, offset=0.1, dtype="bf16")
+    x = wide[:, :k]
+    s, z = F32(0.9), 4
+    wq, ws, cs, (rq, rs, rc) = weight_case(synth.weights(4901, n, k, "bf16"), "bf16")
+    xt = dev(wide, "bf16")[:, :k]
+    assert xt.stride(0) == k + 48
+    res = pdq.linear_decode(xt, s, z, wq, ws, cs, want_acc=True)
+    ref = O.linear_decode(np.ascontiguousarray(x), s, z, rq, rs, rc)
+    assert np.array_equal(host(res["xq"]), ref["xq"])
+    assert np.array_equal(host(res["acc"]), ref["acc"])
+    check_16bit(host(res["y"]), ref["y32"], "bf16", True)
+
+
 def test_decode_saturation_counted():
     x = synth.activations(4400, 8, 256, [3, 9], 100.0, offset=0.1, dtype="bf16")
     ref = decode_case(x, synth.weights(4401, 64, 256, "bf16"), "bf16", 0.05, 17)
@@ -320,6 +348,24 @@ def test_static_blocks():
     check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc, rc, z), s, rs), "bf16", exact=True)
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (1, 33, 1040), (1, 7, 16), (2, 300, 4096),
+                                   (16, 100, 3072), (17, 64, 512), (1, 50, 4112)])
+def test_static_gemm_skinny(m, n, k):
+    # the GEMM alone on already-quantized activations: M = 1 (dot-product
+    # kernel), M <= 16 with K <= 4096 (LDS-staged MFMA), otherwise the
+    # register-path kernel
+    xq = synth.random_int8(6200 + m, (m, k))
+    s, z = F32(0.37), -11
+    w = synth.weights(6201 + n, n, k, "bf16")
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, "bf16")
+    bias = synth.bias(6202, n)
+    res = pdq.gemm_static(torch.from_numpy(xq).cuda(), s, z, wq, ws, cs, torch.from_numpy(bias).cuda(),
+                          want_acc=True)
+    acc = O.int_matmul(xq, rq)
+    assert np.array_equal(host(res["acc"]), acc)
+    check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc, rc, z), s, rs, bias), "bf16", exact=True)
+
+
 # ---------------------------------------------------------------------------
 # rounding at and around the ties: inputs at (k + 1/2) S and a few ulps away
 # ---------------------------------------------------------------------------
@@ -351,6 +397,26 @@ def test_per_token_rounding_near_ties():
     q_ref, s_ref = O.quantize_rows_absmax(x)
     assert np.array_equal(host(xs), s_ref)
     assert np.array_equal(host(xq), q_ref)
+
+
+@pytest.mark.parametrize("s", [0.5, 3.3963, 17.25, 1e-3])
+def test_decode_fused_rounding_near_ties(s):
+    # the same tie-straddling inputs through the one-launch decode path (16 rows
+    # at a time), codes and saturation count against the oracle
+    s = F32(s)
+    v = _near_ties(s, 700)
+    v = v[: (v.size // 256) * 256].reshape(-1, 256)
+    w = synth.weights(5100, 40, 256, "f32")
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, "f32")
+    for z in (0, -3, 100):
+        for r0 in range(0, v.shape[0], 16):
+            x = np.ascontiguousarray(v[r0:r0 + 16])
+            sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+            res = pdq.linear_decode(dev(x, "f32"), s, z, wq, ws, cs, sat_count=sat, want_acc=True)
+            ref = O.linear_decode(x, s, z, rq, rs, rc)
+            assert np.array_equal(host(res["xq"]), ref["xq"])
+            assert int(host(sat)[0]) == ref["sat"]
+            assert np.array_equal(host(res["acc"]), ref["acc"])
 
 
 @pytest.mark.parametrize("s", [0.5, 3.3963, 0.0078125, 17.25, 1e-3])

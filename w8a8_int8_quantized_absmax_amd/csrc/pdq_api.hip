@@ -213,6 +213,30 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
     if (!aligned(xq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) ||
         !aligned(y, 2) || !aligned(acc_out, 4) || !aligned(sat_count, 4))
         return PDQ_ERR_ALIGN;
+    if (N > 0 && decode_fusable(M, K)) {
+        // one launch: the GEMM quantizes the activations itself (and writes xq)
+        if (!y) return PDQ_ERR_NULL;
+        DecodeArgs d{};
+        d.wq = wq;
+        d.M = (int)M;
+        d.N = (int)N;
+        d.K = (int)K;
+        d.s = a_scale;
+        d.z = a_zp;
+        d.sw = w_scale;
+        d.colsum = w_colsum;
+        d.bias = bias;
+        d.y = y;
+        d.ldy = ldy;
+        d.acc_out = acc_out;
+        d.x = x;
+        d.x_dt = x_dt;
+        d.ldx = ldx;
+        d.xq_out = xq;
+        d.sat = sat_count;
+        launch_decode_fused(d, static_cast<hipStream_t>(stream));
+        return launched();
+    }
     PDQ_TRY(pdq_quantize_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, stream));
     return pdq_gemm_static(xq, M, K, a_scale, a_zp, wq, w_scale, w_colsum, bias, N, y, ldy, acc_out,
                            stream);

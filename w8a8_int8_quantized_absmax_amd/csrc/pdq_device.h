@@ -174,6 +174,26 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
+// Static asymmetric codes of 8 values (decode phase): r = rne(fl(x / s)),
+// pre-clamped to +-512 so that the integer conversion stays in range (the
+// clamped value saturates exactly when the unclamped one does), r' = r + z,
+// code = clamp(r', -128, 127).  Adds the number of r' outside [-128, 127] to
+// nsat.  inv = fl(1 / s).
+__device__ __forceinline__ uint2 static_codes8(const float (&v)[8], float s, float inv, int z, int& nsat) {
+    float rq[8];
+    rne_quotient8<false>(v, s, inv, rq);
+    int code[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float r = fminf(fmaxf(rq[j], -512.0f), 512.0f);
+        const int ri = (int)r + z;
+        nsat += (ri < -128) | (ri > 127);
+        code[j] = min(max(ri, -128), 127);
+    }
+    return make_uint2(pack4_i8(code[0], code[1], code[2], code[3]),
+                      pack4_i8(code[4], code[5], code[6], code[7]));
+}
+
 // Float max / min through integer atomics (valid for every non-NaN value,
 // including +-INF and the {+INF, -INF} starting state).  -0 is taken as +0 so
 // that the sign test below routes it through the signed-integer branch.

@@ -49,7 +49,7 @@ void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st);
 
 // decode.hip --------------------------------------------------------------
 struct DecodeArgs {
-    const int8_t* xq;  // [M, K] dense
+    const int8_t* xq;  // [M, K] dense (launch_decode_gemv input)
     const int8_t* wq;  // [N, K] dense
     int M, N, K;
     float s;
@@ -60,8 +60,18 @@ struct DecodeArgs {
     uint16_t* y;
     int64_t ldy;
     int32_t* acc_out;
+    // launch_decode_fused only: 16-bit or f32 activations, quantized in-kernel
+    const void* x;
+    int x_dt;
+    int64_t ldx;
+    int8_t* xq_out;  // [M, K] dense, written by workgroup 0
+    uint32_t* sat;   // nullable saturation counter
 };
+// Activations already quantized (xq).
 void launch_decode_gemv(const DecodeArgs& a, hipStream_t st);
+// Static quantization fused into the GEMM; only when decode_fusable(M, K).
+bool decode_fusable(int64_t M, int64_t K);
+void launch_decode_fused(const DecodeArgs& a, hipStream_t st);
 
 // outlier.hip -------------------------------------------------------------
 void launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t st);

@@ -239,19 +239,9 @@ __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x
     if (c < total) {
         const int64_t row = c / nch;
         const int col = (int)(c - row * nch);
-        float v[8], rq[8];
+        float v[8];
         widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
-        rne_quotient8<false>(v, s, inv, rq);
-        int code[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float r = fminf(fmaxf(rq[j], -512.0f), 512.0f);  // keeps the int conversion in range
-            const int ri = (int)r + z;
-            nsat += (ri < -128) | (ri > 127);
-            code[j] = min(max(ri, -128), 127);
-        }
-        reinterpret_cast<uint2*>(q)[c] = make_uint2(pack4_i8(code[0], code[1], code[2], code[3]),
-                                                    pack4_i8(code[4], code[5], code[6], code[7]));
+        reinterpret_cast<uint2*>(q)[c] = static_codes8(v, s, inv, z, nsat);
     }
     if (sat) {
         nsat = wave_sum(nsat);
