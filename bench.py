@@ -60,6 +60,38 @@ def timed(fn, iters: int, warmup: int, stream) -> float:
     return start.elapsed_time(stop) / iters
 
 
+def graph_timed(fn, calls: int, replays: int, stream) -> float:
+    """Average milliseconds per call of fn(i), i < calls, captured into one HIP
+    graph and replayed `replays` times: the launches then go back to back
+    without the host's per-call overhead (a few microseconds of Python and
+    ctypes that would otherwise starve the GPU between ~5 us kernels)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (replays * calls)
+    del g
+    return ms
+
+
 def kernel_hash() -> str:
     with open(GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -163,12 +195,26 @@ def bench_decode(args, torch, pdq, synth):
         iters = max(args.steps * 10, 200)
         ms_call = timed(call, iters, args.warmup * 4, stream)
         ms_gemv = timed(gemv, iters, args.warmup * 4, stream)
+        # the same calls replayed from a HIP graph (one call per weight copy)
+        # (all copies hold the same weights, so every replay must leave the
+        # eager output in y)
+        y_eager = y.clone()
+        ms_call_g = graph_timed(call, nrot, max(args.steps // 2, 10), stream)
+        if not torch.equal(y, y_eager):
+            raise RuntimeError(f"decode M={m}: the replayed call changed the output")
+        ms_gemv_g = graph_timed(gemv, nrot, max(args.steps // 2, 10), stream)
+        if not torch.equal(y, y_eager):
+            raise RuntimeError(f"decode M={m}: the replayed GEMV changed the output")
         # algorithmic bytes: int8 W once, bf16 X, bf16 Y, w_scale + colsum
         call_bytes = N * K + 2 * m * K + 2 * m * N + 8 * N
         gemv_bytes = N * K + m * K + 2 * m * N + 8 * N
         res[str(m)] = dict(us_call=ms_call * 1e3, us_gemv=ms_gemv * 1e3,
+                           us_call_graph=ms_call_g * 1e3, us_gemv_graph=ms_gemv_g * 1e3,
                            call_GBps=call_bytes / (ms_call * 1e-3) / 1e9,
                            gemv_GBps=gemv_bytes / (ms_gemv * 1e-3) / 1e9,
+                           call_graph_GBps=call_bytes / (ms_call_g * 1e-3) / 1e9,
+                           gemv_graph_GBps=gemv_bytes / (ms_gemv_g * 1e-3) / 1e9,
+                           gemv_graph_frac=gemv_bytes / (ms_gemv_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            gemv_frac=gemv_bytes / (ms_gemv * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            saturated=nsat, saturated_frac=nsat / (m * K))
     del wqs
@@ -266,7 +312,9 @@ def main():
         dec = bench_decode(args, torch, pdq, synth)
         for m, r in dec["per_batch"].items():
             log(f"[decode] M={m}: call {r['us_call']:.2f} us, GEMV {r['us_gemv']:.2f} us = "
-                f"{r['gemv_GBps']:.0f} GB/s; saturated {r['saturated']}")
+                f"{r['gemv_GBps']:.0f} GB/s; from a graph: call {r['us_call_graph']:.2f} us "
+                f"({r['call_graph_GBps']:.0f} GB/s), GEMV {r['us_gemv_graph']:.2f} us "
+                f"({r['gemv_graph_GBps']:.0f} GB/s); saturated {r['saturated']}")
         llm = bench_llm_int8(args, torch, pdq, synth)
         log(f"[llm.int8] {llm['ms']*1e3:.1f} us, {llm['int8_tops']:.0f} TOPS, |O|={llm['n_outlier']}")
 

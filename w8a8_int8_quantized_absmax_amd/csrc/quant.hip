@@ -265,11 +265,24 @@ __global__ __launch_bounds__(256) void k_minmax(const void* __restrict__ x, int6
             hi = fmaxf(hi, v[j]);
         }
     }
+    // one atomic pair per workgroup: the running state lives at two addresses,
+    // and same-address atomics are serialized in the L2
+    __shared__ float s_lo[4], s_hi[4];
     lo = wave_min(lo);
     hi = wave_max(hi);
-    if ((threadIdx.x & 63) == 0 && lo <= hi) {
-        atomic_min_f32(mm, lo);
-        atomic_max_f32(mm + 1, hi);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[wave] = lo;
+        s_hi[wave] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        lo = fminf(fminf(s_lo[0], s_lo[1]), fminf(s_lo[2], s_lo[3]));
+        hi = fmaxf(fmaxf(s_hi[0], s_hi[1]), fmaxf(s_hi[2], s_hi[3]));
+        if (lo <= hi) {
+            atomic_min_f32(mm, lo);
+            atomic_max_f32(mm + 1, hi);
+        }
     }
 }
 
@@ -328,7 +341,7 @@ void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, flo
     const int64_t total = M * (K / 8);
     if (total <= 0) return;
     int64_t blocks = (total + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
+    if (blocks > 256) blocks = 256;  // one per CU, each striding over the tensor
     const int nch = (int)(K / 8);
     switch (dt) {
         case kF32:
