@@ -276,73 +276,54 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // tile with one 8-byte write; the tile then leaves in 16-byte row chunks.
     int side_steps = 0;
     bool poison = false;
+    const int ml0 = wm * 128 + (lane & 31);
+    const int nl0 = wn * 128 + 4 * (lane >> 5);
+    [[maybe_unused]] uint4 xs0[4], ws0[4];
     if constexpr (SIDE) {
         const int cnt = *a.count;
         poison = cnt > a.max_count;
         side_steps = poison ? 0 : (cnt + 15) / 16;
+        // The first 16 outlier columns of this wave's X_out and W_out rows,
+        // fetched while the last K tiles land.  Rows past M or N are clamped:
+        // they only feed outputs that are never stored.
+        if (side_steps > 0) {
+            const int koff = 8 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = min(m0 + ml0 + 32 * i, M - 1);
+                xs0[i] = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int wr = min(n0 + wn * 128 + 32 * j + (lane & 31), N - 1);
+                ws0[j] = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
+            }
+        }
     }
     wait_loads_and_sync<0>();  // the ring is no longer read or written
     auto yrow = [&](int ml) -> uint8_t* {
         uint8_t* b = ml < 128 ? (ml < 64 ? st0 : st1) : (ml < 192 ? st2 : st3);
         return b + (ml & 63) * kYPitch;
     };
-    const bool has_bias = a.bias != nullptr;
-    const int ml0 = wm * 128 + (lane & 31);
-    const int nl0 = wn * 128 + 4 * (lane >> 5);
     float sam[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sam[i] = s_sa[ml0 + 32 * i];
+    auto side_mfma = [&](uint4 wv, uint4 xv, v16f c) -> v16f {
+        if constexpr (OUT == kF16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wv),
+                                                          __builtin_bit_cast(v8h, xv), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, wv),
+                                                           __builtin_bit_cast(v8bf, xv), c, 0, 0, 0);
+    };
+    if (a.acc_out) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float sbv[4][4], bv[4][4];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
-                bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ml = ml0 + 32 * i;
-            v16f side = v16f{};
-            if constexpr (SIDE) {
-                // 16-bit product of the outlier columns for this 32x32 block,
-                // in the same (n, m) orientation: W_out rows x X_out rows.
-                const int m = m0 + ml;
-                const int wr = n0 + wn * 128 + 32 * j + (lane & 31);
-                for (int ks = 0; ks < side_steps; ++ks) {
-                    const int koff = ks * 16 + 8 * (lane >> 5);
-                    uint4 xv = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
-                    if (m < M) xv = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
-                    if (wr < N) wv = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
-                    if constexpr (OUT == kF16)
-                        side = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wv),
-                                                                      __builtin_bit_cast(v8h, xv),
-                                                                      side, 0, 0, 0);
-                    else
-                        side = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, wv),
-                                                                       __builtin_bit_cast(v8bf, xv),
-                                                                       side, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float t = __fmul_rn(sam[i], sbv[g][e]);
-                    float v = __fmul_rn(t, (float)acc[i][j][4 * g + e]);
-                    if constexpr (SIDE) v = __fadd_rn(v, side[4 * g + e]);
-                    if (has_bias) v = __fadd_rn(v, bv[g][e]);
-                    if (poison) v = __builtin_nanf("");
-                    o[e] = OUT == kF16 ? f32_to_f16(v) : f32_to_bf16(v);
-                }
-                const int nl = nl0 + 32 * j + 8 * g;
-                *reinterpret_cast<uint2*>(yrow(ml) + nl * 2) =
-                    make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-                if (a.acc_out) {
-                    const int m = m0 + ml, n = n0 + nl;
+                for (int g = 0; g < 4; ++g) {
+                    const int m = m0 + ml0 + 32 * i, n = n0 + nl0 + 32 * j + 8 * g;
                     if (m < M) {
                         int32_t* ap = a.acc_out + (size_t)m * N + n;
 #pragma unroll
@@ -350,9 +331,63 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                             if (n + e < N) ap[e] = acc[i][j][4 * g + e];
                     }
                 }
+    }
+    // The bias test is taken once for the whole tile, not per element.
+    auto convert = [&](auto bias_tag) {
+        constexpr bool kBias = decltype(bias_tag)::value;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float sbv[4][4], bv[4][4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
+                    if constexpr (kBias) bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ml = ml0 + 32 * i;
+                v16f side = v16f{};
+                if constexpr (SIDE) {
+                    // 16-bit product of the outlier columns for this 32x32
+                    // block, in the same (n, m) orientation: W_out rows x
+                    // X_out rows.
+                    if (side_steps > 0) {
+                        side = side_mfma(ws0[j], xs0[i], side);
+                        const int m = min(m0 + ml, M - 1);
+                        const int wr = min(n0 + wn * 128 + 32 * j + (lane & 31), N - 1);
+                        for (int ks = 1; ks < side_steps; ++ks) {
+                            const int koff = ks * 16 + 8 * (lane >> 5);
+                            const uint4 xv = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
+                            const uint4 wv = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
+                            side = side_mfma(wv, xv, side);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = __fmul_rn(sam[i], sbv[g][e]);
+                        v[e] = __fmul_rn(t, (float)acc[i][j][4 * g + e]);
+                        if constexpr (SIDE) v[e] = __fadd_rn(v[e], side[4 * g + e]);
+                        if constexpr (kBias) v[e] = __fadd_rn(v[e], bv[g][e]);
+                        if constexpr (SIDE)
+                            if (poison) v[e] = __builtin_nanf("");
+                    }
+                    const int nl = nl0 + 32 * j + 8 * g;
+                    *reinterpret_cast<uint2*>(yrow(ml) + nl * 2) =
+                        make_uint2(f32x2_to_16<OUT>(v[0], v[1]), f32x2_to_16<OUT>(v[2], v[3]));
+                }
             }
         }
-    }
+    };
+    if (a.bias)
+        convert(std::true_type{});
+    else
+        convert(std::false_type{});
     __syncthreads();
     // 256 rows x 32 chunks of 8 outputs; consecutive threads take consecutive
     // chunks of a row.

@@ -53,6 +53,19 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Two values converted by one instruction (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32, same rounding as above), `lo` in the low half.
+typedef float v2f __attribute__((ext_vector_type(2)));
+template <int OUT>
+__device__ __forceinline__ uint32_t f32x2_to_16(float lo, float hi) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+    if constexpr (OUT == kF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2h));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
 template <int DT>
 __device__ __forceinline__ Raw8<DT> load_raw8(const void* row, int chunk) {
     Raw8<DT> r;
