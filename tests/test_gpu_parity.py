@@ -78,6 +78,21 @@ def test_prefill_ragged(dtype, m, n, k):
     prefill_case(x, w, dtype, bias=synth.bias(2200 + n, n))
 
 
+# K tiles of 64: every count modulo the depth of the kernel's LDS ring (five),
+# whole and ragged, with and without bias.
+@pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 336, 640, 656, 1216, 1280])
+def test_prefill_k_depths(k):
+    x = synth.activations(2300 + k, 300, k, [1, k - 2], 100.0, dtype="bf16")
+    w = synth.weights(2400 + k, 520, k, "bf16")
+    bias = synth.bias(2500 + k, 520) if k % 128 == 0 else None
+    res = prefill_case(x, w, "bf16", bias=bias)
+    # the same output without the INT32 accumulator copy
+    wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    y2 = pdq.linear_prefill(dev(x, "bf16"), wq, ws, b)["y"]
+    assert torch.equal(res["y"], y2)
+
+
 def test_prefill_empty_batch():
     w = synth.weights(7, 64, 64, "bf16")
     wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
