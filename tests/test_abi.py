@@ -104,10 +104,13 @@ def test_calibrate_validation(L):
 
 def test_outlier_workspace_size(L):
     ws = L.pdq_linear_int8_outlier_workspace
-    # flags (K u32) + X_out (M x P f16) + W_out (N x P f16), each 256-aligned, P = ceil16(max)
-    assert ws(2048, 28672, 8192, 64) == 8192 * 4 + 2048 * 64 * 2 + 28672 * 64 * 2
-    assert ws(3, 5, 16, 1) == 256 + 256 + 256
-    assert ws(3, 5, 16, 0) == 256
+    # predicate bytes (row blocks x pitch, pitch = ceil16(K / 8); at most 32 row
+    # blocks of ceil32(ceil(M / 32)) rows) + mask (pitch) + X_out (M x P f16)
+    # + W_out (N x P f16), each 256-aligned, P = ceil16(max)
+    assert ws(2048, 28672, 8192, 64) == 32 * 1024 + 1024 + 2048 * 64 * 2 + 28672 * 64 * 2
+    assert ws(3, 5, 16, 1) == 4 * 256
+    assert ws(3, 5, 16, 0) == 2 * 256
+    assert ws(0, 5, 16, 1) == 2 * 256  # no predicate rows, no X_out
     assert ws(-1, 5, 16, 1) == 0
 
 

@@ -319,6 +319,39 @@ def test_outlier_capacity_exceeded_poisons_output():
     assert torch.isnan(res["y"].float()).all()
 
 
+def test_outlier_capacity_beyond_fused_gather():
+    """More capacity than the index kernel keeps in LDS: the separate W gather runs."""
+    k = 8192
+    x = synth.normal(5900, (33, k))
+    cols = [3, 4100, k - 1]
+    x[:, cols] = synth.normal(5901, (33, len(cols)), 60.0)
+    x = synth.round_to(x, "f16")
+    res, cnt = outlier_case(x, synth.weights(5902, 40, k, "f16"), "f16", 6.0, max_out=5000)
+    assert cnt == 3
+
+
+def test_outlier_single_hits_in_far_row_blocks():
+    """One outlier element in the first and one in the last row of a tall batch
+    (32 row blocks, the last one short), the rest regular; x with a row pitch
+    wider than K gives the same result as a dense copy."""
+    m, k, n = 3001, 256, 72
+    x = synth.normal(6000, (m, k))
+    x[0, k - 1] = 40.0
+    x[m - 1, 5] = -9.5
+    x = synth.round_to(x, "bf16")
+    res, cnt = outlier_case(x, synth.weights(6001, n, k, "bf16"), "bf16", 6.0)
+    assert cnt == 2 and host(res["idx"])[:2].tolist() == [5, k - 1]
+    wide = torch.zeros((m, k + 40), dtype=torch.bfloat16, device="cuda")
+    wide[:, :k] = dev(x, "bf16")
+    w = dev(synth.weights(6001, n, k, "bf16"), "bf16")
+    wq, ws, _ = pdq.quantize_weight(w)
+    a = pdq.linear_int8_outlier(wide[:, :k], 6.0, wq, ws, w)
+    b = pdq.linear_int8_outlier(wide[:, :k].contiguous(), 6.0, wq, ws, w)
+    for key in ("y", "xq", "x_scale", "count"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["idx"][:2], b["idx"][:2])
+
+
 def test_outlier_llm_int8_full_sampled():
     c = synth.LlmInt8()
     x, w = c.x(), c.w()

@@ -5,91 +5,185 @@
 // X) with a magnitude above the threshold are outliers; they and the matching
 // weight columns go to a 16-bit GEMM, the rest to the INT8 path.
 //
-//  * k_outlier_flags  flags[k] = 1 if some |x[m,k]| > threshold.  Only the
-//                     predicate matters (not the column maximum), so each
-//                     thread ORs it over its rows and touches memory with an
-//                     atomic only where an outlier actually is.
-//  * k_outlier_compact one workgroup: ascending index list + count by a
-//                     block-wide prefix sum of the flags.
-//  * k_gather_cols    X_out / W_out: the outlier columns of a 16-bit matrix,
-//                     packed and zero-padded to a multiple of 16 for the 16-bit
-//                     MFMA in the GEMM epilogue.
+//  * k_outlier_partial one predicate byte per (row block, chunk of 8 columns):
+//                     bit j set when some |x[m, 8c + j]| > threshold in the
+//                     block.  Every byte is written, so nothing needs clearing
+//                     first and no atomics are involved.
+//  * k_outlier_index  ORs the row blocks into the final per-chunk mask, counts
+//                     and lists the outlier columns in ascending order, and
+//                     gathers the outlier columns of W.  Every workgroup
+//                     derives the list itself (a few KB from L2) and gathers
+//                     its own slab of W rows; workgroup 0 publishes the mask,
+//                     the index list and the count.
+//  * k_gather_cols    X_out / W_out from a published index list: the W gather
+//                     for capacities beyond what k_outlier_index holds in LDS.
+//
+// The X gather is fused into the activation quantizer (quant.hip), which
+// reads every row anyway.  X_out and W_out are packed and zero-padded to a
+// multiple of 16 columns for the 16-bit MFMA in the GEMM epilogue.
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
+
+#include <algorithm>
 
 namespace pdq {
 
 namespace {
 
-__global__ __launch_bounds__(256) void k_fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
+constexpr int kPartialGroups = 4;  // row groups per workgroup (64 chunks each)
+constexpr int kPartialUnroll = 8;  // rows in flight per thread
 
-constexpr int kFlagRows = 64;     // rows per workgroup
-constexpr int kFlagChunks = 64;   // 8-column chunks per workgroup (512 columns)
-
-// Block (256 threads) = 64 column chunks x 4 row groups; each thread ORs the
-// predicate over 16 rows of its 8 columns.
+// Block (256 threads) = 64 column chunks x 4 row groups.  Row block
+// blockIdx.y covers rows [R y, min(M, R y + R)); each thread ORs the
+// predicate of its 8 columns over every fourth row of it, eight loads in
+// flight (rows past the block re-read its last row: the OR is unchanged),
+// then the four row groups combine through LDS.
 template <int DT>
-__global__ __launch_bounds__(256) void k_outlier_flags(const void* __restrict__ x, int64_t ld_bytes,
-                                                       int64_t M, int nch, float thr,
-                                                       uint32_t* __restrict__ flags) {
+__global__ __launch_bounds__(256) void k_outlier_partial(const void* __restrict__ x, int64_t ld_bytes,
+                                                         int64_t M, int nch, int R, float thr,
+                                                         uint8_t* __restrict__ partial,
+                                                         int pitch) {
+    __shared__ uint32_t s_hit[kPartialGroups][64];
     const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
-    const int c = blockIdx.x * kFlagChunks + cl;
-    if (c >= nch) return;
-    const int64_t r0 = (int64_t)blockIdx.y * kFlagRows + rg;
+    const int craw = blockIdx.x * 64 + cl;
+    const int c = min(craw, nch - 1);
+    const int64_t r0 = (int64_t)blockIdx.y * R;
+    const int64_t rlast = min(M, r0 + R) - 1;
+    const char* xb = static_cast<const char*>(x);
     uint32_t hit = 0;
-    for (int i = 0; i < kFlagRows / 4; ++i) {
-        const int64_t r = r0 + 4 * i;
-        if (r >= M) break;
-        float v[8];
-        widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + r * ld_bytes, c), v);
+    for (int64_t r = r0 + rg; r <= rlast; r += kPartialGroups * kPartialUnroll) {
+        Raw8<DT> raw[kPartialUnroll];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) hit |= (uint32_t)(fabsf(v[j]) > thr) << j;
-    }
-    if (hit) {
+        for (int u = 0; u < kPartialUnroll; ++u)
+            raw[u] = load_raw8<DT>(xb + min(r + kPartialGroups * u, rlast) * ld_bytes, c);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if ((hit >> j) & 1u) atomicOr(flags + c * 8 + j, 1u);
-    }
-}
-
-constexpr int kCompactThreads = 1024;
-
-__global__ __launch_bounds__(1024) void k_outlier_compact(const uint32_t* __restrict__ flags, int K,
-                                                          int32_t* __restrict__ idx,
-                                                          int32_t* __restrict__ count,
-                                                          int max_out) {
-    __shared__ int wave_tot[kCompactThreads / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (K + kCompactThreads - 1) / kCompactThreads;
-    const int k0 = tid * per;
-    int local = 0;
-    for (int k = k0; k < k0 + per && k < K; ++k) local += flags[k] != 0;
-    // inclusive scan inside the wavefront
-    int incl = local;
+        for (int u = 0; u < kPartialUnroll; ++u) {
+            float v[8];
+            widen8<DT>(raw[u], v);
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d);
-        if (lane >= d) incl += v;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < kCompactThreads / 64; ++w) {
-        if (w < wave) before += wave_tot[w];
-        total += wave_tot[w];
-    }
-    int pos = before + incl - local;
-    for (int k = k0; k < k0 + per && k < K; ++k) {
-        if (flags[k] != 0) {
-            if (pos < max_out) idx[pos] = k;
-            ++pos;
+            for (int j = 0; j < 8; ++j) hit |= (uint32_t)(fabsf(v[j]) > thr) << j;
         }
     }
-    if (tid == 0) *count = total;
+    s_hit[rg][cl] = hit;
+    __syncthreads();
+    if (rg == 0 && craw < nch)
+        partial[(int64_t)blockIdx.y * pitch + craw] =
+            (uint8_t)(s_hit[0][cl] | s_hit[1][cl] | s_hit[2][cl] | s_hit[3][cl]);
+}
+
+constexpr int kIndexThreads = 256;
+constexpr int kMaxRowBlocks = 32;
+constexpr int kMaxMaskWords = (65536 / 8 + 3) / 4;  // K <= 65536
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int& total, int* s_wave) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kIndexThreads / 64; ++w) {
+        before += w < wave ? s_wave[w] : 0;
+        total += s_wave[w];
+    }
+    return before + incl - v;
+}
+
+// Thread t owns the mask words (4 chunks each) [t * wpt, t * wpt + wpt).
+// gather: W rows [blockIdx.x * rows_per_wg, ...) of the outlier columns
+// into wo (pitch P), zero-padded to a multiple of 16, when the count fits
+// max_out; wo == null skips it.
+__global__ __launch_bounds__(kIndexThreads) void k_outlier_index(
+    const uint8_t* __restrict__ partial, int nrb, int pitch, int nch, uint8_t* __restrict__ mask,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count,
+    int max_out, const uint16_t* __restrict__ w16, int64_t N, int64_t ldw,
+    uint16_t* __restrict__ wo, int P, int rows_per_wg) {
+    __shared__ int32_t s_idx[kOutlierIdxCap];
+    __shared__ uint32_t s_words[kMaxMaskWords];
+    __shared__ int s_wave[kIndexThreads / 64];
+    const int tid = threadIdx.x;
+    const bool publish = blockIdx.x == 0;
+    const int nwords = (nch + 3) / 4;
+    const int wpt = (nwords + kIndexThreads - 1) / kIndexThreads;
+    const int w0 = tid * wpt;
+    const int nw = max(0, min(wpt, nwords - w0));
+
+    // pass 1: OR of the row blocks (32 loads in flight per word), count
+    int mine = 0;
+    for (int k = 0; k < nw; ++k) {
+        const int w = w0 + k;
+        uint32_t m = 0;
+        if (nrb > 0) {
+#pragma unroll
+            for (int b = 0; b < kMaxRowBlocks; ++b)  // clamped: repeats OR the same bytes
+                m |= reinterpret_cast<const uint32_t*>(partial + (int64_t)min(b, nrb - 1) * pitch)[w];
+        }
+        const int valid = min(4, nch - 4 * w);  // chunks of the last word past nch
+        if (valid < 4) m &= (1u << (8 * valid)) - 1u;
+        mine += __popc(m);
+        s_words[w] = m;
+        if (publish) reinterpret_cast<uint32_t*>(mask)[w] = m;
+    }
+    int total;
+    int run = block_exclusive_scan(mine, total, s_wave);
+
+    // pass 2: ascending index list
+    const int cap = min(max_out, kOutlierIdxCap);
+    for (int k = 0; k < nw; ++k) {
+        const int w = w0 + k;
+        const uint32_t m = s_words[w];
+        const int valid = min(4, nch - 4 * w);
+        for (int e = 0; e < valid; ++e) {
+            const int c = 4 * w + e;
+            uint32_t byte = (m >> (8 * e)) & 0xffu;
+            while (byte) {
+                const int j = __ffs(byte) - 1;
+                byte &= byte - 1;
+                if (run < cap) s_idx[run] = 8 * c + j;
+                if (publish && run < max_out) idx[run] = 8 * c + j;
+                ++run;
+            }
+        }
+    }
+    if (publish && tid == 0) *count = total;
+    __syncthreads();
+    if (!wo || total > max_out) return;
+
+    const int used = (total + 15) / 16 * 16;
+    if (used == 0) return;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)min((int64_t)rows_per_wg, N - row0);
+    if (used <= kIndexThreads) {
+        // kIndexThreads / used rows at a time, one column per thread; eight
+        // rows' loads are issued (clamped) before any of them is stored
+        constexpr int kG = 8;
+        const int rpi = kIndexThreads / used, rl = tid / used, j = tid - rl * used;
+        const int col = s_idx[min(j, total - 1)];
+        if (rl < rpi) {
+            for (int rb = rl; rb < nrows; rb += rpi * kG) {
+                uint16_t v[kG];
+#pragma unroll
+                for (int u = 0; u < kG; ++u)
+                    v[u] = w16[(row0 + min(rb + u * rpi, nrows - 1)) * ldw + col];
+#pragma unroll
+                for (int u = 0; u < kG; ++u) {
+                    const int r = rb + u * rpi;
+                    if (r < nrows) wo[(row0 + r) * P + j] = j < total ? v[u] : (uint16_t)0;
+                }
+            }
+        }
+    } else {
+        for (int r = 0; r < nrows; ++r)
+            for (int j = tid; j < used; j += kIndexThreads)
+                wo[(row0 + r) * P + j] = j < total ? w16[(row0 + r) * ldw + s_idx[j]] : (uint16_t)0;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ src, int64_t rows,
@@ -108,28 +202,53 @@ __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict_
 
 }  // namespace
 
-void launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t st) {
-    if (n <= 0) return;
-    hipLaunchKernelGGL(k_fill_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+int outlier_row_blocks(int64_t M) {
+    if (M <= 0) return 0;
+    const int64_t R = outlier_rows_per_block(M);
+    return (int)((M + R - 1) / R);
 }
 
-void launch_outlier_flags(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float thr,
-                          uint32_t* flags, hipStream_t st) {
+int64_t outlier_rows_per_block(int64_t M) {
+    const int64_t per = (M + kMaxRowBlocks - 1) / kMaxRowBlocks;
+    const int64_t step = kPartialGroups * kPartialUnroll;
+    return (per + step - 1) / step * step;
+}
+
+int outlier_partial_pitch(int64_t K) { return (int)((K / 8 + 15) / 16 * 16); }
+
+void launch_outlier_partial(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float thr,
+                            uint8_t* partial, hipStream_t st) {
     const int nch = (int)(K / 8);
     if (M <= 0 || nch <= 0) return;
-    const dim3 grid((nch + kFlagChunks - 1) / kFlagChunks, (unsigned)((M + kFlagRows - 1) / kFlagRows));
+    const int64_t R = outlier_rows_per_block(M);
+    const dim3 grid((nch + 63) / 64, (unsigned)outlier_row_blocks(M));
+    const int pitch = outlier_partial_pitch(K);
     if (dt == kF16)
-        hipLaunchKernelGGL(k_outlier_flags<kF16>, grid, dim3(256), 0, st, x, ldx * 2, M, nch, thr,
-                           flags);
+        hipLaunchKernelGGL(k_outlier_partial<kF16>, grid, dim3(256), 0, st, x, ldx * 2, M, nch, (int)R,
+                           thr, partial, pitch);
     else
-        hipLaunchKernelGGL(k_outlier_flags<kBF16>, grid, dim3(256), 0, st, x, ldx * 2, M, nch, thr,
-                           flags);
+        hipLaunchKernelGGL(k_outlier_partial<kBF16>, grid, dim3(256), 0, st, x, ldx * 2, M, nch, (int)R,
+                           thr, partial, pitch);
 }
 
-void launch_outlier_compact(const uint32_t* flags, int64_t K, int32_t* idx, int32_t* count,
-                            int64_t max_out, hipStream_t st) {
-    hipLaunchKernelGGL(k_outlier_compact, dim3(1), dim3(kCompactThreads), 0, st, flags, (int)K, idx,
-                       count, (int)max_out);
+void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask,
+                          int32_t* idx, int32_t* count, int64_t max_out,
+                          const void* w16, int64_t N, int64_t ldw, uint16_t* wo, int P,
+                          hipStream_t st) {
+    const int nch = (int)(K / 8);
+    const bool gather = wo && N > 0 && max_out <= kOutlierIdxCap;
+    int groups = 1, rows_per_wg = 0;
+    if (gather) {
+        groups = (int)std::min<int64_t>(256, std::max<int64_t>(1, (N + 127) / 128));
+        rows_per_wg = (int)((N + groups - 1) / groups);
+        groups = (int)((N + rows_per_wg - 1) / rows_per_wg);
+    }
+    hipLaunchKernelGGL(k_outlier_index, dim3(groups), dim3(kIndexThreads), 0, st, partial,
+                       outlier_row_blocks(M), outlier_partial_pitch(K), nch, mask, idx, count,
+                       (int)max_out, static_cast<const uint16_t*>(w16), N, ldw,
+                       gather ? wo : nullptr, P, rows_per_wg);
+    if (wo && N > 0 && !gather)
+        launch_gather_cols(w16, N, ldw, idx, count, (int)max_out, wo, P, st);
 }
 
 void launch_gather_cols(const void* src, int64_t rows, int64_t ld, const int32_t* idx,

@@ -245,7 +245,9 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
 size_t pdq_linear_int8_outlier_workspace(int64_t M, int64_t N, int64_t K, int64_t max_outliers) {
     if (M < 0 || N < 0 || K < 0 || max_outliers < 0) return 0;
     const int64_t P = side_pitch(max_outliers);
-    return align256((size_t)K * 4) + align256((size_t)(M * P * 2)) + align256((size_t)(N * P * 2));
+    const size_t pitch = (size_t)outlier_partial_pitch(K);
+    return align256((size_t)outlier_row_blocks(M) * pitch) + align256(pitch) +
+           align256((size_t)(M * P * 2)) + align256((size_t)(N * P * 2));
 }
 
 pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx,
@@ -275,20 +277,26 @@ pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t P = side_pitch(max_outliers);
+    const size_t pitch = (size_t)outlier_partial_pitch(K);
     char* ws = static_cast<char*>(workspace);
-    uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
-    uint16_t* xo = reinterpret_cast<uint16_t*>(ws + align256((size_t)K * 4));
-    uint16_t* wo = reinterpret_cast<uint16_t*>(ws + align256((size_t)K * 4) +
-                                               align256((size_t)(M * P * 2)));
+    uint8_t* partial = reinterpret_cast<uint8_t*>(ws);
+    ws += align256((size_t)outlier_row_blocks(M) * pitch);
+    uint8_t* mask = reinterpret_cast<uint8_t*>(ws);
+    ws += align256(pitch);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws);
+    ws += align256((size_t)(M * P * 2));
+    uint16_t* wo = reinterpret_cast<uint16_t*>(ws);
 
-    launch_fill_zero_u32(flags, K, st);
-    launch_outlier_flags(x, dt, M, K, ldx, threshold, flags, st);
-    launch_outlier_compact(flags, K, outlier_idx, n_outlier, max_outliers, st);
+    // predicates per row block -> mask, index list, count and the W gather
+    // -> INT8 codes of the regular columns with the X gather -> INT8 GEMM
+    // with the 16-bit side product in its epilogue
+    launch_outlier_partial(x, dt, M, K, ldx, threshold, partial, st);
+    launch_outlier_index(partial, M, K, mask, outlier_idx, n_outlier, max_outliers, w16, N, ldw, wo,
+                         (int)P, st);
     if (M > 0) {
-        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, flags, st);
-        launch_gather_cols(x, M, ldx, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P, st);
+        const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
+        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
     }
-    launch_gather_cols(w16, N, ldw, outlier_idx, n_outlier, (int)max_outliers, wo, (int)P, st);
     GemmArgs g{};
     g.A = xq;
     g.B = wq;

@@ -9,11 +9,22 @@
 namespace pdq {
 
 // quant.hip ---------------------------------------------------------------
+// Outlier columns of the LLM.int8() decomposition, for the row quantizer:
+// they take no part in the absmax and are coded 0, and with xo set their
+// 16-bit values are also packed into xo[r, :] (pitch P, zero-padded to a
+// multiple of 16) when *count <= max_out.
+struct OutlierSkip {
+    const uint8_t* mask;   // [K/8] bit j of byte c: column 8c + j is an outlier
+    const int32_t* idx;    // [max_out] ascending outlier columns (the first max_out)
+    const int32_t* count;  // total number of outlier columns
+    int max_out;
+    uint16_t* xo;          // [rows, P] or null
+    int P;
+};
 // Per-row absmax symmetric INT8: q[r,:] (dense, pitch K), scale[r]; optional
-// code sums.  `skip_cols` (nullable, K flags) marks outlier columns by a
-// nonzero flag: they take no part in the absmax and are coded 0.
+// code sums; optional outlier columns to skip (16-bit inputs only).
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const uint32_t* skip_cols, hipStream_t st);
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st);
 
 // Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127); saturation
 // count added to *sat (nullable).
@@ -74,13 +85,25 @@ bool decode_fusable(int64_t M, int64_t K);
 void launch_decode_fused(const DecodeArgs& a, hipStream_t st);
 
 // outlier.hip -------------------------------------------------------------
-void launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t st);
-// flags[k] |= (|x[m,k]| > threshold) for some m; flags must start at zero.
-void launch_outlier_flags(const void* x, int dt, int64_t M, int64_t K, int64_t ldx,
-                          float threshold, uint32_t* flags, hipStream_t st);
-// Ascending indices of the nonzero flags (first max_out of them) and their count.
-void launch_outlier_compact(const uint32_t* flags, int64_t K, int32_t* idx, int32_t* count,
-                            int64_t max_out, hipStream_t st);
+// Capacity (outlier columns) up to which the W gather is fused into
+// launch_outlier_index; beyond it a separate gather runs.
+constexpr int kOutlierIdxCap = 4096;
+// Row blocks of the partial predicate pass (at most 32), rows per block, and
+// the byte pitch of one block's predicate row (K/8 chunks, padded to 16).
+int outlier_row_blocks(int64_t M);
+int64_t outlier_rows_per_block(int64_t M);
+int outlier_partial_pitch(int64_t K);
+// partial[b, c]: bit j set when some |x[m, 8c + j]| > threshold, m in row block b.
+void launch_outlier_partial(const void* x, int dt, int64_t M, int64_t K, int64_t ldx,
+                            float threshold, uint8_t* partial, hipStream_t st);
+// From the partial predicates: mask[c] (K/8 bytes, padded to a multiple of
+// 4), idx (first max_out ascending outlier columns), *count; and wo[n, :] =
+// w16[n, idx[:]] zero-padded to round_up(count, 16) when wo is set and
+// count <= max_out.
+void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask,
+                          int32_t* idx, int32_t* count, int64_t max_out,
+                          const void* w16, int64_t N, int64_t ldw, uint16_t* wo, int P,
+                          hipStream_t st);
 // dst[r, j] = src[r, idx[j]] for j < count, 0 for count <= j < round_up(count, 16);
 // nothing when count > max_out.  16-bit elements.
 void launch_gather_cols(const void* src, int64_t rows, int64_t ld, const int32_t* idx,

@@ -30,17 +30,31 @@ namespace {
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, four per workgroup
 
 template <bool SKIP>
-__device__ __forceinline__ uint32_t skip_mask(const uint32_t* __restrict__ flags, int chunk) {
-    if constexpr (!SKIP) {
+__device__ __forceinline__ uint32_t skip_mask(const OutlierSkip& sk, int chunk) {
+    if constexpr (!SKIP)
         return 0u;
+    else
+        return sk.mask[chunk];
+}
+
+// The chunk with its skipped elements (bit j of m) replaced by +0: they then
+// neither raise the absmax nor get a nonzero code.  Plain bit operations, so
+// no per-element lane masks stay live between the absmax and the codes.
+template <int DT>
+__device__ __forceinline__ Raw8<DT> zero_skipped(Raw8<DT> r, uint32_t m) {
+    if constexpr (DT == kF32) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(r.w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] &= ((m >> j) & 1u) - 1u;
     } else {
-        const uint4* p = reinterpret_cast<const uint4*>(flags + chunk * 8);
-        const uint4 a = p[0], b = p[1];
-        return (uint32_t)(a.x != 0) | ((uint32_t)(a.y != 0) << 1) | ((uint32_t)(a.z != 0) << 2) |
-               ((uint32_t)(a.w != 0) << 3) | ((uint32_t)(b.x != 0) << 4) |
-               ((uint32_t)(b.y != 0) << 5) | ((uint32_t)(b.z != 0) << 6) |
-               ((uint32_t)(b.w != 0) << 7);
+        uint32_t* w = reinterpret_cast<uint32_t*>(r.w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = ((m >> (2 * k)) & 1u) - 1u, hi = ((m >> (2 * k + 1)) & 1u) - 1u;
+            w[k] &= (lo & 0xffffu) | (hi & 0xffff0000u);
+        }
     }
+    return r;
 }
 
 template <int DT>
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
                                                     float* __restrict__ scale,
                                                     int32_t* __restrict__ colsum,
-                                                    const uint32_t* __restrict__ skip) {
+                                                    OutlierSkip skip) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;  // whole wavefront leaves together
@@ -125,6 +139,25 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
     uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
     int csum = 0;
     float s;
+    // Outlier gather into X_out: lane j fetches x[row, idx[j]] (j < 64; the
+    // index is clamped into the row, entries past the count are unset) while
+    // the row is being quantized, and stores it, or the zero padding, once
+    // the count is known to fit.
+    const bool gather = SKIP && DT != kF32 && skip.xo != nullptr && skip.max_out > 0;
+    const uint16_t* xr16 = reinterpret_cast<const uint16_t*>(xr);
+    int gidx = 0;
+    uint16_t gval = 0;
+    auto gather_store = [&]() {
+        const int cnt = *skip.count;
+        if (cnt > skip.max_out) return;
+        uint16_t* xo_row = skip.xo + row * skip.P;
+        const int used = (cnt + 15) / 16 * 16;
+        if (lane < used) xo_row[lane] = lane < cnt ? gval : (uint16_t)0;
+        for (int j = lane + 64; j < used; j += 64) {
+            const uint16_t v = xr16[skip.idx[min(j, cnt - 1)]];
+            xo_row[j] = j < cnt ? v : (uint16_t)0;
+        }
+    };
 
     if constexpr (CPL > 0) {
         Raw8<DT> raw[CPL];
@@ -140,9 +173,17 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             }
             sk[i] = (FULL || c < nch) ? skip_mask<SKIP>(skip, min(c, nch - 1)) : 0u;
         }
+        if (gather) gidx = skip.idx[min(lane, skip.max_out - 1)];
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+        for (int i = 0; i < CPL; ++i) {
+            if constexpr (SKIP) {
+                raw[i] = zero_skipped<DT>(raw[i], sk[i]);
+                sk[i] = 0;
+            }
+            amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+        }
+        if (gather) gval = xr16[min(max(gidx, 0), nch * 8 - 1)];
         amax = wave_max_full(amax);
         s = absmax_step(amax);
         const float inv = 1.0f / s;
@@ -153,7 +194,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             if constexpr (COLSUM)
                 code = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
             else
-                code = chunk_codes_absmax<DT, SKIP>(raw[i], sk[i], s, inv);
+                code = chunk_codes_absmax<DT, false>(raw[i], 0u, s, inv);
             if (FULL || c < nch) qr[c] = code;
         }
     } else {
@@ -163,6 +204,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         amax = wave_max_full(amax);
         s = absmax_step(amax);
         const float inv = 1.0f / s;
+        if (gather) gval = xr16[min(max(skip.idx[min(lane, skip.max_out - 1)], 0), nch * 8 - 1)];
         for (int c = lane; c < nch; c += 64) {
             const Raw8<DT> r = load_raw8<DT>(xr, c);
             const uint32_t m = skip_mask<SKIP>(skip, c);
@@ -172,6 +214,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                 qr[c] = chunk_codes_absmax<DT, SKIP>(r, m, s, inv);
         }
     }
+    if (gather) gather_store();
     if (lane == 0) scale[row] = s;
     if constexpr (COLSUM) {
         csum = wave_sum(csum);
@@ -181,21 +224,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
 
 template <int DT, int CPL, bool FULL>
 void launch_rows(dim3 grid, const void* x, int64_t ldb, int64_t rows, int nch, int8_t* q, float* scale,
-                 int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+                 int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+    const OutlierSkip none{};
     if (skip)
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
+                           rows, nch, q, scale, colsum, *skip);
     else if (colsum)
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
+                           rows, nch, q, scale, colsum, none);
     else
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, skip);
+                           rows, nch, q, scale, colsum, none);
 }
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                    int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+                    int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
@@ -207,7 +251,7 @@ void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t*
 
 template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                   int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+                   int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
     if (per_lane <= 1)
@@ -305,7 +349,7 @@ __global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restric
 }  // namespace
 
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const uint32_t* skip, hipStream_t st) {
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     if (rows <= 0) return;
     switch (dt) {
         case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
