@@ -82,11 +82,20 @@ const char* pdq_status_string(pdq_status s);
  * section 1 absmax formula.
  *
  *   w        [N, K] of w_dt (F32, BF16 or F16), row pitch ldw >= K
- *   wq       [N, K] int8 out, dense (row pitch K)
+ *   wq       packed INT8 weight out, pdq_weight_bytes(N, K) bytes: the codes
+ *            wq[n, k] in blocks of 16 output channels x 64 K values; block
+ *            (g, s) -- channels 16 g .., K values 64 s .. -- is the 1024 bytes
+ *            at (g * ceil(K / 64) + s) * 1024, channel r of the group its 64
+ *            bytes at r * 64, and within them the 16-byte chunk c (K values
+ *            64 s + 16 c ..) sits at position c ^ ((r >> 2) & 3).  Channels
+ *            >= N and K values >= K are written as 0.  Every GEMM entry point
+ *            takes its weight in this layout.
  *   w_scale  [N] float out: S_w[n] = max_k |w[n,k]| / 127
  *   w_colsum [N] int32 out, or NULL: sum_k wq[n,k] (needed by decode's
  *            zero-point correction, [LLM.int8] part 1 section 2)
  */
+size_t pdq_weight_bytes(int64_t N, int64_t K);
+
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream);
 
@@ -118,7 +127,7 @@ pdq_status pdq_calibrate_static(const void* x, pdq_dtype x_dt, int64_t M, int64_
  * vector-wise outer product of scales.
  *
  *   x        [M, K] of x_dt (F32, BF16, F16), row pitch ldx
- *   wq       [N, K] int8 from pdq_quantize_weight; w_scale [N] float
+ *   wq       packed INT8 weight from pdq_quantize_weight; w_scale [N] float
  *   bias     [N] float or NULL
  *   xq       [M, K] int8 out (dense), x_scale [M] float out: the quantized
  *            activations and their per-token scales (also the GEMM operand)

@@ -6,6 +6,7 @@ enqueued (the pointers are never dereferenced), so these run without a GPU.
 import ctypes
 import os
 
+import numpy as np
 import pytest
 
 from w8a8_int8_quantized_absmax_amd import pdq
@@ -133,3 +134,34 @@ def test_outlier_validation(L):
     assert out8(L, work_bytes=need - 1) == WS
     assert out8(L, work=P + 16) == ALIGN
     assert out8(L, w16=P + 1) == ALIGN
+
+
+def test_weight_bytes(L):
+    # ceil(N / 16) x ceil(K / 64) blocks of 1024 bytes
+    assert L.pdq_weight_bytes(11008, 4096) == 688 * 64 * 1024 == 11008 * 4096
+    assert L.pdq_weight_bytes(1, 16) == 1024
+    assert L.pdq_weight_bytes(257, 80) == 17 * 2 * 1024
+    assert L.pdq_weight_bytes(0, 64) == 0
+    assert L.pdq_weight_bytes(-1, 64) == 0
+
+
+def test_unpack_weight_inverts_the_layout():
+    """pdq.unpack_weight against the test-side packer written from the header."""
+    import torch
+    from packing import pack_weight
+    from w8a8_int8_quantized_absmax_amd import pdq
+
+    rng = np.random.default_rng(7)
+    for n, k in [(1, 16), (300, 80), (256, 64), (513, 1040)]:
+        codes = rng.integers(-127, 128, (n, k)).astype(np.int8)
+        image = pack_weight(codes)
+        assert image.size == -(-n // 16) * -(-k // 64) * 1024
+        assert np.array_equal(pdq.unpack_weight(torch.from_numpy(image), n, k), codes)
+        assert np.count_nonzero(image) == np.count_nonzero(codes)  # padding is zero
+    # one chunk placed by hand: channel 21 = group 1, r = 5 (r >> 2 = 1), chunk 2
+    # of K tile 1 -> position 3 of block (1, 1)
+    codes = np.zeros((22, 128), np.int8)
+    codes[21, 64 + 32:64 + 48] = np.arange(1, 17)
+    image = pack_weight(codes)
+    base = (1 * 2 + 1) * 1024 + 5 * 64 + 3 * 16
+    assert image[base:base + 16].tolist() == list(range(1, 17))

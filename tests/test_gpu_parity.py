@@ -12,6 +12,7 @@ import torch
 import oracle.pdq_oracle as O
 from w8a8_int8_quantized_absmax_amd import pdq, synth
 from gpu_helpers import check_16bit, dev, host, sample_rows
+from packing import pack_weight
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -20,7 +21,9 @@ F32 = np.float32
 def weight_case(w, dtype):
     wq, ws, cs = pdq.quantize_weight(dev(w, dtype))
     rq, rs, rc = O.quantize_weight(w)
-    assert np.array_equal(host(wq), rq)
+    # the whole packed image, padding included, and the binding's unpacking
+    assert np.array_equal(host(wq), pack_weight(rq))
+    assert np.array_equal(pdq.unpack_weight(wq, *w.shape), rq)
     assert np.array_equal(host(ws).view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(host(cs), rc)
     return wq, ws, cs, (rq, rs, rc)

@@ -19,7 +19,10 @@
 // 128-bit fragment reads are free of bank conflicts (see swz).  Tiles move
 // global -> LDS directly (global_load_lds, no register staging) through a
 // ring of four LDS buffers: three K tiles are in flight while one feeds the
-// MFMAs.
+// MFMAs.  B is the packed weight (pdq_device.h), whose 1 KB blocks already
+// are the LDS images of 16 rows: every B load instruction is one block,
+// every request a whole cache line (a row-major panel costs a half-line
+// request per row).
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -145,20 +148,24 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // in row l/4, chunk position l%4.  The lane fetches the logical chunk that
     // the swizzle puts at its position (the swizzle is an involution in kc).
     // Wave w fills rows [64w, 64w + 64) of both the A and the B tile: 4 + 4
-    // instructions per K tile.  Rows past M (N) are clamped onto the last row:
-    // they only feed outputs that are never stored.  Chunks past K are clamped
-    // onto the last chunk and zeroed in the A fragments of the last K tile,
-    // which zeroes their products.
+    // instructions per K tile.  A rows past M are clamped onto the last row:
+    // they only feed outputs that are never stored.  A chunks past K are
+    // clamped onto the last chunk and zeroed in the A fragments of the last K
+    // tile, which zeroes their products (the packed B holds zeros there and
+    // in its rows past N).
     const int rbase = wave * 64 + (lane >> 2);
     // row r = rbase + 16 i has (r >> 2) & 3 == (lane >> 4) & 3 for every i
     const int koff = swz_pos(rbase, lane & 3) * 16;
     const int8_t* pa[4];
-    const int8_t* pb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        pa[i] = a.A + (size_t)min(m0 + rbase + 16 * i, M - 1) * K;
-        pb[i] = a.B + (size_t)min(n0 + rbase + 16 * i, N - 1) * K;
-    }
+    for (int i = 0; i < 4; ++i) pa[i] = a.A + (size_t)min(m0 + rbase + 16 * i, M - 1) * K;
+    // B: the packed blocks of this wave's four 16-row groups (groups past the
+    // last are clamped: they feed outputs never stored), lane l's 16 bytes at 16 l
+    const int8_t* pb[4];
+    const int lastg = (N - 1) / kWGroup;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        pb[i] = a.B + wpack_block(min(n0 / kWGroup + wave * 4 + i, lastg), 0, nkt) + lane * 16;
     // Load number `i` (0..7: A rows, then B rows) of K tile kt into `buf`.
     auto issue_one = [&](uint8_t* buf, int kt, bool partial, int i) {
         uint8_t* la = buf + wave * 64 * BK;
@@ -166,8 +173,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         if (i < 4)
             __builtin_amdgcn_global_load_lds(pa[i] + gk, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
         else
-            __builtin_amdgcn_global_load_lds(pb[i - 4] + gk, (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb[i - 4] + (size_t)kt * kWBlock,
+                                             (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK), 16, 0, 0);
     };
     // Fragments of one 32-wide K step: lane l reads row (l%32) of each 32-row
     // block, chunk 2*s + l/32 (16 bytes = 16 K values).

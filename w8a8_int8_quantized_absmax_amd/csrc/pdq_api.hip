@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include "pdq.h"
+#include "pdq_device.h"
 #include "pdq_kernels.h"
 
 using namespace pdq;
@@ -64,6 +65,11 @@ const char* pdq_status_string(pdq_status s) {
     return "unknown status";
 }
 
+size_t pdq_weight_bytes(int64_t N, int64_t K) {
+    if (N < 0 || K < 0) return 0;
+    return (size_t)((N + kWGroup - 1) / kWGroup) * (size_t)((K + kWTileK - 1) / kWTileK) * kWBlock;
+}
+
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream) {
     if (!dtype_ok(w_dt)) return PDQ_ERR_DTYPE;
@@ -71,7 +77,7 @@ pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t
     if (N > 0 && ((K > 0 && !wq) || !w_scale)) return PDQ_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4)) return PDQ_ERR_ALIGN;
     if (N == 0) return PDQ_OK;
-    launch_quant_rows(w, w_dt, N, K, ldw, wq, w_scale, w_colsum, nullptr,
+    launch_quant_rows(w, w_dt, N, K, ldw, wq, w_scale, w_colsum, nullptr, true,
                       static_cast<hipStream_t>(stream));
     return launched();
 }
@@ -96,7 +102,7 @@ pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int6
     if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
     if (!aligned(xq, 16) || !aligned(x_scale, 4)) return PDQ_ERR_ALIGN;
     if (M == 0) return PDQ_OK;
-    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr,
+    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr, false,
                       static_cast<hipStream_t>(stream));
     return launched();
 }
@@ -295,7 +301,7 @@ pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64
                          (int)P, st);
     if (M > 0) {
         const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
-        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
+        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, false, st);
     }
     GemmArgs g{};
     g.A = xq;

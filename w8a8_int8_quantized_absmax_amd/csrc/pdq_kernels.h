@@ -21,10 +21,13 @@ struct OutlierSkip {
     uint16_t* xo;          // [rows, P] or null
     int P;
 };
-// Per-row absmax symmetric INT8: q[r,:] (dense, pitch K), scale[r]; optional
-// code sums; optional outlier columns to skip (16-bit inputs only).
+// Per-row absmax symmetric INT8: q[r,:] (dense, pitch K; or packed into the
+// weight tiles of pdq_device.h, padding zeroed, when `packed`), scale[r];
+// optional code sums; optional outlier columns to skip (16-bit inputs, dense
+// output only).
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st);
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, bool packed,
+                       hipStream_t st);
 
 // Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127); saturation
 // count added to *sat (nullable).

@@ -126,7 +126,7 @@ __device__ __forceinline__ uint2 chunk_codes_absmax(const Raw8<DT>& r, uint32_t 
 // re-read its last chunk and zero it), so the compiler's waits count them
 // exactly.  CPL == 0: rows too long for registers are streamed twice (the
 // second pass hits the L2).
-template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM>
+template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM, bool PACKED>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
                                                     float* __restrict__ scale,
@@ -134,9 +134,28 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                                                     OutlierSkip skip) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= rows) return;  // whole wavefront leaves together
+    // whole wavefronts leave together; PACKED: the rows of the last 16-row
+    // group past `rows` are padding, written as zeros
+    if (row >= (PACKED ? (rows + kWGroup - 1) / kWGroup * kWGroup : rows)) return;
     const char* xr = static_cast<const char*>(x) + row * ld_bytes;
     uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
+    // codes of chunk c (8 values): dense row-major, or PACKED into the weight
+    // blocks (K tile c / 8, 16-byte chunk (c % 8) / 2, half c % 2)
+    const int ktiles = (nch + 7) / 8;
+    auto store_code = [&](int c, uint2 code) {
+        if constexpr (PACKED) {
+            int8_t* blk = q + wpack_block(row / kWGroup, c >> 3, ktiles);
+            *reinterpret_cast<uint2*>(blk + wpack_pos((int)(row % kWGroup), (c & 7) >> 1) + ((c & 1) << 3)) = code;
+        } else {
+            qr[c] = code;
+        }
+    };
+    if constexpr (PACKED) {
+        if (row >= rows) {
+            for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
+            return;
+        }
+    }
     int csum = 0;
     float s;
     // Outlier gather into X_out: lane j fetches x[row, idx[j]] (j < 64; the
@@ -195,7 +214,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                 code = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
             else
                 code = chunk_codes_absmax<DT, false>(raw[i], 0u, s, inv);
-            if (FULL || c < nch) qr[c] = code;
+            if (FULL || c < nch) store_code(c, code);
         }
     } else {
         float amax = 0.0f;
@@ -209,12 +228,15 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             const Raw8<DT> r = load_raw8<DT>(xr, c);
             const uint32_t m = skip_mask<SKIP>(skip, c);
             if constexpr (COLSUM)
-                qr[c] = chunk_codes<DT>(r, m, s, inv, csum);
+                store_code(c, chunk_codes<DT>(r, m, s, inv, csum));
             else
-                qr[c] = chunk_codes_absmax<DT, SKIP>(r, m, s, inv);
+                store_code(c, chunk_codes_absmax<DT, SKIP>(r, m, s, inv));
         }
     }
     if (gather) gather_store();
+    if constexpr (PACKED) {  // K padding of the last K tile
+        for (int c = nch + lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
+    }
     if (lane == 0) scale[row] = s;
     if constexpr (COLSUM) {
         csum = wave_sum(csum);
@@ -223,51 +245,55 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
 }
 
 template <int DT, int CPL, bool FULL>
-void launch_rows(dim3 grid, const void* x, int64_t ldb, int64_t rows, int nch, int8_t* q, float* scale,
-                 int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, float* scale,
+                 int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
     const OutlierSkip none{};
+    const int64_t rows_pad = packed ? (rows + kWGroup - 1) / kWGroup * kWGroup : rows;
+    const dim3 grid((unsigned)((rows_pad + kRowsPerBlock - 1) / kRowsPerBlock));
     if (skip)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, *skip);
-    else if (colsum)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, none);
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false, false>), grid, dim3(256), 0, st, x,
+                           ldb, rows, nch, q, scale, colsum, *skip);
+    else if (packed && colsum)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true, true>), grid, dim3(256), 0, st, x,
+                           ldb, rows, nch, q, scale, colsum, none);
+    else if (packed)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, true>), grid, dim3(256), 0, st, x,
+                           ldb, rows, nch, q, scale, colsum, none);
     else
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, none);
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, false>), grid, dim3(256), 0, st, x,
+                           ldb, rows, nch, q, scale, colsum, none);
 }
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                    int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+                    int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
     if (CPL > 0 && nch == 64 * CPL)
-        launch_rows<DT, CPL, true>(grid, x, ldb, rows, nch, q, scale, colsum, skip, st);
+        launch_rows<DT, CPL, true>(rows, x, ldb, nch, q, scale, colsum, skip, packed, st);
     else
-        launch_rows<DT, CPL, false>(grid, x, ldb, rows, nch, q, scale, colsum, skip, st);
+        launch_rows<DT, CPL, false>(rows, x, ldb, nch, q, scale, colsum, skip, packed, st);
 }
 
 template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                   int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+                   int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
     if (per_lane <= 1)
-        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else if (per_lane <= 2)
-        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else if (per_lane <= 4)
-        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else if (per_lane <= 8)
-        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else if (per_lane <= 16)
-        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else if (per_lane <= kMaxCpl)
-        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
     else
-        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,12 +375,13 @@ __global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restric
 }  // namespace
 
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, bool packed,
+                       hipStream_t st) {
     if (rows <= 0) return;
     switch (dt) {
-        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
-        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
-        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
+        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
+        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
     }
 }
 

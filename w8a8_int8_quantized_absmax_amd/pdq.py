@@ -39,6 +39,7 @@ SIGNATURES = {
     "pdq_gemm_static": (ctypes.c_int, [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _vp,
                                        _i64, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
+    "pdq_weight_bytes": (_sz, [_i64, _i64]),
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _i64, _vp, _sz, _vp, _vp]),
@@ -108,11 +109,40 @@ def _ld(t: torch.Tensor) -> int:
 
 # ---------------------------------------------------------------------------
 
+def weight_bytes(n: int, k: int) -> int:
+    """Bytes of the packed INT8 weight of N output channels x K (include/pdq.h)."""
+    return int(lib().pdq_weight_bytes(n, k))
+
+
+def unpack_weight(wq: torch.Tensor, n: int, k: int):
+    """The codes wq[n, k] of a packed weight as a host int8 array [N, K].
+
+    Layout (include/pdq.h): 1024-byte blocks of 16 channels x 64 K values,
+    block (g, s) at (g * ceil(K / 64) + s) * 1024, channel r at r * 64 in it,
+    its 16-byte chunk c at position c ^ ((r >> 2) & 3).
+    """
+    import numpy as np
+
+    ng, kt = (n + 15) // 16, (k + 63) // 64
+    b = wq.detach().cpu().numpy()[:ng * kt * 1024].reshape(ng, kt, 16, 4, 16)
+    r = np.arange(16)[:, None]
+    pos = np.arange(4)[None, :] ^ ((r >> 2) & 3)  # [r, c] -> position of chunk c
+    out = b[:, :, r, pos, :]                      # [ng, kt, 16, 4, 16], chunks in K order
+    return out.transpose(0, 2, 1, 3, 4).reshape(ng * 16, kt * 64)[:n, :k]
+
+
+def _check_weight(wq: torch.Tensor, n: int, k: int):
+    if not wq.is_cuda or wq.dtype != torch.int8 or not wq.is_contiguous():
+        raise ValueError("wq must be a contiguous int8 device tensor (a packed weight)")
+    if wq.numel() < weight_bytes(n, k):
+        raise ValueError(f"wq holds {wq.numel()} bytes, a packed {n} x {k} weight needs {weight_bytes(n, k)}")
+
+
 def quantize_weight(w: torch.Tensor):
-    """Per-output-channel symmetric INT8 weight -> (wq int8 [N,K], w_scale f32 [N], colsum i32 [N])."""
+    """Per-output-channel symmetric INT8 weight -> (packed wq int8, w_scale f32 [N], colsum i32 [N])."""
     _check_mat(w, "w")
     n, k = w.shape
-    wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    wq = torch.empty(weight_bytes(n, k), dtype=torch.int8, device=w.device)
     ws = torch.empty(n, dtype=torch.float32, device=w.device)
     cs = torch.empty(n, dtype=torch.int32, device=w.device)
     _call("pdq_quantize_weight", _p(w), _DT[w.dtype], n, k, _ld(w), _p(wq), _p(ws), _p(cs),
@@ -142,7 +172,8 @@ def linear_prefill(x, wq, w_scale, bias=None, want_acc: bool = False, out=None):
     """Per-token dynamic symmetric W8A8 linear -> dict(y bf16, xq, x_scale[, acc])."""
     _check_mat(x, "x")
     m, k = x.shape
-    n = wq.shape[0]
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
     xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
     xs = torch.empty(m, dtype=torch.float32, device=x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
@@ -157,7 +188,8 @@ def linear_decode(x, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None,
     """Per-tensor static asymmetric W8A8 linear -> dict(y bf16, xq[, acc])."""
     _check_mat(x, "x")
     m, k = x.shape
-    n = wq.shape[0]
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
     xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
@@ -177,7 +209,8 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
     _check_mat(x, "x")
     _check_mat(w16, "w16")
     m, k = x.shape
-    n = wq.shape[0]
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
     dev = x.device
     max_outliers = min(max_outliers, k)
     xq = torch.empty((m, k), dtype=torch.int8, device=dev)
@@ -209,7 +242,8 @@ def gemm_per_token(xq, x_scale, wq, w_scale, bias=None, want_acc: bool = False, 
     """INT8 GEMM + per-token/per-channel dequant epilogue -> dict(y bf16[, acc])."""
     _check_mat(xq, "xq", (torch.int8,))
     m, k = xq.shape
-    n = wq.shape[0]
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
     _call("pdq_gemm_per_token", _p(xq), _p(x_scale), m, k, _p(wq), _p(w_scale), _p(bias), n, _p(y),
@@ -232,7 +266,8 @@ def gemm_static(xq, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None, w
     """Skinny INT8 GEMM + zero-point correction + dequant epilogue -> dict(y bf16[, acc])."""
     _check_mat(xq, "xq", (torch.int8,))
     m, k = xq.shape
-    n = wq.shape[0]
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
     _call("pdq_gemm_static", _p(xq), m, k, float(a_scale), int(a_zp), _p(wq), _p(w_scale), _p(colsum),
