@@ -213,8 +213,10 @@ def test_decode_ragged(dtype, m, n, k):
 # 32768; (9, 100, 4096) and (17, 50, 64) sit just past the limits and take the
 # two-kernel path.
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (5, 17, 80), (16, 1000, 1040), (16, 300, 2048),
-                                   (2, 64, 14336), (8, 4096, 4096), (9, 100, 4096), (17, 50, 64)])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (1, 300, 1024), (1, 33, 1040), (1, 4096, 4096),
+                                   (1, 20, 4160), (1, 7, 8192), (5, 17, 80), (16, 1000, 1040),
+                                   (16, 300, 2048), (2, 64, 14336), (8, 4096, 4096), (9, 100, 4096),
+                                   (17, 50, 64)])
 def test_decode_fused_shapes(dtype, m, n, k):
     cal = [synth.activations(4500 + b, 64, k, [1, k - 2], 100.0, offset=0.1, dtype=dtype) for b in range(3)]
     _, s, z = O.calibrate(cal)

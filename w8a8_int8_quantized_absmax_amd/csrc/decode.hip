@@ -33,6 +33,7 @@
 #include "pdq_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace pdq {
 
@@ -93,11 +94,28 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
 }
 
 
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) { return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false); }
+
+// Lane 16 r + t receives lane 16 r + t + J of its DPP row (row_shl J).
+template <int J>
+__device__ __forceinline__ v4i row_shl(v4i v) {
+    if constexpr (J == 0)
+        return v;
+    else
+        return v4i{dpp_i32<0x100 + J>(v.x), dpp_i32<0x100 + J>(v.y), dpp_i32<0x100 + J>(v.z),
+                   dpp_i32<0x100 + J>(v.w)};
+}
+
 constexpr int kFusedBytes = 8192;  // M * K limit of the one-launch path
 // LDS codes per wavefront on that path: M rows x ceil(ceil(K / 64) / 4) K tiles x 64
 constexpr int kFusedWave = kFusedBytes / 4 + 16 * 64;
 
-template <int NMB, bool FUSED, int DT, int kQ = 1>
+// ONEROW (FUSED, M == 1, K <= 4096): lane l quantizes chunk (tile l % 16 of
+// its wavefront, quarter l / 16) into registers, and for tile j the lanes
+// 16 r -- the only ones whose MFMA column is the activation row -- take
+// quarter r from lane 16 r + j of their DPP row: no LDS round trip.
+template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     constexpr int KB = NMB == 1 ? 8 : (NMB == 2 ? 6 : 4);  // K tiles per batch
     __shared__ v4i red[4][NMB][64];
@@ -120,16 +138,22 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     const int nq = M * twmax * 4;
     Raw8<DT> xa[FUSED ? kQ : 1], xb[FUSED ? kQ : 1];
     auto qchunk = [&](int c, int& m, int& s, int& kk) {
-        m = c / (twmax * 4);
-        const int r = c - m * twmax * 4;
-        s = wave + 4 * (r >> 2);
-        kk = s * 64 + 16 * (r & 3);
+        if constexpr (ONEROW) {  // c = lane: tile c % 16, quarter c / 16
+            m = 0;
+            s = wave + 4 * (c & 15);
+            kk = s * 64 + 16 * (c >> 4);
+        } else {
+            m = c / (twmax * 4);
+            const int r = c - m * twmax * 4;
+            s = wave + 4 * (r >> 2);
+            kk = s * 64 + 16 * (r & 3);
+        }
     };
     if constexpr (FUSED) {
 #pragma unroll
         for (int i = 0; i < kQ; ++i) {
             int m, s, kk;
-            qchunk(min(lane + 64 * i, nq - 1), m, s, kk);
+            qchunk(ONEROW ? lane : min(lane + 64 * i, nq - 1), m, s, kk);
             const char* row = static_cast<const char*>(a.x) + (size_t)m * a.ldx * Elem<DT>::bytes;
             const int ck = min(kk, K - 16) / 8;
             xa[i] = load_raw8<DT>(row, ck);
@@ -193,13 +217,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     load(1, f1);
     __builtin_amdgcn_sched_barrier(0);
 
+    v4i xcode = v4i{};  // ONEROW: this lane's codes
     if constexpr (FUSED) {
         const float inv = 1.0f / a.s;
         int nsat = 0;
 #pragma unroll
         for (int i = 0; i < kQ; ++i) {
             const int c = lane + 64 * i;
-            if (c < nq) {
+            if (ONEROW || c < nq) {
                 int m, s, kk;
                 qchunk(c, m, s, kk);
                 v4i code = v4i{};  // zeros past K (the weight is zero there too)
@@ -212,7 +237,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
                     code = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
                     if (blockIdx.x == 0) *reinterpret_cast<v4i*>(a.xq_out + (size_t)m * K + kk) = code;
                 }
-                *reinterpret_cast<v4i*>(&xs[wave][c * 16]) = code;
+                if constexpr (ONEROW)
+                    xcode = code;
+                else
+                    *reinterpret_cast<v4i*>(&xs[wave][c * 16]) = code;
             }
         }
         if (blockIdx.x == 0 && a.sat) {
@@ -221,43 +249,59 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
         }
     }
 
-    // steady state with both refills, then the last one to three batches
-    int b = 0;
-    for (; b + 3 < nbatch; b += 2) {
-        compute(b, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(b + 2, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(b + 1, f1);
-        __builtin_amdgcn_sched_barrier(0);
-        load(b + 3, f1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (b + 2 < nbatch) {
-        compute(b, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(b + 2, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(b + 1, f1);
-        compute(b + 2, f0);
+    if constexpr (ONEROW) {  // at most 16 tiles per wavefront: batches 0 and 1
+        auto run = [&](auto bb, const Frags& f) {
+            constexpr int B = decltype(bb)::value;
+            const v4i xv[KB] = {row_shl<B * KB + 0>(xcode), row_shl<B * KB + 1>(xcode),
+                                row_shl<B * KB + 2>(xcode), row_shl<B * KB + 3>(xcode),
+                                row_shl<B * KB + 4>(xcode), row_shl<B * KB + 5>(xcode),
+                                row_shl<B * KB + 6>(xcode), row_shl<B * KB + 7>(xcode)};
+#pragma unroll
+            for (int i = 0; i < KB; ++i)
+                if (B * KB + i < tsteps) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], xv[i], acc[0], 0, 0, 0);
+        };
+        run(std::integral_constant<int, 0>{}, f0);
+        run(std::integral_constant<int, 1>{}, f1);
     } else {
-        compute(b, f0);
-        if (b + 1 < nbatch) compute(b + 1, f1);
+        // steady state with both refills, then the last one to three batches
+        int b = 0;
+        for (; b + 3 < nbatch; b += 2) {
+            compute(b, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(b + 2, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(b + 1, f1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(b + 3, f1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (b + 2 < nbatch) {
+            compute(b, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(b + 2, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(b + 1, f1);
+            compute(b + 2, f0);
+        } else {
+            compute(b, f0);
+            if (b + 1 < nbatch) compute(b + 1, f1);
+        }
     }
     reduce_and_store<NMB>(a, acc, e, n0, mbase, red);
 }
 
-template <int NMB, bool FUSED, int DT, int kQ = 1>
+template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false>
 void launch_k(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid((a.N + kRows - 1) / kRows, FUSED ? 1 : (a.M + kMRows - 1) / kMRows);
-    hipLaunchKernelGGL((k_decode<NMB, FUSED, DT, kQ>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_decode<NMB, FUSED, DT, kQ, ONEROW>), grid, dim3(256), 0, st, a);
 }
 
 // One-launch path: kQ = 16-value chunks per lane = ceil(M x ceil(tiles / 4) x 4 / 64).
 template <int DT>
 void launch_fused(const DecodeArgs& a, hipStream_t st) {
     const int nq = a.M * (((a.K + 63) / 64 + 3) / 4) * 4;
-    if (nq <= 64) launch_k<1, true, DT, 1>(a, st);
+    if (a.M == 1 && a.K <= 64 * 64) launch_k<1, true, DT, 1, true>(a, st);
+    else if (nq <= 64) launch_k<1, true, DT, 1>(a, st);
     else if (nq <= 128) launch_k<1, true, DT, 2>(a, st);
     else launch_k<1, true, DT, 4>(a, st);
 }
