@@ -15,19 +15,21 @@
 // In the packed layout the 16 channels' K tile is one contiguous 1 KB block
 // (and all of them one contiguous run), so lane l loads its fragment (channel
 // l % 16, K bytes 16 (l / 16) ..) directly: one whole-line, fully coalesced
-// instruction per tile, no LDS transposition.  The epilogue's per-channel operands are loaded first, so
-// their latency hides under the weight stream; the four partial accumulators
-// are summed through LDS.
+// instruction per tile, no LDS transposition.  The epilogue's per-channel
+// operands are loaded first, so their latency hides under the weight stream;
+// the four partial accumulators are summed through LDS.
 //
 // Activations: fragment loads of xq (a few KB, from the cache), up to 64 rows
 // per workgroup row (four register blocks of 16); or -- FUSED, the one-launch
-// path, for M * K up to 8192 -- quantized by every workgroup itself into LDS
-// while its first weight tiles are in flight (static quantization, the PDMIX
-// terminology entry's section 2.3 decode formula and section 2.4 saturation
-// count; workgroup 0 writes xq and counts the saturated values).  Loads are
-// issued in batches of K tiles, two batches in flight, all unconditional
-// (tiles past the wavefront's last are clamped and skipped at use; K bytes
-// past K read in-row bytes that meet the packed weight's zeros).
+// path, for M * K up to 8192 -- quantized inside the kernel while the first
+// weight tiles are in flight (static quantization, the PDMIX terminology
+// entry's section 2.3 decode formula and section 2.4 saturation count;
+// workgroup 0 writes xq and counts the saturated values): each wavefront
+// quantizes exactly the activations of its own K tiles, into its own LDS
+// region, or for one activation row into registers.  Loads are issued in
+// batches of K tiles, two batches in flight, all unconditional (tiles past
+// the wavefront's last are clamped and skipped at use; K bytes past K read
+// in-row bytes that meet the packed weight's zeros).
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -64,8 +66,9 @@ __device__ __forceinline__ EpiOps load_epi(const DecodeArgs& a, int n0, int lane
     return e;
 }
 
-// Sum of the four wavefronts' partial accumulators and the epilogue for the
-// 16 activation rows [mb, mb + 16) handled by register block `blk`.
+// Sum of the four wavefronts' partial accumulators and the epilogue: register
+// block mb holds activation rows mbase + 16 mb .. + 16, and wavefront mb
+// finishes it.
 template <int NMB>
 __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i (&acc)[NMB],
                                                  const EpiOps& e, int n0, int mbase,
@@ -92,7 +95,6 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
         }
     }
 }
-
 
 template <int kCtrl>
 __device__ __forceinline__ int dpp_i32(int v) { return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false); }
