@@ -96,6 +96,14 @@ def test_prefill_k_depths(k):
     assert torch.equal(res["y"], y2)
 
 
+# Per-token codes at decode sizes: up to 64 rows the weight-streaming kernel
+# runs with per-row scales in its epilogue.
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (17, 4096, 4096), (64, 520, 2048), (65, 520, 2048)])
+def test_per_token_skinny(m, n, k):
+    x = synth.activations(2600 + m, m, k, [0, k - 1], 100.0, dtype="bf16")
+    prefill_case(x, synth.weights(2700 + n, n, k, "bf16"), "bf16", bias=synth.bias(2800 + n, n))
+
+
 def test_prefill_empty_batch():
     w = synth.weights(7, 64, 64, "bf16")
     wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
@@ -210,8 +218,8 @@ def test_decode_ragged(dtype, m, n, k):
 
 
 # One-launch path (static quantization inside the GEMM): M <= 16 and M * K <=
-# 32768; (9, 100, 4096) and (17, 50, 64) sit just past the limits and take the
-# two-kernel path.
+# 8192 (the one-row shapes up to K = 8192 and (5, 17, 80)); the other shapes
+# take the two-kernel path, (17, 50, 64) just past the row limit.
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (1, 300, 1024), (1, 33, 1040), (1, 4096, 4096),
                                    (1, 20, 4160), (1, 7, 8192), (5, 17, 80), (16, 1000, 1040),
@@ -222,6 +230,16 @@ def test_decode_fused_shapes(dtype, m, n, k):
     _, s, z = O.calibrate(cal)
     x = synth.activations(4600 + m, m, k, [1, k - 2], 100.0, offset=0.1, dtype=dtype)
     decode_case(x, synth.weights(4700 + n, n, k, dtype), dtype, s, z, bias=synth.bias(4800, n))
+
+
+# Static codes at prefill sizes: past 64 rows the 256 x 256-tile GEMM runs with
+# the zero-point correction in its epilogue.
+@pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096)])
+def test_static_large_m(m, n, k):
+    cal = [synth.activations(4900 + b, 64, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16") for b in range(3)]
+    _, s, z = O.calibrate(cal)
+    x = synth.activations(4950 + m, m, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16")
+    decode_case(x, synth.weights(4960 + n, n, k, "bf16"), "bf16", s, z, bias=synth.bias(4970, n))
 
 
 def test_decode_fused_strided_rows():

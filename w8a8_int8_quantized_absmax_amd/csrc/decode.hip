@@ -4,7 +4,9 @@
 //   y = (S * S_w[n]) * (float)(acc - Z * colsum[n]) [+ bias[n]]
 // i.e. the PDMIX terminology entry's decode formula (section 2.3, static
 // per-tensor S and Z) pushed through the zero-point expansion of the LLM.int8()
-// notes (part 1 section 2) with a symmetric weight.
+// notes (part 1 section 2) with a symmetric weight; or, with per-token scales
+// (the same entry's prefill formula at decode sizes, for the per-token GEMM
+// entry point at small M), y = (S_x[m] * S_w[n]) * (float)acc [+ bias[n]].
 //
 // The weight matrix is read exactly once and is the whole cost (the
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
@@ -47,7 +49,8 @@ constexpr int kMRows = 64;  // activation rows per workgroup (four register bloc
 // Epilogue operands of this lane's four outputs n = n0 + 4 (lane / 16) + r
 // (16x16 accumulator layout: register r is row 4 (lane / 16) + r, the weight
 // row n).  Loaded unconditionally: columns past N are clamped, a missing bias
-// reads the scales and is ignored.
+// or code sum (per-token scales, no zero point) reads the scales and is
+// ignored.
 struct EpiOps {
     float sw[4], bias[4];
     int32_t cs[4];
@@ -56,11 +59,12 @@ struct EpiOps {
 __device__ __forceinline__ EpiOps load_epi(const DecodeArgs& a, int n0, int lane) {
     EpiOps e;
     const float* bp = a.bias ? a.bias : a.sw;
+    const int32_t* cp = a.colsum ? a.colsum : reinterpret_cast<const int32_t*>(a.sw);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int n = min(n0 + 4 * (lane >> 4) + r, a.N - 1);
         e.sw[r] = a.sw[n];
-        e.cs[r] = a.colsum[n];
+        e.cs[r] = cp[n];
         e.bias[r] = bp[n];
     }
     return e;
@@ -87,8 +91,9 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
         if (n < a.N) {
             const int raw = tot[r];
             if (a.acc_out) a.acc_out[(size_t)m * a.N + n] = raw;
-            const int corr = raw - a.z * e.cs[r];
-            const float t = __fmul_rn(a.s, e.sw[r]);
+            // per-token: (S_x[m] * S_w[n]) * acc; static: (S * S_w[n]) * (acc - Z colsum[n])
+            const int corr = a.sa ? raw : raw - a.z * e.cs[r];
+            const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e.sw[r]);
             float y = __fmul_rn(t, (float)corr);
             if (a.bias) y = __fadd_rn(y, e.bias[r]);
             a.y[(size_t)m * a.ldy + n] = f32_to_bf16(y);

@@ -8,7 +8,11 @@
 // rounded to binary32, written as bf16 or f16.  With the side product, side
 // is the 16-bit GEMM over the outlier columns (part 2, "16-bit
 // decomposition" and "mixed-precision decomposition"), run on the 16-bit
-// MFMA into a separate binary32 accumulator per 32x32 sub-tile.
+// MFMA into a separate binary32 accumulator per 32x32 sub-tile.  With a zero
+// point (the static path at large M), S_a is the per-tensor S and acc becomes
+// acc - Z * colsum[n] before the conversion (PDMIX terminology entry section
+// 2.3 decode formula through the zero-point expansion of the LLM.int8() notes,
+// part 1 section 2).
 //
 // Tiling: 256x256 output tile per 256-thread workgroup (4 wavefronts in a
 // 2x2 arrangement, 128x128 each = 4x4 v_mfma_i32_32x32x32_i8 tiles with
@@ -97,7 +101,7 @@ __device__ __forceinline__ void wait_loads_and_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SIDE>
+template <int OUT, bool SIDE, bool ZP>
 __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // The four K-tile buffers (each A[256][64] followed by B[256][64]) are
     // four separate LDS objects, and every access below names its buffer
@@ -111,6 +115,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageAlloc];
     // the tile's row scales, column scales and bias, staged once at the start
     __shared__ __attribute__((aligned(16))) float s_sa[BM], s_sb[BN], s_bias[BN];
+    __shared__ __attribute__((aligned(16))) int32_t s_zc[ZP ? BN : 1];  // z * colsum[n]
     auto stage = [&](auto idx) -> uint8_t* {
         constexpr int i = decltype(idx)::value & (kStages - 1);
         if constexpr (i == 0) return st0;
@@ -136,9 +141,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 
     {
         const int m = m0 + tid, n = n0 + tid;  // 256 threads = BM = BN
-        s_sa[tid] = m < M ? a.sa[m] : 0.0f;
+        s_sa[tid] = m < M ? (a.sa ? a.sa[m] : a.s) : 0.0f;
         s_sb[tid] = n < N ? a.sb[n] : 0.0f;
         s_bias[tid] = (a.bias && n < N) ? a.bias[n] : 0.0f;
+        if constexpr (ZP) s_zc[tid] = n < N ? a.z * a.colsum[n] : 0;
     }
     __syncthreads();
 
@@ -345,12 +351,14 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float sbv[4][4], bv[4][4];
+            int32_t zcv[4][4];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
                     if constexpr (kBias) bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
+                    if constexpr (ZP) zcv[g][e] = s_zc[nl0 + 32 * j + 8 * g + e];
                 }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -378,7 +386,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float t = __fmul_rn(sam[i], sbv[g][e]);
-                        v[e] = __fmul_rn(t, (float)acc[i][j][4 * g + e]);
+                        const int32_t q = ZP ? acc[i][j][4 * g + e] - zcv[g][e] : acc[i][j][4 * g + e];
+                        v[e] = __fmul_rn(t, (float)q);
                         if constexpr (SIDE) v[e] = __fadd_rn(v[e], side[4 * g + e]);
                         if constexpr (kBias) v[e] = __fadd_rn(v[e], bv[g][e]);
                         if constexpr (SIDE)
@@ -421,16 +430,18 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 
 }  // namespace
 
-void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st) {
+void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, bool z_point) {
     if (a.M <= 0 || a.N <= 0) return;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const dim3 grid(tiles), block(256);
-    if (!side)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false>), grid, block, 0, st, a);
+    if (!side && z_point)
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, true>), grid, block, 0, st, a);
+    else if (!side)
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, false>), grid, block, 0, st, a);
     else if (out_dt == kF16)
-        hipLaunchKernelGGL((k_gemm_i8<kF16, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kF16, true, false>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, true, false>), grid, block, 0, st, a);
 }
 
 }  // namespace pdq

@@ -14,6 +14,10 @@ namespace {
 
 constexpr int64_t kMaxK = 65536;        // |sum_k (q_x - Z) q_w| < 255 * 127 * K stays in int32
 constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
+// Activation rows up to which a GEMM runs on the skinny (weight-streaming)
+// kernel of decode.hip rather than on the 256 x 256-tile GEMM, whichever
+// quantization scheme produced the codes.
+constexpr int64_t kSkinnyM = 64;
 
 int elem_bytes(int dt) { return dt == PDQ_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == PDQ_F32 || dt == PDQ_BF16 || dt == PDQ_F16; }
@@ -120,6 +124,22 @@ pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M,
         !aligned(acc_out, 4))
         return PDQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PDQ_OK;
+    if (M <= kSkinnyM) {
+        DecodeArgs d{};
+        d.xq = xq;
+        d.wq = wq;
+        d.M = (int)M;
+        d.N = (int)N;
+        d.K = (int)K;
+        d.sa = x_scale;
+        d.sw = w_scale;
+        d.bias = bias;
+        d.y = y;
+        d.ldy = ldy;
+        d.acc_out = acc_out;
+        launch_decode_gemv(d, static_cast<hipStream_t>(stream));
+        return launched();
+    }
     GemmArgs g{};
     g.A = xq;
     g.B = wq;
@@ -184,6 +204,24 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
         !aligned(acc_out, 4))
         return PDQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PDQ_OK;
+    if (M > kSkinnyM) {
+        GemmArgs g{};
+        g.A = xq;
+        g.B = wq;
+        g.M = (int)M;
+        g.N = (int)N;
+        g.K = (int)K;
+        g.s = a_scale;
+        g.z = a_zp;
+        g.colsum = w_colsum;
+        g.sb = w_scale;
+        g.bias = bias;
+        g.y = y;
+        g.ldy = ldy;
+        g.acc_out = acc_out;
+        launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), true);
+        return launched();
+    }
     DecodeArgs d{};
     d.xq = xq;
     d.wq = wq;

@@ -42,9 +42,12 @@ void launch_minmax_finalize(const float* minmax, float* a_scale, int32_t* a_zp, 
 // gemm_i8.hip -------------------------------------------------------------
 struct GemmArgs {
     const int8_t* A;  // [M, K] dense
-    const int8_t* B;  // [N, K] dense
+    const int8_t* B;  // packed weight (pdq_device.h)
     int M, N, K;
-    const float* sa;  // [M] row scales
+    const float* sa;  // [M] row scales, or null: the per-tensor scale s
+    float s;
+    int z;                  // zero point of A (static path), with colsum
+    const int32_t* colsum;  // [N] code sums of B; used when z_point
     const float* sb;  // [N] column scales
     const float* bias;  // [N] or null
     void* y;
@@ -58,14 +61,16 @@ struct GemmArgs {
     int max_count;
 };
 // out_dt: kBF16 output without side product, or kF16 / kBF16 with the side
-// product when args.xo is set.
-void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st);
+// product when args.xo is set.  z_point (no side product): y uses
+// (float)(acc - z * colsum[n]) -- the static decode formula at any M.
+void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, bool z_point = false);
 
 // decode.hip --------------------------------------------------------------
 struct DecodeArgs {
     const int8_t* xq;  // [M, K] dense (launch_decode_gemv input)
-    const int8_t* wq;  // [N, K] dense
+    const int8_t* wq;  // packed weight (pdq_device.h)
     int M, N, K;
+    const float* sa;  // [M] per-token scales (launch_decode_gemv), or null: s, z
     float s;
     int z;
     const float* sw;
