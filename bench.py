@@ -221,6 +221,72 @@ def bench_decode(args, torch, pdq, synth):
     return dict(S=s, Z=z, K=K, N=N, per_batch=res)
 
 
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
+
+
+def bench_sweep(args, torch, pdq, synth):
+    """C_s / C_g of the two activation schemes over M on the decode linear 4096 -> 4096:
+    per-token dynamic (quantize_per_token + gemm_per_token) against per-tensor
+    static (quantize_static + gemm_static, and the one-launch decode call where
+    it applies), every figure from HIP-graph replays over 16 weight copies (269
+    MB, more than the MALL).  The quantization cost C_s and the GEMM cost C_g
+    are the two terms the pages weigh when they keep dynamic quantization for
+    prefill and static for decode."""
+    c = synth.Decode()
+    K, N = c.K, c.N
+    log(f"[sweep] calibrating on {c.n_calib} batches of [{c.calib_tokens},{K}]")
+    mm = pdq.minmax_state("cuda")
+    for b in range(c.n_calib):
+        out = pdq.calibrate_static(torch.from_numpy(c.calib(b)).to(torch.bfloat16).cuda(), mm,
+                                   finalize=b == c.n_calib - 1)
+    s, z = float(out[0].item()), int(out[1].item())
+    wq0, ws, cs = pdq.quantize_weight(torch.from_numpy(c.w()).to(torch.bfloat16).cuda())
+    nrot = 16
+    wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
+    mmax = max(SWEEP_M)
+    x_all = torch.from_numpy(c.x(mmax)).to(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+    rows = {}
+    for m in SWEEP_M:
+        x = x_all[:m]
+        xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        xsc = torch.empty(m, dtype=torch.float32, device="cuda")
+        y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+        replays = 20 if m <= 256 else 4
+
+        def dq(i):
+            pdq._call("pdq_quantize_per_token", pdq._p(x), pdq.BF16, m, K, K, pdq._p(xq), pdq._p(xsc), pdq._stream(x.device))
+
+        def dg(i):
+            pdq._call("pdq_gemm_per_token", pdq._p(xq), pdq._p(xsc), m, K, pdq._p(wqs[i % nrot]), pdq._p(ws),
+                      None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+        def sq(i):
+            pdq._call("pdq_quantize_static", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(xq), None, pdq._stream(x.device))
+
+        def sg(i):
+            pdq._call("pdq_gemm_static", pdq._p(xq), m, K, s, z, pdq._p(wqs[i % nrot]), pdq._p(ws), pdq._p(cs),
+                      None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+        def call(i):
+            pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(wqs[i % nrot]),
+                      pdq._p(ws), pdq._p(cs), None, N, pdq._p(xq), pdq._p(y), N, None, None, pdq._stream(x.device))
+
+        t = {name: graph_timed(fn, nrot, replays, stream) * 1e3
+             for name, fn in (("dyn_quant", dq), ("dyn_gemm", dg), ("static_quant", sq),
+                              ("static_gemm", sg), ("static_call", call))}
+        t["dyn_total"] = t["dyn_quant"] + t["dyn_gemm"]
+        t["static_total"] = t["static_quant"] + t["static_gemm"]
+        t["dyn_Cs_over_Cg"] = t["dyn_quant"] / t["dyn_gemm"]
+        t["static_Cs_over_Cg"] = t["static_quant"] / t["static_gemm"]
+        t["gemm_TOPS_dyn"] = 2.0 * m * N * K / (t["dyn_gemm"] * 1e-6) / 1e12
+        rows[str(m)] = {k: round(v, 3) for k, v in t.items()}
+        log(f"[sweep] M={m:5d}: dynamic {t['dyn_quant']:8.2f} + {t['dyn_gemm']:8.2f} us, static "
+            f"{t['static_quant']:8.2f} + {t['static_gemm']:8.2f} us (one call {t['static_call']:8.2f} us)")
+    del wqs
+    return dict(S=s, Z=z, K=K, N=N, per_m=rows)
+
+
 def bench_llm_int8(args, torch, pdq, synth):
     c = synth.LlmInt8()
     M, K, N = c.M, c.K, c.N
@@ -278,6 +344,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=60)  # ~13 ms of prefill steps: the clock settles first
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill"], default="all")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline run: the per-token vs static C_s / C_g sweep over "
+                         "M on the decode linear (one JSON line of its own)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run a fill and a plain device copy of this many MiB (known HBM "
                          "traffic, for scaling hardware byte counters)")
@@ -293,6 +362,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     pdq.lib()
+    if args.sweep:
+        sw = bench_sweep(args, torch, pdq, synth)
+        print(json.dumps({"metric": "cs_cg_sweep_us", "unit": "us", "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": "decode linear 4096 -> 4096, bf16 activations, "
+                                                 "per-token dynamic vs per-tensor static INT8",
+                                     "M": list(SWEEP_M)},
+                          "S": sw["S"], "Z": sw["Z"], "per_m": sw["per_m"]}), flush=True)
+        return
     if args.copy_probe:
         # known traffic: the fill kernel writes size bytes, the copy kernel
         # reads size bytes and writes size bytes (far more than the 256 MB MALL)
