@@ -119,7 +119,7 @@ def bench_prefill(args, torch, pdq, synth):
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
     xs = [x] + [x.clone() for _ in range(nrot - 1)]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xq = torch.empty(pdq.act_bytes(M, K), dtype=torch.int8, device="cuda")  # packed codes
     xsc = torch.empty(M, dtype=torch.float32, device="cuda")
     xqs = [xq] + [xq.clone() for _ in range(nrot - 1)]
     stream = torch.cuda.current_stream()
@@ -176,7 +176,7 @@ def bench_decode(args, torch, pdq, synth):
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     for m in c.batches:
         x = torch.from_numpy(c.x(m)).to(torch.bfloat16).cuda()
-        xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        xq = torch.empty(pdq.act_bytes(m, K), dtype=torch.int8, device="cuda")  # packed codes
         y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
         sat.zero_()
         pdq.linear_decode(x, s, z, wq0, ws, cs, sat_count=sat, out=y, xq=xq)
@@ -249,7 +249,7 @@ def bench_sweep(args, torch, pdq, synth):
     rows = {}
     for m in SWEEP_M:
         x = x_all[:m]
-        xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        xq = torch.empty(pdq.act_bytes(m, K), dtype=torch.int8, device="cuda")  # packed codes
         xsc = torch.empty(m, dtype=torch.float32, device="cuda")
         y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
         replays = 20 if m <= 256 else 4
@@ -299,7 +299,7 @@ def bench_llm_int8(args, torch, pdq, synth):
     max_out = 64
     ws_bytes = pdq.int8_outlier_workspace_bytes(M, N, K, max_out)
     work = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xq = torch.empty(pdq.act_bytes(M, K), dtype=torch.int8, device="cuda")  # packed codes
     xs = torch.empty(M, dtype=torch.float32, device="cuda")
     idx = torch.empty(max_out, dtype=torch.int32, device="cuda")
     cnt = torch.empty(1, dtype=torch.int32, device="cuda")

@@ -96,6 +96,29 @@ const char* pdq_status_string(pdq_status s);
  */
 size_t pdq_weight_bytes(int64_t N, int64_t K);
 
+/*
+ * Activation codes (the xq of every entry point below) use the same packed
+ * layout with M rows in place of the N channels: pdq_act_bytes(M, K) bytes
+ * (= pdq_weight_bytes(M, K)), rows >= M and K values >= K written as 0.  The
+ * quantizers write xq in it and the GEMMs read it: as the 16-row x 64 tiles
+ * of the MFMA operands, every load a whole cache line.
+ */
+size_t pdq_act_bytes(int64_t M, int64_t K);
+
+/*
+ * The INT8 GEMM kernel that pdq_gemm_per_token, pdq_gemm_static,
+ * pdq_linear_prefill and pdq_linear_decode run for M activation rows and N
+ * weight channels (pdq_linear_decode runs neither when it fuses the
+ * quantizer into the skinny kernel; pdq_linear_int8_outlier always runs the
+ * tiled one).  Both give the same bits.  -1 when M < 1 or N < 1.
+ *   PDQ_GEMM_SKINNY  one pass over the weight per 64 activation rows,
+ *                    16 channels per workgroup (all M <= 64, and larger M
+ *                    while that is estimated to be faster)
+ *   PDQ_GEMM_TILED   256 x 256 output tiles staged through LDS
+ */
+enum { PDQ_GEMM_SKINNY = 0, PDQ_GEMM_TILED = 1 };
+int pdq_gemm_kernel(int64_t M, int64_t N);
+
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream);
 
@@ -129,8 +152,9 @@ pdq_status pdq_calibrate_static(const void* x, pdq_dtype x_dt, int64_t M, int64_
  *   x        [M, K] of x_dt (F32, BF16, F16), row pitch ldx
  *   wq       packed INT8 weight from pdq_quantize_weight; w_scale [N] float
  *   bias     [N] float or NULL
- *   xq       [M, K] int8 out (dense), x_scale [M] float out: the quantized
- *            activations and their per-token scales (also the GEMM operand)
+ *   xq       packed int8 codes out (pdq_act_bytes(M, K) bytes), x_scale [M]
+ *            float out: the quantized activations and their per-token
+ *            scales (also the GEMM operand)
  *   y        [M, N] bfloat16 out (uint16 bit patterns), row pitch ldy >= N
  *            y = bf16((S_x[m] * S_w[n]) * (float)acc[m,n] [+ bias[n]])
  *   acc_out  [M, N] int32 out (dense) or NULL: acc = sum_k xq[m,k] wq[n,k]
@@ -153,7 +177,8 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
  *              pdq_calibrate_static)
  *   wq, w_scale, w_colsum  from pdq_quantize_weight (w_colsum required)
  *   bias       [N] float or NULL
- *   xq         [M, K] int8 out (dense): q = clamp(rne(x / S) + Z, -128, 127)
+ *   xq         packed int8 codes out (pdq_act_bytes(M, K) bytes):
+ *              q = clamp(rne(x / S) + Z, -128, 127)
  *   y          [M, N] bfloat16 out, row pitch ldy:
  *              y = bf16((S * S_w[n]) * (float)(acc - Z * colsum[n]) [+ bias[n]])
  *   acc_out    [M, N] int32 out or NULL: raw acc = sum_k xq wq (before the
@@ -175,7 +200,7 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
  * callers that quantize an activation once and feed several weight matrices
  * with it (e.g. separate Q, K and V projections of one hidden state), or that
  * produce the INT8 activations themselves.  Arguments as in the composite
- * calls above; xq is dense [M, K] int8.
+ * calls above; xq is the packed [M, K] codes (pdq_act_bytes(M, K) bytes).
  */
 /* Per-token quantizer: S_x[m] = max_k |x[m,k]| / 127, xq = clamp(rne(x / S_x), -127, 127). */
 pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
@@ -214,7 +239,8 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
  *   w16          [N, K] of dt: the original 16-bit weight, row pitch ldw
  *   bias         [N] float or NULL
  *   y            [M, N] of dt out, row pitch ldy
- *   xq           [M, K] int8 out: regular columns quantized, outliers 0
+ *   xq           packed int8 codes out (pdq_act_bytes(M, K) bytes): regular
+ *                columns quantized, outliers 0
  *   x_scale      [M] float out: absmax over regular columns / 127
  *   outlier_idx  int32[max_outliers] out: ascending outlier columns (the
  *                first max_outliers of them)

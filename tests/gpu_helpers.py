@@ -22,13 +22,29 @@ def dev(a: np.ndarray, dtype: str = "f32") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(TORCH_DT[dtype]).cuda()
 
 
-def host(t: torch.Tensor) -> np.ndarray:
+def host(t) -> np.ndarray:
+    """A device tensor as a host array (16-bit floats as their bit patterns);
+    packed activation codes as their [rows, K] matrix."""
+    from w8a8_int8_quantized_absmax_amd import pdq
+
+    if isinstance(t, pdq.Codes):
+        return t.unpack()
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def codes_equal(xq, ref: np.ndarray) -> bool:
+    """Packed device codes (pdq.Codes) hold exactly the packed image of the
+    oracle's [M, K] codes: layout, values and the zero padding."""
+    from packing import pack
+
+    assert xq.shape == ref.shape, (xq.shape, ref.shape)
+    img = pack(np.asarray(ref, np.int8))
+    return bool(np.array_equal(xq.data.detach().cpu().numpy()[:img.size], img))
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

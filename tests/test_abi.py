@@ -145,6 +145,14 @@ def test_weight_bytes(L):
     assert L.pdq_weight_bytes(-1, 64) == 0
 
 
+def test_act_bytes(L):
+    # activation codes: the same layout, M rows in place of N channels
+    for m, k in [(1, 16), (1, 4096), (17, 4096), (4096, 4096), (0, 64), (300, 1040)]:
+        assert L.pdq_act_bytes(m, k) == L.pdq_weight_bytes(m, k)
+    assert L.pdq_act_bytes(1, 4096) == 16 * 4096
+    assert L.pdq_act_bytes(-3, 64) == 0
+
+
 def test_unpack_weight_inverts_the_layout():
     """pdq.unpack_weight against the test-side packer written from the header."""
     import torch

@@ -11,8 +11,8 @@ import torch
 
 import oracle.pdq_oracle as O
 from w8a8_int8_quantized_absmax_amd import pdq, synth
-from gpu_helpers import check_16bit, dev, host, sample_rows
-from packing import pack_weight
+from gpu_helpers import check_16bit, codes_equal, dev, host, sample_rows
+from packing import pack, pack_weight
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -55,7 +55,7 @@ def prefill_case(x, w, dtype, bias=None, rows=None, exact=True):
     b = None if bias is None else torch.from_numpy(bias).cuda()
     res = pdq.linear_prefill(dev(x, dtype), wq, ws, b, want_acc=True)
     xq_ref, sx_ref = O.quantize_rows_absmax(x)
-    assert np.array_equal(host(res["xq"]), xq_ref)
+    assert codes_equal(res["xq"], xq_ref)
     assert np.array_equal(host(res["x_scale"]).view(np.uint32), sx_ref.view(np.uint32))
     r = np.arange(x.shape[0]) if rows is None else rows
     acc_ref = O.int_matmul(xq_ref[r], rq)
@@ -71,9 +71,12 @@ def test_prefill_tiny_f32():
     prefill_case(c.x(), c.w(), "f32", bias=c.bias())
 
 
+# (1100, 2600, 1040) runs on the tiled GEMM, the others on the skinny kernel.
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(300, 700, 1040), (1, 257, 128), (257, 1, 16), (513, 256, 2048)])
+@pytest.mark.parametrize("m,n,k", [(300, 700, 1040), (1, 257, 128), (257, 1, 16), (513, 256, 2048),
+                                   (1100, 2600, 1040)])
 def test_prefill_ragged(dtype, m, n, k):
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
     x = synth.activations(2000 + m, m, k, [0, k - 1, k // 3], 100.0, dtype=dtype)
     if m > 2:
         x[2, :] = 0.0  # all-zero token: scale 1, codes 0
@@ -81,13 +84,18 @@ def test_prefill_ragged(dtype, m, n, k):
     prefill_case(x, w, dtype, bias=synth.bias(2200 + n, n))
 
 
-# K tiles of 64: every count modulo the depth of the kernel's LDS ring (five),
-# whole and ragged, with and without bias.
-@pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 336, 640, 656, 1216, 1280])
-def test_prefill_k_depths(k):
-    x = synth.activations(2300 + k, 300, k, [1, k - 2], 100.0, dtype="bf16")
-    w = synth.weights(2400 + k, 520, k, "bf16")
-    bias = synth.bias(2500 + k, 520) if k % 128 == 0 else None
+# K tiles of 64: every count modulo the depth of the tiled GEMM's LDS ring
+# (four) and of the skinny kernel's batches (two in flight of up to eight
+# tiles per wavefront, four wavefronts), whole and ragged, with and without
+# bias; M x N = 1100 x 2600 runs on the tiled GEMM, 300 x 520 on the skinny
+# kernel.
+@pytest.mark.parametrize("m,n", [(1100, 2600), (300, 520)])
+@pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 336, 640, 656, 1216, 1280, 2112, 4160])
+def test_prefill_k_depths(m, n, k):
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+    x = synth.activations(2300 + k, m, k, [1, k - 2], 100.0, dtype="bf16")
+    w = synth.weights(2400 + k, n, k, "bf16")
+    bias = synth.bias(2500 + k, n) if k % 128 == 0 else None
     res = prefill_case(x, w, "bf16", bias=bias)
     # the same output without the INT32 accumulator copy
     wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
@@ -96,10 +104,12 @@ def test_prefill_k_depths(k):
     assert torch.equal(res["y"], y2)
 
 
-# Per-token codes at decode sizes: up to 64 rows the weight-streaming kernel
-# runs with per-row scales in its epilogue.
-@pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (17, 4096, 4096), (64, 520, 2048), (65, 520, 2048)])
+# Per-token codes at decode sizes: the weight-streaming kernel runs with
+# per-row scales in its epilogue.
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (17, 4096, 4096), (64, 520, 2048), (65, 520, 2048),
+                                   (130, 700, 1040), (600, 1000, 1040), (256, 4096, 4096)])
 def test_per_token_skinny(m, n, k):
+    assert pdq.gemm_kernel(m, n) == "skinny"
     x = synth.activations(2600 + m, m, k, [0, k - 1], 100.0, dtype="bf16")
     prefill_case(x, synth.weights(2700 + n, n, k, "bf16"), "bf16", bias=synth.bias(2800 + n, n))
 
@@ -187,7 +197,7 @@ def decode_case(x, w, dtype, s, z, bias=None, exact=True):
     b = None if bias is None else torch.from_numpy(bias).cuda()
     res = pdq.linear_decode(dev(x, dtype), s, z, wq, ws, cs, b, sat_count=sat, want_acc=True)
     ref = O.linear_decode(x, F32(s), z, rq, rs, rc, bias)
-    assert np.array_equal(host(res["xq"]), ref["xq"])
+    assert codes_equal(res["xq"], ref["xq"])
     assert int(host(sat)[0]) == ref["sat"]
     assert np.array_equal(host(res["acc"]), ref["acc"])
     check_16bit(host(res["y"]), ref["y32"], "bf16", exact)
@@ -232,10 +242,12 @@ def test_decode_fused_shapes(dtype, m, n, k):
     decode_case(x, synth.weights(4700 + n, n, k, dtype), dtype, s, z, bias=synth.bias(4800, n))
 
 
-# Static codes at prefill sizes: past 64 rows the 256 x 256-tile GEMM runs with
-# the zero-point correction in its epilogue.
-@pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096)])
+# Static codes past 64 rows: the zero-point correction in the epilogue of
+# the skinny kernel (the first three) and of the tiled GEMM (the others).
+@pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096),
+                                   (1100, 2600, 1040), (700, 4096, 4096), (2000, 1500, 2048)])
 def test_static_large_m(m, n, k):
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m in (1100, 700, 2000) else "skinny")
     cal = [synth.activations(4900 + b, 64, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16") for b in range(3)]
     _, s, z = O.calibrate(cal)
     x = synth.activations(4950 + m, m, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16")
@@ -252,7 +264,7 @@ def test_decode_fused_strided_rows():
     assert xt.stride(0) == k + 48
     res = pdq.linear_decode(xt, s, z, wq, ws, cs, want_acc=True)
     ref = O.linear_decode(np.ascontiguousarray(x), s, z, rq, rs, rc)
-    assert np.array_equal(host(res["xq"]), ref["xq"])
+    assert codes_equal(res["xq"], ref["xq"])
     assert np.array_equal(host(res["acc"]), ref["acc"])
     check_16bit(host(res["y"]), ref["y32"], "bf16", True)
 
@@ -277,7 +289,7 @@ def outlier_case(x, w, dtype, thr, bias=None, max_out=64, rows=None):
     assert cnt == len(cols)
     assert host(res["idx"])[:min(cnt, max_out)].tolist() == cols[:max_out].tolist()
     xq_ref, sx_ref = O.quantize_rows_regular(x, cols)
-    assert np.array_equal(host(res["xq"]), xq_ref)
+    assert codes_equal(res["xq"], xq_ref)
     assert np.array_equal(host(res["x_scale"]).view(np.uint32), sx_ref.view(np.uint32))
     r = np.arange(x.shape[0]) if rows is None else rows
     ref = O.linear_int8_outlier(x[r], w, rq, rs, thr, bias) if rows is None else None
@@ -324,14 +336,14 @@ def test_outlier_threshold_infinite_equals_vector_wise():
     assert cnt == 0
     wq, ws, _ = pdq.quantize_weight(dev(w, "f16"))
     pre = pdq.linear_prefill(dev(x, "f16"), wq, ws, want_acc=True)
-    assert torch.equal(pre["xq"], res["xq"]) and torch.equal(pre["acc"], res["acc"])
+    assert torch.equal(pre["xq"].data, res["xq"].data) and torch.equal(pre["acc"], res["acc"])
 
 
 def test_outlier_all_columns_is_16bit_matmul():
     x = synth.activations(5700, 20, 64, [], dtype="f16")
     w = synth.weights(5701, 48, 64, "f16")
     res, cnt = outlier_case(x, w, "f16", -1.0, max_out=64)
-    assert cnt == 64 and not res["xq"].any() and not res["acc"].any()
+    assert cnt == 64 and not res["xq"].data.any() and not res["acc"].any()
 
 
 def test_outlier_capacity_exceeded_poisons_output():
@@ -370,8 +382,9 @@ def test_outlier_single_hits_in_far_row_blocks():
     wq, ws, _ = pdq.quantize_weight(w)
     a = pdq.linear_int8_outlier(wide[:, :k], 6.0, wq, ws, w)
     b = pdq.linear_int8_outlier(wide[:, :k].contiguous(), 6.0, wq, ws, w)
-    for key in ("y", "xq", "x_scale", "count"):
+    for key in ("y", "x_scale", "count"):
         assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["xq"].data, b["xq"].data)
     assert torch.equal(a["idx"][:2], b["idx"][:2])
 
 
@@ -392,7 +405,7 @@ def test_per_token_blocks_shared_activation():
     x = synth.activations(6000, 200, 1024, [7, 900], 100.0, dtype="bf16")
     xq, xs = pdq.quantize_per_token(dev(x, "bf16"))
     xq_ref, sx_ref = O.quantize_rows_absmax(x)
-    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(xs), sx_ref)
+    assert codes_equal(xq, xq_ref) and np.array_equal(host(xs), sx_ref)
     for n in (96, 300):  # e.g. two projections of one hidden state
         w = synth.weights(6001 + n, n, 1024, "bf16")
         wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
@@ -409,7 +422,7 @@ def test_static_blocks():
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     xq = pdq.quantize_static(dev(x, "f16"), s, z, sat_count=sat)
     ref_q, ref_sat = O.quantize_static(x, s, z)
-    assert np.array_equal(host(xq), ref_q) and int(host(sat)[0]) == ref_sat
+    assert codes_equal(xq, ref_q) and int(host(sat)[0]) == ref_sat
     w = synth.weights(6101, 130, 512, "f16")
     wq, ws, cs = pdq.quantize_weight(dev(w, "f16"))
     rq, rs, rc = O.quantize_weight(w)
@@ -422,16 +435,15 @@ def test_static_blocks():
 @pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (1, 33, 1040), (1, 7, 16), (2, 300, 4096),
                                    (16, 100, 3072), (17, 64, 512), (1, 50, 4112)])
 def test_static_gemm_skinny(m, n, k):
-    # the GEMM alone on already-quantized activations: M = 1 (dot-product
-    # kernel), M <= 16 with K <= 4096 (LDS-staged MFMA), otherwise the
-    # register-path kernel
+    # the GEMM alone on already-quantized activations (packed on the host
+    # from the layout's definition), on the skinny kernel
     xq = synth.random_int8(6200 + m, (m, k))
     s, z = F32(0.37), -11
     w = synth.weights(6201 + n, n, k, "bf16")
     wq, ws, cs, (rq, rs, rc) = weight_case(w, "bf16")
     bias = synth.bias(6202, n)
-    res = pdq.gemm_static(torch.from_numpy(xq).cuda(), s, z, wq, ws, cs, torch.from_numpy(bias).cuda(),
-                          want_acc=True)
+    res = pdq.gemm_static(pdq.Codes(torch.from_numpy(pack(xq)).cuda(), m, k), s, z, wq, ws, cs,
+                          torch.from_numpy(bias).cuda(), want_acc=True)
     acc = O.int_matmul(xq, rq)
     assert np.array_equal(host(res["acc"]), acc)
     check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc, rc, z), s, rs, bias), "bf16", exact=True)
@@ -453,6 +465,30 @@ def _near_ties(s, kmax, ulps=3):
     return np.concatenate(vals).astype(F32)
 
 
+@pytest.mark.parametrize("m", [1, 5, 37, 70, 300])
+def test_gemm_ignores_code_padding(m):
+    """Only the codes reach the results: the GEMMs give the same bits when the
+    padding of the packed activations (rows past M, K values past K) holds
+    arbitrary bytes instead of zeros."""
+    n, k = 200, 1040
+    xq = synth.random_int8(6300 + m, (m, k))
+    img = pack(xq)
+    pad = pack(np.ones((m, k), np.int8)) == 0
+    dirty = np.where(pad, synth.random_int8(6301 + m, img.shape), img)
+    assert (dirty != img).any() or not pad.any()
+    w = synth.weights(6302, n, k, "bf16")
+    wq, ws, cs = pdq.quantize_weight(dev(w, "bf16"))
+    xs = torch.from_numpy(np.linspace(0.01, 0.2, m, dtype=F32)).cuda()
+    outs = []
+    for image in (img, dirty):
+        codes = pdq.Codes(torch.from_numpy(image).cuda(), m, k)
+        a = pdq.gemm_static(codes, F32(0.37), -11, wq, ws, cs, want_acc=True)
+        b = pdq.gemm_per_token(codes, xs, wq, ws, want_acc=True)
+        outs.append([host(t) for t in (a["y"], a["acc"], b["y"], b["acc"])])
+    for clean, junk in zip(*outs):
+        assert np.array_equal(clean, junk)
+
+
 def test_per_token_rounding_near_ties():
     rows = []
     for c in (127.0, 1.0, 3.3, 0.021, 5e4, 2.0):
@@ -467,7 +503,7 @@ def test_per_token_rounding_near_ties():
     xq, xs = pdq.quantize_per_token(dev(x, "f32"))
     q_ref, s_ref = O.quantize_rows_absmax(x)
     assert np.array_equal(host(xs), s_ref)
-    assert np.array_equal(host(xq), q_ref)
+    assert codes_equal(xq, q_ref)
 
 
 @pytest.mark.parametrize("s", [0.5, 3.3963, 17.25, 1e-3])
@@ -485,7 +521,7 @@ def test_decode_fused_rounding_near_ties(s):
             sat = torch.zeros(1, dtype=torch.int32, device="cuda")
             res = pdq.linear_decode(dev(x, "f32"), s, z, wq, ws, cs, sat_count=sat, want_acc=True)
             ref = O.linear_decode(x, s, z, rq, rs, rc)
-            assert np.array_equal(host(res["xq"]), ref["xq"])
+            assert codes_equal(res["xq"], ref["xq"])
             assert int(host(sat)[0]) == ref["sat"]
             assert np.array_equal(host(res["acc"]), ref["acc"])
 
@@ -499,5 +535,5 @@ def test_static_rounding_near_ties(s):
         sat = torch.zeros(1, dtype=torch.int32, device="cuda")
         xq = pdq.quantize_static(dev(v, "f32"), s, z, sat_count=sat)
         q_ref, sat_ref = O.quantize_static(v, s, z)
-        assert np.array_equal(host(xq), q_ref)
+        assert codes_equal(xq, q_ref)
         assert int(host(sat)[0]) == sat_ref

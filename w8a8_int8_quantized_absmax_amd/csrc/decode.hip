@@ -21,17 +21,21 @@
 // operands are loaded first, so their latency hides under the weight stream;
 // the four partial accumulators are summed through LDS.
 //
-// Activations: fragment loads of xq (a few KB, from the cache), up to 64 rows
-// per workgroup row (four register blocks of 16); or -- FUSED, the one-launch
-// path, for M * K up to 8192 -- quantized inside the kernel while the first
-// weight tiles are in flight (static quantization, the PDMIX terminology
-// entry's section 2.3 decode formula and section 2.4 saturation count;
-// workgroup 0 writes xq and counts the saturated values): each wavefront
-// quantizes exactly the activations of its own K tiles, into its own LDS
-// region, or for one activation row into registers.  Loads are issued in
-// batches of K tiles, two batches in flight, all unconditional (tiles past
-// the wavefront's last are clamped and skipped at use; K bytes past K read
-// in-row bytes that meet the packed weight's zeros).
+// Activations: fragment loads of the packed xq (from the cache), up to 64
+// rows per workgroup row (four register blocks of 16), one 16-row block per
+// K tile and register block -- again one contiguous 1 KB load (the rows of a
+// partial block past M are clamped onto its last row, so that they cost no
+// extra lines); or -- FUSED, the one-launch path, for M * K up to 8192 --
+// quantized inside the kernel while the first weight tiles are in flight
+// (static quantization, the PDMIX terminology entry's section 2.3 decode
+// formula and section 2.4 saturation count; workgroup 0 writes the codes of
+// xq and counts the saturated values, the first few others write its zero
+// padding rows): each wavefront quantizes exactly the activations of its own
+// K tiles, into its own LDS region, or for one activation row into
+// registers.  Loads are issued in batches of K tiles, two batches in flight,
+// all unconditional (tiles past the wavefront's last are clamped and skipped
+// at use; K values past K are zeros in the packed operands, and in the
+// quantized LDS copy).
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -171,9 +175,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
     // this lane's weight fragment in K tile s: wp + s * kWBlock
     const int8_t* wp = a.wq + wpack_block(n0 / kWGroup, 0, nsteps) + wpack_pos(lane & 15, lane >> 4);
+    // this lane's activation fragment of register block mb in K tile s:
+    // xp[mb] + s * kWBlock (row lane % 16 of the block, clamped into M)
     const int8_t* xp[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) xp[mb] = a.xq + (size_t)min(mbase + mb * 16 + (lane & 15), M - 1) * K;
+    for (int mb = 0; mb < NMB; ++mb) {
+        const int g = min(mbase / 16 + mb, (M - 1) / 16);
+        xp[mb] = a.xq + wpack_block(g, 0, nsteps) + wpack_pos(min(lane & 15, M - 1 - 16 * g), lane >> 4);
+    }
     const int xrow = min(lane & 15, M - 1);  // FUSED (M <= 16)
     const int8_t* xw = xs[FUSED ? wave : 0];
     const int tsteps = (nsteps - wave + 3) / 4;
@@ -183,7 +192,6 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
         v4i w[KB];
         v4i x[FUSED ? 1 : NMB][KB];
     };
-    auto kof = [&](int b, int i) { return min(min(wave + 4 * (b * KB + i), nsteps - 1) * 64 + kl, K - 16); };
     auto load = [&](int b, Frags& f) {
 #pragma unroll
         for (int i = 0; i < KB; ++i) {
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
             f.w[i] = *reinterpret_cast<const v4i*>(wp + (size_t)s * kWBlock);
             if constexpr (!FUSED) {
 #pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) f.x[mb][i] = *reinterpret_cast<const v4i*>(xp[mb] + kof(b, i));
+                for (int mb = 0; mb < NMB; ++mb) f.x[mb][i] = *reinterpret_cast<const v4i*>(xp[mb] + (size_t)s * kWBlock);
             }
         }
     };
@@ -235,14 +243,18 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
                 int m, s, kk;
                 qchunk(c, m, s, kk);
                 v4i code = v4i{};  // zeros past K (the weight is zero there too)
-                if (s < nsteps && kk < K) {
-                    float v[8];
-                    widen8<DT>(xa[i], v);
-                    const uint2 lo = static_codes8(v, a.s, inv, a.z, nsat);
-                    widen8<DT>(xb[i], v);
-                    const uint2 hi = static_codes8(v, a.s, inv, a.z, nsat);
-                    code = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-                    if (blockIdx.x == 0) *reinterpret_cast<v4i*>(a.xq_out + (size_t)m * K + kk) = code;
+                if (s < nsteps) {
+                    if (kk < K) {
+                        float v[8];
+                        widen8<DT>(xa[i], v);
+                        const uint2 lo = static_codes8(v, a.s, inv, a.z, nsat);
+                        widen8<DT>(xb[i], v);
+                        const uint2 hi = static_codes8(v, a.s, inv, a.z, nsat);
+                        code = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+                    }
+                    if (blockIdx.x == 0)
+                        *reinterpret_cast<v4i*>(a.xq_out + wpack_block(0, s, nsteps) + wpack_pos(m, (kk >> 4) & 3)) =
+                            code;
                 }
                 if constexpr (ONEROW)
                     xcode = code;
@@ -253,6 +265,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
         if (blockIdx.x == 0 && a.sat) {
             nsat = wave_sum(nsat);
             if (lane == 0 && nsat) atomicAdd(a.sat, (uint32_t)nsat);
+        }
+        // the zero rows M .. 15 of the codes' one 16-row group: 16-byte chunk
+        // p = (row - M, tile, chunk) of them per thread, by the workgroups
+        // after the first (or by the only one)
+        const int first = gridDim.x > 1 ? 1 : 0, nwg = gridDim.x - first;
+        const int npad = (kWGroup - M) * nsteps * 4;
+        if ((int)blockIdx.x >= first) {
+            for (int p = (blockIdx.x - first) * 256 + tid; p < npad; p += nwg * 256) {
+                const int r = M + p / (nsteps * 4), t = (p / 4) % nsteps;
+                *reinterpret_cast<v4i*>(a.xq_out + wpack_block(0, t, nsteps) + wpack_pos(r, p & 3)) = v4i{};
+            }
         }
     }
 

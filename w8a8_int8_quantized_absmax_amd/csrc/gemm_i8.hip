@@ -18,15 +18,15 @@
 // 2x2 arrangement, 128x128 each = 4x4 v_mfma_i32_32x32x32_i8 tiles with
 // their INT32 accumulators in registers, W rows as the MFMA row operand so
 // that each lane ends up with runs of 4 consecutive outputs), K staged through
-// LDS 64 bytes at a time.  A and B are both K-contiguous, so a K tile of 256
-// rows is 256 lines of 64 bytes, XOR-swizzled in 16-byte chunks so that the
-// 128-bit fragment reads are free of bank conflicts (see swz).  Tiles move
-// global -> LDS directly (global_load_lds, no register staging) through a
-// ring of four LDS buffers: three K tiles are in flight while one feeds the
-// MFMAs.  B is the packed weight (pdq_device.h), whose 1 KB blocks already
-// are the LDS images of 16 rows: every B load instruction is one block,
-// every request a whole cache line (a row-major panel costs a half-line
-// request per row).
+// LDS 64 bytes at a time.  A K tile of 256 rows is 256 lines of 64 bytes,
+// XOR-swizzled in 16-byte chunks so that the 128-bit fragment reads are free
+// of bank conflicts (see swz).  Tiles move global -> LDS directly
+// (global_load_lds, no register staging) through a ring of four LDS buffers:
+// three K tiles are in flight while one feeds the MFMAs.  A and B are both
+// packed (pdq_device.h): their 1 KB blocks already are the LDS images of 16
+// rows, so every load instruction is one block, every request a whole cache
+// line (a row-major panel costs a half-line request per row), and the zeros
+// of the K padding make a partial last K tile need no masking.
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -150,34 +150,24 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 
 
     // Global -> LDS without registers: one global_load_lds_dwordx4 moves 64
-    // lanes x 16 bytes into 1 KB of LDS (16 rows of 64 bytes), lane l landing
-    // in row l/4, chunk position l%4.  The lane fetches the logical chunk that
-    // the swizzle puts at its position (the swizzle is an involution in kc).
-    // Wave w fills rows [64w, 64w + 64) of both the A and the B tile: 4 + 4
-    // instructions per K tile.  A rows past M are clamped onto the last row:
-    // they only feed outputs that are never stored.  A chunks past K are
-    // clamped onto the last chunk and zeroed in the A fragments of the last K
-    // tile, which zeroes their products (the packed B holds zeros there and
-    // in its rows past N).
-    const int rbase = wave * 64 + (lane >> 2);
-    // row r = rbase + 16 i has (r >> 2) & 3 == (lane >> 4) & 3 for every i
-    const int koff = swz_pos(rbase, lane & 3) * 16;
+    // lanes x 16 bytes into 1 KB of LDS, lane l's 16 bytes at 16 l: one packed
+    // block, which already is the swizzled image of its 16 rows.  Wave w fills
+    // rows [64w, 64w + 64) of both the A and the B tile, four 16-row groups
+    // each: 4 + 4 instructions per K tile.  Groups past the last (of A or B)
+    // are clamped onto it: they only feed outputs that are never stored.
     const int8_t* pa[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pa[i] = a.A + (size_t)min(m0 + rbase + 16 * i, M - 1) * K;
-    // B: the packed blocks of this wave's four 16-row groups (groups past the
-    // last are clamped: they feed outputs never stored), lane l's 16 bytes at 16 l
     const int8_t* pb[4];
-    const int lastg = (N - 1) / kWGroup;
+    const int lastga = (M - 1) / kWGroup, lastgb = (N - 1) / kWGroup;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        pb[i] = a.B + wpack_block(min(n0 / kWGroup + wave * 4 + i, lastg), 0, nkt) + lane * 16;
-    // Load number `i` (0..7: A rows, then B rows) of K tile kt into `buf`.
-    auto issue_one = [&](uint8_t* buf, int kt, bool partial, int i) {
+    for (int i = 0; i < 4; ++i) {
+        pa[i] = a.A + wpack_block(min(m0 / kWGroup + wave * 4 + i, lastga), 0, nkt) + lane * 16;
+        pb[i] = a.B + wpack_block(min(n0 / kWGroup + wave * 4 + i, lastgb), 0, nkt) + lane * 16;
+    }
+    // Load number `i` (0..7: A groups, then B groups) of K tile kt into `buf`.
+    auto issue_one = [&](uint8_t* buf, int kt, int i) {
         uint8_t* la = buf + wave * 64 * BK;
-        const int gk = partial ? min(kt * BK + koff, K - 16) : kt * BK + koff;
         if (i < 4)
-            __builtin_amdgcn_global_load_lds(pa[i] + gk, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pa[i] + (size_t)kt * kWBlock, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(pb[i - 4] + (size_t)kt * kWBlock,
                                              (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK), 16, 0, 0);
@@ -197,13 +187,6 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     auto mfma = [&](const v4i (&fa)[4], const v4i (&fb)[4], int i, int j) {
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
-    // A past K (last tile only, when K % 64 != 0): zeroed fragments give zero
-    // products whatever B holds there.
-    auto mask_a = [&](v4i (&fa)[4], int s, int kvalid) {
-        if ((2 * s + (lane >> 5)) * 16 >= kvalid)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = v4i{};
-    };
     // K loop.  Each 64-byte K tile is two steps of 16 MFMAs on register set
     // f0 (step 0) and f1 (step 1).  Step 0 reads step 1's fragments and spreads
     // the 8 loads of tile kt+3 (into the buffer tile kt-1 used) over its MFMAs.
@@ -217,12 +200,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // (those re-load the last tile into a buffer nobody reads again), so the
     // number of loads in flight is the same on every path and each wait below
     // -- and each wait the compiler derives for the LDS reads -- is exact.
-    const int nfull = K / BK;
     v4i f0a[4], f0b[4], f1a[4], f1b[4];
-    auto issue_tile = [&](uint8_t* buf, int t, int i) {
-        const int te = min(t, nkt - 1);
-        issue_one(buf, te, te >= nfull, i);
-    };
+    auto issue_tile = [&](uint8_t* buf, int t, int i) { issue_one(buf, min(t, nkt - 1), i); };
     if (nkt > 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) issue_tile(st0, 0, i);
@@ -237,11 +216,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             const uint8_t* sb = stage(std::integral_constant<int, s0>{});
             const uint8_t* sn = stage(std::integral_constant<int, s0 + 1>{});
             uint8_t* sd = stage(std::integral_constant<int, s0 + kStages - 1>{});
-            const int kvalid = K - kt * BK;
             const int next = kt + kStages - 1;
             read_frags(sb, 1, f1a, f1b);
             __builtin_amdgcn_sched_barrier(0);
-            if (kvalid < BK) mask_a(f0a, 0, kvalid);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -250,7 +227,6 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     if (j & 1) issue_tile(sd, next, 2 * i + (j >> 1));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            if (kvalid < BK) mask_a(f1a, 1, kvalid);
             mfma(f1a, f1b, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             // Loads issued after tile kt+1's: tiles kt+2 and kt+3.  Also after

@@ -14,10 +14,20 @@ namespace {
 
 constexpr int64_t kMaxK = 65536;        // |sum_k (q_x - Z) q_w| < 255 * 127 * K stays in int32
 constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
-// Activation rows up to which a GEMM runs on the skinny (weight-streaming)
-// kernel of decode.hip rather than on the 256 x 256-tile GEMM, whichever
-// quantization scheme produced the codes.
-constexpr int64_t kSkinnyM = 64;
+// Which kernel runs an M x N INT8 GEMM, whichever quantization scheme
+// produced the codes: the skinny (weight-streaming) kernel of decode.hip or
+// the 256 x 256-tile GEMM.  The skinny kernel runs ceil(N / 16) x
+// ceil(M / 64) workgroups, each one pass over the K tiles of 16 weight
+// channels for up to 64 activation rows, and costs about 4 us plus 4.7 us per
+// 256 of them; the tiled GEMM costs about 52 us per round of 256 tiles, however
+// few tiles the round holds (both measured on MI355X at K = 4096; K scales
+// both alike).  Up to 64 rows the skinny kernel always runs.
+bool skinny_gemm(int64_t M, int64_t N) {
+    if (M <= 64) return true;
+    const double units = (double)((N + 15) / 16) * (double)((M + 63) / 64);
+    const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
+    return 4.0 + 4.7 * units / 256.0 < 52.0 * ceil(tiles / 256.0);
+}
 
 int elem_bytes(int dt) { return dt == PDQ_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == PDQ_F32 || dt == PDQ_BF16 || dt == PDQ_F16; }
@@ -74,6 +84,13 @@ size_t pdq_weight_bytes(int64_t N, int64_t K) {
     return (size_t)((N + kWGroup - 1) / kWGroup) * (size_t)((K + kWTileK - 1) / kWTileK) * kWBlock;
 }
 
+size_t pdq_act_bytes(int64_t M, int64_t K) { return pdq_weight_bytes(M, K); }
+
+int pdq_gemm_kernel(int64_t M, int64_t N) {
+    if (M < 1 || N < 1) return -1;
+    return skinny_gemm(M, N) ? PDQ_GEMM_SKINNY : PDQ_GEMM_TILED;
+}
+
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream) {
     if (!dtype_ok(w_dt)) return PDQ_ERR_DTYPE;
@@ -81,8 +98,7 @@ pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t
     if (N > 0 && ((K > 0 && !wq) || !w_scale)) return PDQ_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4)) return PDQ_ERR_ALIGN;
     if (N == 0) return PDQ_OK;
-    launch_quant_rows(w, w_dt, N, K, ldw, wq, w_scale, w_colsum, nullptr, true,
-                      static_cast<hipStream_t>(stream));
+    launch_quant_rows(w, w_dt, N, K, ldw, wq, w_scale, w_colsum, nullptr, static_cast<hipStream_t>(stream));
     return launched();
 }
 
@@ -106,8 +122,7 @@ pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int6
     if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
     if (!aligned(xq, 16) || !aligned(x_scale, 4)) return PDQ_ERR_ALIGN;
     if (M == 0) return PDQ_OK;
-    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr, false,
-                      static_cast<hipStream_t>(stream));
+    launch_quant_rows(x, x_dt, M, K, ldx, xq, x_scale, nullptr, nullptr, static_cast<hipStream_t>(stream));
     return launched();
 }
 
@@ -124,7 +139,7 @@ pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M,
         !aligned(acc_out, 4))
         return PDQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PDQ_OK;
-    if (M <= kSkinnyM) {
+    if (skinny_gemm(M, N)) {
         DecodeArgs d{};
         d.xq = xq;
         d.wq = wq;
@@ -204,7 +219,7 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
         !aligned(acc_out, 4))
         return PDQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PDQ_OK;
-    if (M > kSkinnyM) {
+    if (!skinny_gemm(M, N)) {
         GemmArgs g{};
         g.A = xq;
         g.B = wq;
@@ -339,7 +354,7 @@ pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64
                          (int)P, st);
     if (M > 0) {
         const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
-        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, false, st);
+        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
     }
     GemmArgs g{};
     g.A = xq;

@@ -29,15 +29,17 @@ struct Elem<kF16> {
     static constexpr int bytes = 2;
 };
 
-// Packed INT8 weight, the layout every GEMM of the library reads: groups of
-// 16 output channels x 64 K values, group g's K tile s a contiguous 1 KB
-// block at (g * ceil(K / 64) + s) * 1024; channel r of the group at r * 64
-// within it, its 16-byte chunk c (K values 16 c .. 16 c + 15 of the tile) at
-// position c ^ ((r >> 2) & 3).  One block is then exactly what one
-// global_load_lds instruction of the GEMM moves into its swizzled LDS tile
-// (every request a whole cache line), and a decode workgroup's 16 channels
-// are one contiguous run of ceil(K / 64) blocks.  Channels >= N (up to the
-// next multiple of 16) and K values >= K are stored as 0.
+// Packed INT8 operand, the layout of every INT8 matrix of the library (the
+// weight codes and the activation codes alike): groups of 16 rows x 64 K
+// values, group g's K tile s a contiguous 1 KB block at
+// (g * ceil(K / 64) + s) * 1024; row r of the group at r * 64 within it, its
+// 16-byte chunk c (K values 16 c .. 16 c + 15 of the tile) at position
+// c ^ ((r >> 2) & 3).  One block is then exactly what one global_load_lds
+// instruction of the GEMM moves into its swizzled LDS tile (every request a
+// whole cache line), and also one 16 x 64 fragment of the skinny kernel's
+// v_mfma_i32_16x16x64_i8, loaded by one contiguous instruction.  Rows past
+// the matrix (up to the next multiple of 16) and K values >= K are stored
+// as 0.
 constexpr int kWGroup = 16, kWTileK = 64, kWBlock = kWGroup * kWTileK;
 __device__ __forceinline__ int wpack_pos(int r, int c) { return r * kWTileK + ((c ^ ((r >> 2) & 3)) << 4); }
 __device__ __forceinline__ int64_t wpack_block(int64_t g, int64_t s, int64_t ktiles) {

@@ -21,16 +21,14 @@ struct OutlierSkip {
     uint16_t* xo;          // [rows, P] or null
     int P;
 };
-// Per-row absmax symmetric INT8: q[r,:] (dense, pitch K; or packed into the
-// weight tiles of pdq_device.h, padding zeroed, when `packed`), scale[r];
-// optional code sums; optional outlier columns to skip (16-bit inputs, dense
-// output only).
+// Per-row absmax symmetric INT8: q (packed tiles of pdq_device.h, padding
+// zeroed), scale[r]; optional code sums; optional outlier columns to skip
+// (16-bit inputs only).
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const OutlierSkip* skip, bool packed,
-                       hipStream_t st);
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st);
 
-// Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127); saturation
-// count added to *sat (nullable).
+// Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127), packed,
+// padding zeroed; saturation count added to *sat (nullable).
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
                          int8_t* q, uint32_t* sat, hipStream_t st);
 
@@ -41,8 +39,8 @@ void launch_minmax_finalize(const float* minmax, float* a_scale, int32_t* a_zp, 
 
 // gemm_i8.hip -------------------------------------------------------------
 struct GemmArgs {
-    const int8_t* A;  // [M, K] dense
-    const int8_t* B;  // packed weight (pdq_device.h)
+    const int8_t* A;  // packed activation codes (pdq_device.h)
+    const int8_t* B;  // packed weight
     int M, N, K;
     const float* sa;  // [M] row scales, or null: the per-tensor scale s
     float s;
@@ -67,8 +65,8 @@ void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, bo
 
 // decode.hip --------------------------------------------------------------
 struct DecodeArgs {
-    const int8_t* xq;  // [M, K] dense (launch_decode_gemv input)
-    const int8_t* wq;  // packed weight (pdq_device.h)
+    const int8_t* xq;  // packed activation codes (pdq_device.h; launch_decode_gemv input)
+    const int8_t* wq;  // packed weight
     int M, N, K;
     const float* sa;  // [M] per-token scales (launch_decode_gemv), or null: s, z
     float s;
@@ -83,7 +81,7 @@ struct DecodeArgs {
     const void* x;
     int x_dt;
     int64_t ldx;
-    int8_t* xq_out;  // [M, K] dense, written by workgroup 0
+    int8_t* xq_out;  // packed activation codes, written by workgroup 0 (padding rows by others)
     uint32_t* sat;   // nullable saturation counter
 };
 // Activations already quantized (xq).

@@ -9,10 +9,13 @@
 //                   on X_normal).  One wavefront per row: the row is read from
 //                   HBM once with 16-byte loads, kept in registers in its
 //                   storage format, reduced with cross-lane shuffles, then
-//                   quantized and written as packed INT8.
+//                   quantized and written as INT8 codes.
 //  * k_quant_static per-tensor static asymmetric INT8 of the decode phase
 //                   (PDMIX terminology entry, section 2.3 decode formula),
 //                   with the saturation count of section 2.4.
+//
+// Every code matrix is written in the packed tile layout of pdq_device.h,
+// the layout the GEMMs read, padding rows and K values as zeros.
 //  * k_minmax       the MinMax observer of the static calibration, and
 //    k_minmax_finalize its (S, Z) (PDMIX usage guide, section 3).
 //
@@ -126,7 +129,7 @@ __device__ __forceinline__ uint2 chunk_codes_absmax(const Raw8<DT>& r, uint32_t 
 // re-read its last chunk and zero it), so the compiler's waits count them
 // exactly.  CPL == 0: rows too long for registers are streamed twice (the
 // second pass hits the L2).
-template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM, bool PACKED>
+template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
                                                     float* __restrict__ scale,
@@ -134,27 +137,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                                                     OutlierSkip skip) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    // whole wavefronts leave together; PACKED: the rows of the last 16-row
-    // group past `rows` are padding, written as zeros
-    if (row >= (PACKED ? (rows + kWGroup - 1) / kWGroup * kWGroup : rows)) return;
+    // whole wavefronts leave together; the rows of the last 16-row group past
+    // `rows` are padding, written as zeros
+    if (row >= (rows + kWGroup - 1) / kWGroup * kWGroup) return;
     const char* xr = static_cast<const char*>(x) + row * ld_bytes;
-    uint2* qr = reinterpret_cast<uint2*>(q + row * (int64_t)nch * 8);
-    // codes of chunk c (8 values): dense row-major, or PACKED into the weight
-    // blocks (K tile c / 8, 16-byte chunk (c % 8) / 2, half c % 2)
+    // codes of chunk c (8 values) into the packed blocks: K tile c / 8,
+    // 16-byte chunk (c % 8) / 2, half c % 2
     const int ktiles = (nch + 7) / 8;
+    int8_t* const qg = q + wpack_block(row / kWGroup, 0, ktiles);
+    const int rg = (int)(row % kWGroup);
     auto store_code = [&](int c, uint2 code) {
-        if constexpr (PACKED) {
-            int8_t* blk = q + wpack_block(row / kWGroup, c >> 3, ktiles);
-            *reinterpret_cast<uint2*>(blk + wpack_pos((int)(row % kWGroup), (c & 7) >> 1) + ((c & 1) << 3)) = code;
-        } else {
-            qr[c] = code;
-        }
+        *reinterpret_cast<uint2*>(qg + (int64_t)(c >> 3) * kWBlock + wpack_pos(rg, (c & 7) >> 1) + ((c & 1) << 3)) =
+            code;
     };
-    if constexpr (PACKED) {
-        if (row >= rows) {
-            for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
-            return;
-        }
+    if (row >= rows) {
+        for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
+        return;
     }
     int csum = 0;
     float s;
@@ -234,9 +232,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         }
     }
     if (gather) gather_store();
-    if constexpr (PACKED) {  // K padding of the last K tile
-        for (int c = nch + lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
-    }
+    for (int c = nch + lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));  // K padding
     if (lane == 0) scale[row] = s;
     if constexpr (COLSUM) {
         csum = wave_sum(csum);
@@ -246,72 +242,86 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
 
 template <int DT, int CPL, bool FULL>
 void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, float* scale,
-                 int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
+                 int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     const OutlierSkip none{};
-    const int64_t rows_pad = packed ? (rows + kWGroup - 1) / kWGroup * kWGroup : rows;
+    const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
     const dim3 grid((unsigned)((rows_pad + kRowsPerBlock - 1) / kRowsPerBlock));
     if (skip)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false, false>), grid, dim3(256), 0, st, x,
-                           ldb, rows, nch, q, scale, colsum, *skip);
-    else if (packed && colsum)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true, true>), grid, dim3(256), 0, st, x,
-                           ldb, rows, nch, q, scale, colsum, none);
-    else if (packed)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, true>), grid, dim3(256), 0, st, x,
-                           ldb, rows, nch, q, scale, colsum, none);
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, *skip);
+    else if (colsum)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, none);
     else
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, false>), grid, dim3(256), 0, st, x,
-                           ldb, rows, nch, q, scale, colsum, none);
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false>), grid, dim3(256), 0, st, x, ldb,
+                           rows, nch, q, scale, colsum, none);
 }
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                    int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
+                    int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
     if (CPL > 0 && nch == 64 * CPL)
-        launch_rows<DT, CPL, true>(rows, x, ldb, nch, q, scale, colsum, skip, packed, st);
+        launch_rows<DT, CPL, true>(rows, x, ldb, nch, q, scale, colsum, skip, st);
     else
-        launch_rows<DT, CPL, false>(rows, x, ldb, nch, q, scale, colsum, skip, packed, st);
+        launch_rows<DT, CPL, false>(rows, x, ldb, nch, q, scale, colsum, skip, st);
 }
 
 template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                   int32_t* colsum, const OutlierSkip* skip, bool packed, hipStream_t st) {
+                   int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
     if (per_lane <= 1)
-        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else if (per_lane <= 2)
-        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else if (per_lane <= 4)
-        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else if (per_lane <= 8)
-        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else if (per_lane <= 16)
-        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else if (per_lane <= kMaxCpl)
-        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, st);
     else
-        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, packed, st);
+        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, st);
 }
 
 // ---------------------------------------------------------------------------
 
-template <int DT>
+// One thread per 8-value chunk of the padded code matrix (rows rounded up to
+// 16, K to 64): chunk (row, col) of the activations, or a zero of the padding.
+// WIDE: the chunk index needs 64 bits.
+template <int DT, bool WIDE>
 __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x, int64_t ld_bytes,
-                                                      int64_t total, int nch,
+                                                      int64_t rows, int nch, int cpr, int64_t total,
                                                       int8_t* __restrict__ q, float s, int z,
                                                       uint32_t* __restrict__ sat) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const float inv = 1.0f / s;
     int nsat = 0;
     if (c < total) {
-        const int64_t row = c / nch;
-        const int col = (int)(c - row * nch);
-        float v[8];
-        widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
-        reinterpret_cast<uint2*>(q)[c] = static_codes8(v, s, inv, z, nsat);
+        int64_t row;
+        int col;
+        if constexpr (WIDE) {
+            row = c / cpr;
+            col = (int)(c - row * cpr);
+        } else {
+            const uint32_t r32 = (uint32_t)c / (uint32_t)cpr;
+            row = r32;
+            col = (int)((uint32_t)c - r32 * (uint32_t)cpr);
+        }
+        uint2 code = make_uint2(0u, 0u);
+        if (row < rows && col < nch) {
+            float v[8];
+            widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
+            code = static_codes8(v, s, inv, z, nsat);
+        }
+        const int ktiles = cpr / 8;
+        *reinterpret_cast<uint2*>(q + wpack_block(row / kWGroup, col >> 3, ktiles) +
+                                  wpack_pos((int)(row % kWGroup), (col & 7) >> 1) + ((col & 1) << 3)) = code;
     }
     if (sat) {
         nsat = wave_sum(nsat);
@@ -375,35 +385,37 @@ __global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restric
 }  // namespace
 
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
-                       float* scale, int32_t* colsum, const OutlierSkip* skip, bool packed,
-                       hipStream_t st) {
+                       float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     if (rows <= 0) return;
     switch (dt) {
-        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
-        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
-        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, packed, st); break;
+        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
     }
+}
+
+template <int DT>
+void quant_static_dt(const void* x, int64_t M, int64_t ldb, int nch, int cpr, int64_t total, int8_t* q,
+                     float s, int z, uint32_t* sat, hipStream_t st) {
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (total <= 0xffffffffll)
+        hipLaunchKernelGGL((k_quant_static<DT, false>), grid, dim3(256), 0, st, x, ldb, M, nch, cpr, total,
+                           q, s, z, sat);
+    else
+        hipLaunchKernelGGL((k_quant_static<DT, true>), grid, dim3(256), 0, st, x, ldb, M, nch, cpr, total,
+                           q, s, z, sat);
 }
 
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
                          int8_t* q, uint32_t* sat, hipStream_t st) {
-    const int64_t total = M * (K / 8);
-    if (total <= 0) return;
-    const dim3 grid((unsigned)((total + 255) / 256));
+    if (M <= 0 || K <= 0) return;
     const int nch = (int)(K / 8);
+    const int cpr = (int)((K + kWTileK - 1) / kWTileK * 8);  // chunks per padded row
+    const int64_t total = (M + kWGroup - 1) / kWGroup * kWGroup * cpr;
     switch (dt) {
-        case kF32:
-            hipLaunchKernelGGL(k_quant_static<kF32>, grid, dim3(256), 0, st, x, ldx * 4, total, nch,
-                               q, s, z, sat);
-            break;
-        case kBF16:
-            hipLaunchKernelGGL(k_quant_static<kBF16>, grid, dim3(256), 0, st, x, ldx * 2, total,
-                               nch, q, s, z, sat);
-            break;
-        default:
-            hipLaunchKernelGGL(k_quant_static<kF16>, grid, dim3(256), 0, st, x, ldx * 2, total, nch,
-                               q, s, z, sat);
-            break;
+        case kF32: quant_static_dt<kF32>(x, M, ldx * 4, nch, cpr, total, q, s, z, sat, st); break;
+        case kBF16: quant_static_dt<kBF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, sat, st); break;
+        default: quant_static_dt<kF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, sat, st); break;
     }
 }
 

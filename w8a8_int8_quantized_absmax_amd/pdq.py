@@ -40,6 +40,8 @@ SIGNATURES = {
                                        _i64, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "pdq_weight_bytes": (_sz, [_i64, _i64]),
+    "pdq_act_bytes": (_sz, [_i64, _i64]),
+    "pdq_gemm_kernel": (ctypes.c_int, [_i64, _i64]),
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _i64, _vp, _sz, _vp, _vp]),
@@ -86,7 +88,9 @@ def _call(name: str, *args) -> None:
 
 
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    return ctypes.c_void_p((t.data if isinstance(t, Codes) else t).data_ptr())
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -114,21 +118,81 @@ def weight_bytes(n: int, k: int) -> int:
     return int(lib().pdq_weight_bytes(n, k))
 
 
-def unpack_weight(wq: torch.Tensor, n: int, k: int):
-    """The codes wq[n, k] of a packed weight as a host int8 array [N, K].
+def act_bytes(m: int, k: int) -> int:
+    """Bytes of the packed INT8 activation codes of M rows x K (include/pdq.h)."""
+    return int(lib().pdq_act_bytes(m, k))
 
-    Layout (include/pdq.h): 1024-byte blocks of 16 channels x 64 K values,
-    block (g, s) at (g * ceil(K / 64) + s) * 1024, channel r at r * 64 in it,
-    its 16-byte chunk c at position c ^ ((r >> 2) & 3).
+
+def unpack(buf: torch.Tensor, rows: int, k: int, padded: bool = False):
+    """The codes [rows, k] of a packed INT8 matrix (weight or activations) as a host int8 array.
+
+    Layout (include/pdq.h): 1024-byte blocks of 16 rows x 64 K values, block
+    (g, s) at (g * ceil(K / 64) + s) * 1024, row r at r * 64 in it, its
+    16-byte chunk c at position c ^ ((r >> 2) & 3).  padded: the whole
+    [16 ceil(rows / 16), 64 ceil(k / 64)] matrix, padding included.
     """
     import numpy as np
 
-    ng, kt = (n + 15) // 16, (k + 63) // 64
-    b = wq.detach().cpu().numpy()[:ng * kt * 1024].reshape(ng, kt, 16, 4, 16)
+    ng, kt = (rows + 15) // 16, (k + 63) // 64
+    b = buf.detach().cpu().numpy()[:ng * kt * 1024].reshape(ng, kt, 16, 4, 16)
     r = np.arange(16)[:, None]
     pos = np.arange(4)[None, :] ^ ((r >> 2) & 3)  # [r, c] -> position of chunk c
     out = b[:, :, r, pos, :]                      # [ng, kt, 16, 4, 16], chunks in K order
-    return out.transpose(0, 2, 1, 3, 4).reshape(ng * 16, kt * 64)[:n, :k]
+    out = out.transpose(0, 2, 1, 3, 4).reshape(ng * 16, kt * 64)
+    return out if padded else out[:rows, :k]
+
+
+unpack_weight = unpack
+
+
+def gemm_kernel(m: int, n: int) -> str:
+    """The GEMM kernel the library runs for M activation rows x N channels: "skinny" or "tiled"."""
+    return {0: "skinny", 1: "tiled"}.get(int(lib().pdq_gemm_kernel(m, n)), "none")
+
+
+class Codes:
+    """INT8 activation codes of a [rows, k] matrix in the packed layout (include/pdq.h).
+
+    data: contiguous int8 device tensor of at least act_bytes(rows, k) bytes.
+    """
+
+    __slots__ = ("data", "rows", "k")
+
+    def __init__(self, data: torch.Tensor, rows: int, k: int):
+        if not data.is_cuda or data.dtype != torch.int8 or not data.is_contiguous():
+            raise ValueError("packed codes must be a contiguous int8 device tensor")
+        if data.numel() < act_bytes(rows, k):
+            raise ValueError(f"{data.numel()} bytes cannot hold packed {rows} x {k} codes "
+                             f"({act_bytes(rows, k)} needed)")
+        self.data, self.rows, self.k = data, int(rows), int(k)
+
+    @classmethod
+    def empty(cls, rows: int, k: int, device) -> "Codes":
+        return cls(torch.empty(max(act_bytes(rows, k), 1), dtype=torch.int8, device=device), rows, k)
+
+    @property
+    def shape(self):
+        return (self.rows, self.k)
+
+    def unpack(self, padded: bool = False):
+        """Host int8 array [rows, k] (padded: with the zero padding rows and K values)."""
+        return unpack(self.data, self.rows, self.k, padded)
+
+
+def _codes_out(xq, m: int, k: int, device) -> Codes:
+    if xq is None:
+        return Codes.empty(m, k, device)
+    if isinstance(xq, Codes):
+        if xq.shape != (m, k):
+            raise ValueError(f"codes of shape {xq.shape} given for a {m} x {k} activation")
+        return xq
+    return Codes(xq, m, k)
+
+
+def _codes_in(xq) -> Codes:
+    if not isinstance(xq, Codes):
+        raise ValueError("xq must be packed activation codes (a Codes object)")
+    return xq
 
 
 def _check_weight(wq: torch.Tensor, n: int, k: int):
@@ -174,7 +238,7 @@ def linear_prefill(x, wq, w_scale, bias=None, want_acc: bool = False, out=None):
     m, k = x.shape
     n = w_scale.shape[0]
     _check_weight(wq, n, k)
-    xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    xq = Codes.empty(m, k, x.device)
     xs = torch.empty(m, dtype=torch.float32, device=x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
@@ -190,7 +254,7 @@ def linear_decode(x, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None,
     m, k = x.shape
     n = w_scale.shape[0]
     _check_weight(wq, n, k)
-    xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    xq = _codes_out(xq, m, k, x.device)
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
     _call("pdq_linear_decode", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp),
@@ -213,7 +277,7 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
     _check_weight(wq, n, k)
     dev = x.device
     max_outliers = min(max_outliers, k)
-    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    xq = Codes.empty(m, k, dev)
     xs = torch.empty(m, dtype=torch.float32, device=dev)
     idx = torch.empty(max(max_outliers, 1), dtype=torch.int32, device=dev)
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
@@ -229,10 +293,10 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
 
 
 def quantize_per_token(x, xq=None, x_scale=None):
-    """Per-token dynamic symmetric INT8 -> (xq int8 [M,K], x_scale f32 [M])."""
+    """Per-token dynamic symmetric INT8 -> (xq packed Codes [M,K], x_scale f32 [M])."""
     _check_mat(x, "x")
     m, k = x.shape
-    xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    xq = _codes_out(xq, m, k, x.device)
     xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=x.device)
     _call("pdq_quantize_per_token", _p(x), _DT[x.dtype], m, k, _ld(x), _p(xq), _p(xs), _stream(x.device))
     return xq, xs
@@ -240,22 +304,23 @@ def quantize_per_token(x, xq=None, x_scale=None):
 
 def gemm_per_token(xq, x_scale, wq, w_scale, bias=None, want_acc: bool = False, out=None):
     """INT8 GEMM + per-token/per-channel dequant epilogue -> dict(y bf16[, acc])."""
-    _check_mat(xq, "xq", (torch.int8,))
+    xq = _codes_in(xq)
     m, k = xq.shape
     n = w_scale.shape[0]
     _check_weight(wq, n, k)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
-    acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    dev = xq.data.device
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
     _call("pdq_gemm_per_token", _p(xq), _p(x_scale), m, k, _p(wq), _p(w_scale), _p(bias), n, _p(y),
-          _ld(y), _p(acc), _stream(xq.device))
+          _ld(y), _p(acc), _stream(dev))
     return dict(y=y, acc=acc)
 
 
 def quantize_static(x, a_scale: float, a_zp: int, xq=None, sat_count=None):
-    """Per-tensor static asymmetric INT8 -> xq int8 [M,K]."""
+    """Per-tensor static asymmetric INT8 -> xq packed Codes [M,K]."""
     _check_mat(x, "x")
     m, k = x.shape
-    xq = xq if xq is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    xq = _codes_out(xq, m, k, x.device)
     _call("pdq_quantize_static", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp), _p(xq),
           _p(sat_count), _stream(x.device))
     return xq
@@ -263,13 +328,14 @@ def quantize_static(x, a_scale: float, a_zp: int, xq=None, sat_count=None):
 
 def gemm_static(xq, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None, want_acc: bool = False,
                 out=None):
-    """Skinny INT8 GEMM + zero-point correction + dequant epilogue -> dict(y bf16[, acc])."""
-    _check_mat(xq, "xq", (torch.int8,))
+    """INT8 GEMM + zero-point correction + dequant epilogue -> dict(y bf16[, acc])."""
+    xq = _codes_in(xq)
     m, k = xq.shape
     n = w_scale.shape[0]
     _check_weight(wq, n, k)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
-    acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    dev = xq.data.device
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
     _call("pdq_gemm_static", _p(xq), m, k, float(a_scale), int(a_zp), _p(wq), _p(w_scale), _p(colsum),
-          _p(bias), n, _p(y), _ld(y), _p(acc), _stream(xq.device))
+          _p(bias), n, _p(y), _ld(y), _p(acc), _stream(dev))
     return dict(y=y, acc=acc)
