@@ -174,6 +174,35 @@ def quantize_static(x, s, z):
 
 
 # ---------------------------------------------------------------------------
+# Per-token dynamic asymmetric quantization (prefill with Z_token)
+# ---------------------------------------------------------------------------
+
+def quantize_rows_asym(x):
+    """Per-token dynamic asymmetric INT8: (q int8 [R,K], S float32 [R], Z int32 [R]).
+
+    [PDMIX-term] 2.3, the prefill formula with its per-token zero point:
+    Q = clamp(round(X / S_token) + Z_token, -128, 127), where S_token and
+    Z_token are computed online from each token's own values.  A token's
+    (S, Z) are those of the MinMax asymmetric grid of its range -- the
+    decode phase's per-tensor parameters (minmax_finalize), one token at a
+    time -- and its codes follow the decode formula with them
+    (quantize_static).  The range of a token always covers its values, so
+    nothing saturates.
+    """
+    x = _f32(x)
+    rows = x.shape[0]
+    q = np.zeros(x.shape, np.int8)
+    s = np.ones(rows, F32)
+    z = np.zeros(rows, np.int32)
+    for r in range(rows):
+        if x.shape[1] == 0:
+            continue
+        s[r], z[r] = minmax_finalize(minmax_update(None, x[r]))
+        q[r], _ = quantize_static(x[r:r + 1], s[r], z[r])
+    return q, s, z
+
+
+# ---------------------------------------------------------------------------
 # INT8 x INT8 -> INT32 contraction and the dequantizing epilogue
 # ---------------------------------------------------------------------------
 
@@ -199,11 +228,17 @@ def zero_point_correct(acc, colsum, z):
 
     [LLM.int8] part 1 section 2 expands a zero-point product into four terms.
     With a symmetric weight (zp_b = 0) the expansion reduces to
-    sum_k (q_a - Z) q_b = sum_k q_a q_b - Z * sum_k q_b.
+    sum_k (q_a - Z) q_b = sum_k q_a q_b - Z * sum_k q_b.  Z is one per-tensor
+    value, or one value per row of acc (per-token zero points).
     """
     acc = np.asarray(acc, dtype=np.int64)
-    if z:
-        acc = acc - np.int64(z) * np.asarray(colsum, dtype=np.int64)[None, :]
+    colsum = np.asarray(colsum, dtype=np.int64)[None, :]
+    z = np.asarray(z, dtype=np.int64)
+    if z.ndim == 0:
+        if z:
+            acc = acc - z * colsum
+    else:
+        acc = acc - z.reshape(-1)[:, None] * colsum
     assert np.all(np.abs(acc) < 2**31), "accumulator leaves int32"
     return acc
 
@@ -240,6 +275,18 @@ def linear_prefill(x, wq, sw, bias=None):
     acc = int_matmul(xq, wq)
     assert np.all(np.abs(acc) < 2**31)
     return dict(xq=xq, x_scale=sx, acc=acc, y32=dequantize(acc, sx, sw, bias))
+
+
+def linear_prefill_asym(x, wq, sw, colsum, bias=None):
+    """Prefill with per-token dynamic asymmetric activations ([PDMIX-term] 2.3,
+    the prefill formula with Z_token): y = S_x[m] S_w[n] (acc - Z_x[m] colsum[n]).
+
+    Returns dict(xq, x_scale, x_zp, acc (raw, before the zero-point term), y32).
+    """
+    xq, sx, zx = quantize_rows_asym(x)
+    acc = int_matmul(xq, wq)
+    acc_c = zero_point_correct(acc, colsum, zx)
+    return dict(xq=xq, x_scale=sx, x_zp=zx, acc=acc, y32=dequantize(acc_c, sx, sw, bias))
 
 
 def linear_decode(x, s, z, wq, sw, colsum, bias=None):

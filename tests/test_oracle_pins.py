@@ -301,6 +301,88 @@ def test_calibration_resume_is_exact():
 
 
 # ---------------------------------------------------------------------------
+# Per-token dynamic asymmetric quantization (the prefill formula with Z_token)
+# ---------------------------------------------------------------------------
+
+def check_asym_rows(oracle=O):
+    """Closed forms of the per-token asymmetric grid, derived by hand: 255 steps
+    over the row's range widened to contain 0, the range's low end on -128."""
+    x = np.array([[-1, 0, 1, 2],            # width 3: S = 3/255; -1 -> -128 => Z = -128 + 85
+                  [0, 0.25, 1, 1],          # low end 0 => Z = -128; 0.25 * 255 = 63.75 -> 64
+                  [0, 0, 0, 0],             # empty range: S = 1, Z = 0
+                  [3, 3, 3, 3],             # widened to [0, 3]: Z = -128, all at the top
+                  [-2, -0.8, -1.2, -0.1]],  # widened to [-2, 0]: Z = -128 + 255
+                 F32)
+    q, s, z = oracle.quantize_rows_asym(x)
+    assert z.tolist() == [-43, -128, 0, -128, 127]
+    assert q.tolist() == [[-128, -43, 42, 127], [-128, -64, 127, 127], [0, 0, 0, 0],
+                          [127, 127, 127, 127], [-128, 25, -26, 114]]
+    for width, sr in zip([3, 1, None, 3, 2], s):
+        if width is None:
+            assert sr == 1
+        else:
+            assert abs(float(sr) * 255 - width) <= width * 2.0**-23
+
+
+def test_per_token_asym_closed_forms():
+    check_asym_rows()
+
+
+def test_per_token_asym_error_bound_and_range():
+    """Every value of a token lies inside its grid: |S (q - Z) - x| <= S / 2, and the
+    token's minimum lands on -128 (its maximum on 127 when positive)."""
+    x = synth.activations(45, 48, 320, [3, 100], 100.0, offset=0.3, dtype="f32")
+    x[5] = np.abs(x[5])   # all non-negative
+    x[6] = -np.abs(x[6])  # all non-positive
+    q, s, z = O.quantize_rows_asym(x)
+    s64 = s.astype(np.float64)[:, None]
+    err = np.abs(s64 * (q.astype(np.int64) - z[:, None]) - x.astype(np.float64))
+    assert np.all(err <= s64 / 2 * (1 + 2.0**-18))
+    r = np.arange(x.shape[0])
+    assert np.all(q[r, np.argmin(x, axis=1)] == -128)
+    pos = np.max(x, axis=1) > 0
+    assert np.all(q[r, np.argmax(x, axis=1)][pos] == 127)
+
+
+def test_per_token_asym_one_token_is_the_per_tensor_grid():
+    """One token's per-token parameters are the per-tensor ones of a calibration on
+    that token alone, and its codes the decode formula's (itself pinned above)."""
+    x = synth.activations(46, 7, 256, [9], 50.0, offset=0.1, dtype="f32")
+    q, s, z = O.quantize_rows_asym(x)
+    for r in range(x.shape[0]):
+        _, s1, z1 = O.calibrate([x[r:r + 1]])
+        q1, sat = O.quantize_static(x[r:r + 1], s1, z1)
+        assert (s[r], z[r], sat) == (s1, z1, 0)
+        assert np.array_equal(q[r], q1[0])
+
+
+def check_prefill_asym(oracle=O):
+    """The zero-point epilogue equals the binary64 product of the dequantized
+    operands S_x (q - Z) and S_w q_w ([PDMIX-term] 2.3 dequantization per
+    operand; [LLM.int8] part 1 section 2 expansion), up to the epilogue's own
+    binary32 roundings."""
+    x = synth.activations(47, 24, 192, [5, 77], 100.0, offset=0.2, dtype="f32")
+    w = synth.weights(48, 40, 192, "f32")
+    b = synth.bias(49, 40)
+    wq, sw, colsum = oracle.quantize_weight(w)
+    q, sx, zx = oracle.quantize_rows_asym(x)
+    acc = oracle.zero_point_correct(oracle.int_matmul(q, wq), colsum, zx)
+    y32 = oracle.dequantize(acc, sx, sw, b)
+    xd = sx.astype(np.float64)[:, None] * (q.astype(np.float64) - zx[:, None])
+    wd = sw.astype(np.float64)[:, None] * wq.astype(np.float64)
+    y64 = xd @ wd.T + b
+    scale = np.abs(xd) @ np.abs(wd).T + np.abs(b)
+    assert np.all(np.abs(y32 - y64) <= 4 * 2.0**-24 * scale)
+
+
+def test_prefill_asym_epilogue_is_the_dequantized_product():
+    check_prefill_asym()
+    res = O.linear_prefill_asym(*[synth.activations(50, 3, 64, [], dtype="f32")] +
+                                list(O.quantize_weight(synth.weights(51, 5, 64, "f32"))))
+    assert set(res) == {"xq", "x_scale", "x_zp", "acc", "y32"}
+
+
+# ---------------------------------------------------------------------------
 # Brute force of whole layers on tiny shapes
 # ---------------------------------------------------------------------------
 
@@ -413,6 +495,39 @@ def _plus_zero_point(acc, colsum, z):
     return np.asarray(acc, np.int64) + np.int64(z) * np.asarray(colsum, np.int64)[None, :]
 
 
+def _plus_zero_point_rows(acc, colsum, z):
+    z = np.asarray(z, np.int64)
+    if z.ndim == 0:
+        return O.zero_point_correct(acc, colsum, z)
+    return np.asarray(acc, np.int64) + z[:, None] * np.asarray(colsum, np.int64)[None, :]
+
+
+def _asym_rows_unwidened(x):
+    """Range not widened to contain 0."""
+    x = np.asarray(x, F32)
+    q = np.zeros(x.shape, np.int8)
+    s = np.ones(x.shape[0], F32)
+    z = np.zeros(x.shape[0], np.int32)
+    for r in range(x.shape[0]):
+        lo, hi = F32(x[r].min()), F32(x[r].max())
+        if hi > lo:
+            s[r] = F32(F32(hi - lo) / F32(255))
+            z[r] = min(max(-128 - int(np.rint(F32(lo / s[r]))), -128), 127)
+        q[r], _ = O.quantize_static(x[r:r + 1], s[r], z[r])
+    return q, s, z
+
+
+def _asym_rows_zero_point_sign(x):
+    """Z = -128 + rne(lo / S) instead of -128 - rne(lo / S)."""
+    q, s, z = O.quantize_rows_asym(x)
+    x = np.asarray(x, F32)
+    for r in range(x.shape[0]):
+        lo = min(F32(x[r].min()), F32(0))
+        z[r] = min(max(-128 + int(np.rint(F32(lo / s[r]))), -128), 127)
+        q[r], _ = O.quantize_static(x[r:r + 1], s[r], z[r])
+    return q, s, z
+
+
 def _nonstrict_outliers(x, thr):
     return np.nonzero(np.max(np.abs(np.asarray(x, F32)), axis=0) >= F32(thr))[0]
 
@@ -430,6 +545,9 @@ def _rowwise_over_all_columns(x, cols):
     (_Mutant(zero_point_correct=_plus_zero_point), check_four_term),
     (_Mutant(quantize_rows_regular=_rowwise_over_all_columns), check_outlier_example),
     (_Mutant(outlier_columns=_nonstrict_outliers), check_threshold_strict),
+    (_Mutant(zero_point_correct=_plus_zero_point_rows), check_prefill_asym),
+    (_Mutant(quantize_rows_asym=_asym_rows_unwidened), check_asym_rows),
+    (_Mutant(quantize_rows_asym=_asym_rows_zero_point_sign), check_asym_rows),
 ])
 def test_planted_mistake_is_caught(mutant, check):
     with pytest.raises(AssertionError):
