@@ -8,8 +8,10 @@ prefill linear (quantize + GEMM + epilogue) and `value` is 2*M*N*K / step
 time in TOPS.  `roofline` is the INT8 GEMM kernel alone, timed with HIP
 events on the stream it is launched on, against the chip's dense INT8 peak.
 
-Also measured in the same run and reported under "decode" and "llm_int8":
-the static per-tensor decode linear 4096 -> 4096 at M in {1, 8, 32, 64}
+Also measured in the same run and reported under "prefill_asym", "decode" and
+"llm_int8": the same prefill linear with per-token asymmetric activations
+(the prefill formula with its per-token zero point), the static per-tensor
+decode linear 4096 -> 4096 at M in {1, 8, 32, 64}
 (HBM GB/s of the skinny GEMM against 8 TB/s, weights rotated over >= 1 GiB of
 copies so that no cache serves them), and the LLM.int8() decomposition
 2048 x (8192 -> 28672) in fp16 with threshold 6.0.
@@ -114,7 +116,7 @@ def bench_prefill(args, torch, pdq, synth):
     log(f"[prefill] generating X[{M},{K}] and W[{N},{K}] ({c.dtype})")
     x_host, w_host = c.x(), c.w()
     x = torch.from_numpy(x_host).to(torch.bfloat16).cuda()
-    wq0, ws, _ = pdq.quantize_weight(torch.from_numpy(w_host).to(torch.bfloat16).cuda())
+    wq0, ws, cs = pdq.quantize_weight(torch.from_numpy(w_host).to(torch.bfloat16).cuda())
     nrot = 8  # 8 x 45 MB of INT8 weights + 8 x 34 MB of activations: more than the 256 MB MALL
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
     xs = [x] + [x.clone() for _ in range(nrot - 1)]
@@ -148,12 +150,40 @@ def bench_prefill(args, torch, pdq, synth):
                   pdq._p(xsc), pdq._stream(x.device))
 
     ms_quant = timed(quant, args.steps, args.warmup, stream)
+
+    # the per-token asymmetric variant (prefill formula with Z_token): the
+    # composite call, its quantizer and its GEMM, on the same operands
+    xz = torch.empty(M, dtype=torch.int32, device="cuda")
+
+    def step_asym(i):
+        r = i % nrot
+        pdq._call("pdq_linear_prefill_asym", pdq._p(xs[r]), pdq.BF16, M, K, K, pdq._p(wqs[r]), pdq._p(ws),
+                  pdq._p(cs), None, N, pdq._p(xqs[r]), pdq._p(xsc), pdq._p(xz), pdq._p(y), N, None,
+                  pdq._stream(x.device))
+
+    def quant_asym(i):
+        r = i % nrot
+        pdq._call("pdq_quantize_per_token_asym", pdq._p(xs[r]), pdq.BF16, M, K, K, pdq._p(xqs[r]),
+                  pdq._p(xsc), pdq._p(xz), pdq._stream(x.device))
+
+    def gemm_asym(i):
+        r = i % nrot
+        pdq._call("pdq_gemm_per_token_asym", pdq._p(xqs[r]), pdq._p(xsc), pdq._p(xz), M, K, pdq._p(wqs[r]),
+                  pdq._p(ws), pdq._p(cs), None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+    asym_steps = max(args.steps // 2, 10)
+    ms_step_asym = timed(step_asym, asym_steps, args.warmup // 2, stream)
+    ms_quant_asym = timed(quant_asym, asym_steps, args.warmup // 2, stream)
+    for r in range(nrot):  # codes, scales and zero points of every activation copy
+        quant_asym(r)
+    ms_gemm_asym = timed(gemm_asym, asym_steps, args.warmup // 2, stream)
     ops = 2.0 * M * N * K
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     gemm_bytes = M * K + N * K + 4 * (M + N) + 2 * M * N  # xq, wq, scales, bf16 y
     quant_bytes = 2 * M * K + M * K + 4 * M
     del wqs, xs, xqs
     return dict(M=M, K=K, N=N, ms_step=ms_step, ms_gemm=ms_gemm, ms_quant=ms_quant, ops=ops,
+                ms_step_asym=ms_step_asym, ms_quant_asym=ms_quant_asym, ms_gemm_asym=ms_gemm_asym,
                 gemm_tops=gemm_tops, gemm_bytes=gemm_bytes, quant_bytes=quant_bytes,
                 x_host=x_host, w_host=w_host)
 
@@ -384,6 +414,8 @@ def main():
     pre = bench_prefill(args, torch, pdq, synth)
     log(f"[prefill] step {pre['ms_step']*1e3:.1f} us (quant {pre['ms_quant']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm']*1e3:.1f} us = {pre['gemm_tops']:.0f} TOPS)")
+    log(f"[prefill asym] step {pre['ms_step_asym']*1e3:.1f} us (quant {pre['ms_quant_asym']*1e3:.1f} us, "
+        f"GEMM {pre['ms_gemm_asym']*1e3:.1f} us)")
     dec = llm = None
     if args.only == "all":
         dec = bench_decode(args, torch, pdq, synth)
@@ -419,6 +451,11 @@ def main():
                      "us_per_launch": round(pre["ms_gemm"] * 1e3, 2)},
         "prefill_quant": {"us": round(pre["ms_quant"] * 1e3, 2),
                           "GBps": round(pre["quant_bytes"] / (pre["ms_quant"] * 1e-3) / 1e9, 1)},
+        "prefill_asym": {"us_step": round(pre["ms_step_asym"] * 1e3, 2),
+                         "us_quant": round(pre["ms_quant_asym"] * 1e3, 2),
+                         "us_gemm": round(pre["ms_gemm_asym"] * 1e3, 2),
+                         "gemm_TOPS": round(pre["ops"] / (pre["ms_gemm_asym"] * 1e-3) / 1e12, 1),
+                         "frac": round(pre["ops"] / (pre["ms_gemm_asym"] * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
     }
     if dec:
         out["decode"] = {"unit": "GB/s", "peak": PEAK_HBM_GBS, "S": dec["S"], "Z": dec["Z"],

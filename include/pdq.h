@@ -106,8 +106,8 @@ size_t pdq_weight_bytes(int64_t N, int64_t K);
 size_t pdq_act_bytes(int64_t M, int64_t K);
 
 /*
- * The INT8 GEMM kernel that pdq_gemm_per_token, pdq_gemm_static,
- * pdq_linear_prefill and pdq_linear_decode run for M activation rows and N
+ * The INT8 GEMM kernel that pdq_gemm_per_token, pdq_gemm_per_token_asym,
+ * pdq_gemm_static and the linear entry points run for M activation rows and N
  * weight channels (pdq_linear_decode runs neither when it fuses the
  * quantizer into the skinny kernel; pdq_linear_int8_outlier always runs the
  * tiled one).  Both give the same bits.  -1 when M < 1 or N < 1.
@@ -194,6 +194,32 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
                              void* stream);
 
 /*
+ * Prefill linear with per-token dynamic ASYMMETRIC activations: the
+ * [PDMIX-term] 2.3 prefill formula taken with its per-token zero point
+ * Z_token, Q = clamp(round(X / S_token) + Z_token, -128, 127), both computed
+ * online per token.  A token's (S, Z) are the MinMax asymmetric grid of its
+ * own range (as pdq_calibrate_static finalises a per-tensor range, one token
+ * at a time): lo = min(min_k x[m,k], 0), hi = max(max_k x[m,k], 0);
+ * S_x[m] = (hi - lo) / 255 (1 if hi == lo); Z_x[m] = clamp(-128 - rne(lo /
+ * S_x[m]), -128, 127); xq = clamp(rne(x / S_x[m]) + Z_x[m], -128, 127).  The
+ * GEMM removes the zero point through the weight code sums ([LLM.int8] part 1
+ * section 2 with a symmetric weight):
+ *   y = bf16((S_x[m] * S_w[n]) * (float)(acc - Z_x[m] * colsum[n]) [+ bias[n]]).
+ * (The default PDMIX prefill, pdq_linear_prefill, is per-token symmetric.)
+ *
+ *   x, wq, w_scale, bias, y, ldy   as in pdq_linear_prefill
+ *   w_colsum  [N] int32 from pdq_quantize_weight (required)
+ *   xq        packed int8 codes out (pdq_act_bytes(M, K) bytes)
+ *   x_scale   [M] float out; x_zp [M] int32 out
+ *   acc_out   [M, N] int32 out or NULL: raw acc = sum_k xq wq (before the
+ *             zero-point term)
+ */
+pdq_status pdq_linear_prefill_asym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                                   const float* bias, int64_t N, int8_t* xq, float* x_scale, int32_t* x_zp,
+                                   uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream);
+
+/*
  * Building blocks of the two PDMIX phases.  pdq_linear_prefill is
  * pdq_quantize_per_token followed by pdq_gemm_per_token; pdq_linear_decode is
  * pdq_quantize_static followed by pdq_gemm_static.  They are exposed for
@@ -210,6 +236,16 @@ pdq_status pdq_quantize_per_token(const void* x, pdq_dtype x_dt, int64_t M, int6
 pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M, int64_t K,
                               const int8_t* wq, const float* w_scale, const float* bias, int64_t N,
                               uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream);
+
+/* The two halves of pdq_linear_prefill_asym: the per-token asymmetric quantizer (x_scale,
+ * x_zp [M] out) and the GEMM with the per-token zero-point epilogue. */
+pdq_status pdq_quantize_per_token_asym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                       int8_t* xq, float* x_scale, int32_t* x_zp, void* stream);
+
+pdq_status pdq_gemm_per_token_asym(const int8_t* xq, const float* x_scale, const int32_t* x_zp, int64_t M,
+                                   int64_t K, const int8_t* wq, const float* w_scale,
+                                   const int32_t* w_colsum, const float* bias, int64_t N, uint16_t* y,
+                                   int64_t ldy, int32_t* acc_out, void* stream);
 
 /* Static quantizer: xq = clamp(rne(x / S) + Z, -128, 127); sat_count (nullable) incremented. */
 pdq_status pdq_quantize_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,

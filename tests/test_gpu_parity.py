@@ -114,6 +114,60 @@ def test_per_token_skinny(m, n, k):
     prefill_case(x, synth.weights(2700 + n, n, k, "bf16"), "bf16", bias=synth.bias(2800 + n, n))
 
 
+# ---------------------------------------------------------------------------
+# prefill, per-token dynamic asymmetric (the prefill formula with Z_token)
+# ---------------------------------------------------------------------------
+
+def prefill_asym_case(x, w, dtype, bias=None, rows=None):
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, dtype)
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    res = pdq.linear_prefill_asym(dev(x, dtype), wq, ws, cs, b, want_acc=True)
+    q_ref, s_ref, z_ref = O.quantize_rows_asym(x)
+    assert codes_equal(res["xq"], q_ref)
+    assert np.array_equal(host(res["x_scale"]).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(res["x_zp"]), z_ref)
+    r = np.arange(x.shape[0]) if rows is None else rows
+    acc_ref = O.int_matmul(q_ref[r], rq)
+    assert np.array_equal(host(res["acc"])[r], acc_ref)
+    y_ref = O.dequantize(O.zero_point_correct(acc_ref, rc, z_ref[r]), s_ref[r], rs, bias)
+    check_16bit(host(res["y"])[r], y_ref, "bf16", exact=True)
+    return res
+
+
+# Both GEMM kernels: (1100, 2600) runs on the tiled one, the others on the skinny one.
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (37, 520, 2048), (300, 700, 1040), (257, 1, 16),
+                                   (1100, 2600, 1040)])
+def test_prefill_asym_ragged(dtype, m, n, k):
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+    x = synth.activations(7000 + m, m, k, [0, k - 1, k // 3], 100.0, offset=0.3, dtype=dtype)
+    if m > 5:
+        x[2, :] = 0.0                # empty range: S = 1, Z = 0
+        x[3, :] = np.abs(x[3, :])    # non-negative token: Z = -128
+        x[4, :] = -np.abs(x[4, :])   # non-positive token: Z = 127
+        x[5, :] = 1.5                # one value: range [0, 1.5]
+    prefill_asym_case(x, synth.weights(7100 + n, n, k, dtype), dtype, bias=synth.bias(7200 + n, n))
+
+
+def test_prefill_asym_7b_full_sampled():
+    c = synth.Prefill7B()
+    prefill_asym_case(c.x(), c.w(), c.dtype, rows=sample_rows(c.M, 48, 7))
+
+
+@pytest.mark.parametrize("m,n,k", [(20, 300, 512), (800, 3000, 512)])
+def test_prefill_asym_building_blocks(m, n, k):
+    """Quantizer + GEMM entry points give the composite call's bits."""
+    x = synth.activations(7300 + m, m, k, [5], 100.0, offset=-0.2, dtype="bf16")
+    w = synth.weights(7301, n, k, "bf16")
+    wq, ws, cs = pdq.quantize_weight(dev(w, "bf16"))
+    xd = dev(x, "bf16")
+    one = pdq.linear_prefill_asym(xd, wq, ws, cs, want_acc=True)
+    xq, xs, xz = pdq.quantize_per_token_asym(xd)
+    two = pdq.gemm_per_token_asym(xq, xs, xz, wq, ws, cs, want_acc=True)
+    assert torch.equal(one["xq"].data, xq.data) and torch.equal(one["x_zp"], xz)
+    assert torch.equal(one["y"], two["y"]) and torch.equal(one["acc"], two["acc"])
+
+
 def test_prefill_empty_batch():
     w = synth.weights(7, 64, 64, "bf16")
     wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))

@@ -5,8 +5,8 @@
 // i.e. the PDMIX terminology entry's decode formula (section 2.3, static
 // per-tensor S and Z) pushed through the zero-point expansion of the LLM.int8()
 // notes (part 1 section 2) with a symmetric weight; or, with per-token scales
-// (the same entry's prefill formula at decode sizes, for the per-token GEMM
-// entry point at small M), y = (S_x[m] * S_w[n]) * (float)acc [+ bias[n]].
+// (the same entry's prefill formula, for the per-token GEMM entry points),
+// y = (S_x[m] * S_w[n]) * (float)(acc [- Z_x[m] * colsum[n]]) [+ bias[n]].
 //
 // The weight matrix is read exactly once and is the whole cost (the
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
@@ -95,8 +95,9 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
         if (n < a.N) {
             const int raw = tot[r];
             if (a.acc_out) a.acc_out[(size_t)m * a.N + n] = raw;
-            // per-token: (S_x[m] * S_w[n]) * acc; static: (S * S_w[n]) * (acc - Z colsum[n])
-            const int corr = a.sa ? raw : raw - a.z * e.cs[r];
+            // per-token: (S_x[m] * S_w[n]) * (acc [- Z_x[m] colsum[n]]);
+            // static: (S * S_w[n]) * (acc - Z colsum[n])
+            const int corr = a.za ? raw - a.za[m] * e.cs[r] : (a.sa ? raw : raw - a.z * e.cs[r]);
             const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e.sw[r]);
             float y = __fmul_rn(t, (float)corr);
             if (a.bias) y = __fadd_rn(y, e.bias[r]);

@@ -9,10 +9,10 @@
 // is the 16-bit GEMM over the outlier columns (part 2, "16-bit
 // decomposition" and "mixed-precision decomposition"), run on the 16-bit
 // MFMA into a separate binary32 accumulator per 32x32 sub-tile.  With a zero
-// point (the static path at large M), S_a is the per-tensor S and acc becomes
-// acc - Z * colsum[n] before the conversion (PDMIX terminology entry section
-// 2.3 decode formula through the zero-point expansion of the LLM.int8() notes,
-// part 1 section 2).
+// point acc becomes acc - Z * colsum[n] before the conversion (PDMIX
+// terminology entry section 2.3 through the zero-point expansion of the
+// LLM.int8() notes, part 1 section 2): ZP == 1, the static path's per-tensor
+// S and Z; ZP == 2, per-token scales S_a[m] with per-token zero points Z[m].
 //
 // Tiling: 256x256 output tile per 256-thread workgroup (4 wavefronts in a
 // 2x2 arrangement, 128x128 each = 4x4 v_mfma_i32_32x32x32_i8 tiles with
@@ -101,7 +101,7 @@ __device__ __forceinline__ void wait_loads_and_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SIDE, bool ZP>
+template <int OUT, bool SIDE, int ZP>
 __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // The four K-tile buffers (each A[256][64] followed by B[256][64]) are
     // four separate LDS objects, and every access below names its buffer
@@ -115,7 +115,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageAlloc];
     // the tile's row scales, column scales and bias, staged once at the start
     __shared__ __attribute__((aligned(16))) float s_sa[BM], s_sb[BN], s_bias[BN];
-    __shared__ __attribute__((aligned(16))) int32_t s_zc[ZP ? BN : 1];  // z * colsum[n]
+    // ZP == 1: z * colsum[n]; ZP == 2: colsum[n], with the row zero points in s_za
+    __shared__ __attribute__((aligned(16))) int32_t s_zc[ZP ? BN : 1];
+    __shared__ __attribute__((aligned(16))) int32_t s_za[ZP == 2 ? BM : 1];
     auto stage = [&](auto idx) -> uint8_t* {
         constexpr int i = decltype(idx)::value & (kStages - 1);
         if constexpr (i == 0) return st0;
@@ -144,7 +146,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         s_sa[tid] = m < M ? (a.sa ? a.sa[m] : a.s) : 0.0f;
         s_sb[tid] = n < N ? a.sb[n] : 0.0f;
         s_bias[tid] = (a.bias && n < N) ? a.bias[n] : 0.0f;
-        if constexpr (ZP) s_zc[tid] = n < N ? a.z * a.colsum[n] : 0;
+        if constexpr (ZP == 1) s_zc[tid] = n < N ? a.z * a.colsum[n] : 0;
+        if constexpr (ZP == 2) {
+            s_zc[tid] = n < N ? a.colsum[n] : 0;
+            s_za[tid] = m < M ? a.za[m] : 0;
+        }
     }
     __syncthreads();
 
@@ -295,8 +301,12 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         return b + (ml & 63) * kYPitch;
     };
     float sam[4];
+    [[maybe_unused]] int zam[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sam[i] = s_sa[ml0 + 32 * i];
+    for (int i = 0; i < 4; ++i) {
+        sam[i] = s_sa[ml0 + 32 * i];
+        if constexpr (ZP == 2) zam[i] = -s_za[ml0 + 32 * i];  // negated: one multiply-add below
+    }
     auto side_mfma = [&](uint4 wv, uint4 xv, v16f c) -> v16f {
         if constexpr (OUT == kF16)
             return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wv),
@@ -362,7 +372,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float t = __fmul_rn(sam[i], sbv[g][e]);
-                        const int32_t q = ZP ? acc[i][j][4 * g + e] - zcv[g][e] : acc[i][j][4 * g + e];
+                        // |Z| <= 128 and |colsum| < 127 * 65536 < 2^23: a 24-bit
+                        // multiply-add (v_mad_i32_i24)
+                        const int32_t q = ZP == 1   ? acc[i][j][4 * g + e] - zcv[g][e]
+                                          : ZP == 2 ? __mul24(zam[i], zcv[g][e]) + acc[i][j][4 * g + e]
+                                                    : acc[i][j][4 * g + e];
                         v[e] = __fmul_rn(t, (float)q);
                         if constexpr (SIDE) v[e] = __fadd_rn(v[e], side[4 * g + e]);
                         if constexpr (kBias) v[e] = __fadd_rn(v[e], bv[g][e]);
@@ -406,18 +420,20 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 
 }  // namespace
 
-void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, bool z_point) {
+void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, int zp_mode) {
     if (a.M <= 0 || a.N <= 0) return;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const dim3 grid(tiles), block(256);
-    if (!side && z_point)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, true>), grid, block, 0, st, a);
+    if (!side && zp_mode == 1)
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 1>), grid, block, 0, st, a);
+    else if (!side && zp_mode == 2)
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 2>), grid, block, 0, st, a);
     else if (!side)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 0>), grid, block, 0, st, a);
     else if (out_dt == kF16)
-        hipLaunchKernelGGL((k_gemm_i8<kF16, true, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kF16, true, 0>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, true, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, true, 0>), grid, block, 0, st, a);
 }
 
 }  // namespace pdq

@@ -189,6 +189,86 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
     return pdq_gemm_per_token(xq, x_scale, M, K, wq, w_scale, bias, N, y, ldy, acc_out, stream);
 }
 
+pdq_status pdq_quantize_per_token_asym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                       int8_t* xq, float* x_scale, int32_t* x_zp, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (M > 0 && ((K > 0 && !xq) || !x_scale || !x_zp)) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_zp, 4)) return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    launch_quant_rows_asym(x, x_dt, M, K, ldx, xq, x_scale, x_zp, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_gemm_per_token_asym(const int8_t* xq, const float* x_scale, const int32_t* x_zp, int64_t M,
+                                   int64_t K, const int8_t* wq, const float* w_scale,
+                                   const int32_t* w_colsum, const float* bias, int64_t N, uint16_t* y,
+                                   int64_t ldy, int32_t* acc_out, void* stream) {
+    PDQ_TRY(check_operand(xq, 1, M, K, K));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (M > 0 && (!x_scale || !x_zp)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(x_scale, 4) || !aligned(x_zp, 4) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) ||
+        !aligned(bias, 4) || !aligned(y, 2) || !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    if (M == 0 || N == 0) return PDQ_OK;
+    if (skinny_gemm(M, N)) {
+        DecodeArgs d{};
+        d.xq = xq;
+        d.wq = wq;
+        d.M = (int)M;
+        d.N = (int)N;
+        d.K = (int)K;
+        d.sa = x_scale;
+        d.za = x_zp;
+        d.sw = w_scale;
+        d.colsum = w_colsum;
+        d.bias = bias;
+        d.y = y;
+        d.ldy = ldy;
+        d.acc_out = acc_out;
+        launch_decode_gemv(d, static_cast<hipStream_t>(stream));
+        return launched();
+    }
+    GemmArgs g{};
+    g.A = xq;
+    g.B = wq;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.sa = x_scale;
+    g.za = x_zp;
+    g.colsum = w_colsum;
+    g.sb = w_scale;
+    g.bias = bias;
+    g.y = y;
+    g.ldy = ldy;
+    g.acc_out = acc_out;
+    launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), 2);
+    return launched();
+}
+
+pdq_status pdq_linear_prefill_asym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                                   const float* bias, int64_t N, int8_t* xq, float* x_scale, int32_t* x_zp,
+                                   uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (M > 0 && ((K > 0 && !xq) || !x_scale || !x_zp)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_zp, 4) || !aligned(w_scale, 4) ||
+        !aligned(w_colsum, 4) || !aligned(bias, 4) || !aligned(y, 2) || !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    PDQ_TRY(pdq_quantize_per_token_asym(x, x_dt, M, K, ldx, xq, x_scale, x_zp, stream));
+    return pdq_gemm_per_token_asym(xq, x_scale, x_zp, M, K, wq, w_scale, w_colsum, bias, N, y, ldy, acc_out,
+                                   stream);
+}
+
 pdq_status pdq_quantize_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
                                float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count,
                                void* stream) {
@@ -234,7 +314,7 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
         g.y = y;
         g.ldy = ldy;
         g.acc_out = acc_out;
-        launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), true);
+        launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), 1);
         return launched();
     }
     DecodeArgs d{};

@@ -27,6 +27,13 @@ struct OutlierSkip {
 void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
                        float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st);
 
+// Per-row (per-token) dynamic asymmetric INT8: range [min(min, 0), max(max,
+// 0)] of each row, scale[r] = (hi - lo) / 255 (1 if empty), zp[r] =
+// clamp(-128 - rne(lo / scale), -128, 127), q = clamp(rne(x / scale) + zp,
+// -128, 127), packed, padding zeroed.
+void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
+                            float* scale, int32_t* zp, hipStream_t st);
+
 // Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127), packed,
 // padding zeroed; saturation count added to *sat (nullable).
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
@@ -45,7 +52,8 @@ struct GemmArgs {
     const float* sa;  // [M] row scales, or null: the per-tensor scale s
     float s;
     int z;                  // zero point of A (static path), with colsum
-    const int32_t* colsum;  // [N] code sums of B; used when z_point
+    const int32_t* za;      // [M] per-row zero points of A (zp_mode 2), with colsum
+    const int32_t* colsum;  // [N] code sums of B; used when zp_mode != 0
     const float* sb;  // [N] column scales
     const float* bias;  // [N] or null
     void* y;
@@ -59,9 +67,10 @@ struct GemmArgs {
     int max_count;
 };
 // out_dt: kBF16 output without side product, or kF16 / kBF16 with the side
-// product when args.xo is set.  z_point (no side product): y uses
-// (float)(acc - z * colsum[n]) -- the static decode formula at any M.
-void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, bool z_point = false);
+// product when args.xo is set.  zp_mode (no side product): 1, y uses
+// (float)(acc - z * colsum[n]) -- the static decode formula at any M; 2,
+// (float)(acc - za[m] * colsum[n]) with the per-row scales sa.
+void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, int zp_mode = 0);
 
 // decode.hip --------------------------------------------------------------
 struct DecodeArgs {
@@ -69,6 +78,7 @@ struct DecodeArgs {
     const int8_t* wq;  // packed weight
     int M, N, K;
     const float* sa;  // [M] per-token scales (launch_decode_gemv), or null: s, z
+    const int32_t* za;  // [M] per-token zero points (with sa), or null
     float s;
     int z;
     const float* sw;

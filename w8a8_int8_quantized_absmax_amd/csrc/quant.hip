@@ -10,6 +10,10 @@
 //                   HBM once with 16-byte loads, kept in registers in its
 //                   storage format, reduced with cross-lane shuffles, then
 //                   quantized and written as INT8 codes.
+//                   ASYM: per-token dynamic asymmetric instead (the same
+//                   entry's prefill formula with its per-token zero point):
+//                   a row's range widened to contain 0, S = (hi - lo) / 255,
+//                   Z = -128 - rne(lo / S), codes by the decode formula.
 //  * k_quant_static per-tensor static asymmetric INT8 of the decode phase
 //                   (PDMIX terminology entry, section 2.3 decode formula),
 //                   with the saturation count of section 2.4.
@@ -128,12 +132,13 @@ __device__ __forceinline__ uint2 chunk_codes_absmax(const Raw8<DT>& r, uint32_t 
 // row is exactly CPL wavefront-wide chunks; otherwise lanes past the row
 // re-read its last chunk and zero it), so the compiler's waits count them
 // exactly.  CPL == 0: rows too long for registers are streamed twice (the
-// second pass hits the L2).
-template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM>
+// second pass hits the L2).  `rowint` receives the code sum of each row
+// (COLSUM) or its zero point (ASYM).
+template <int DT, int CPL, bool FULL, bool SKIP, bool COLSUM, bool ASYM = false>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, int64_t ld_bytes,
                                                     int64_t rows, int nch, int8_t* __restrict__ q,
                                                     float* __restrict__ scale,
-                                                    int32_t* __restrict__ colsum,
+                                                    int32_t* __restrict__ rowint,
                                                     OutlierSkip skip) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
@@ -154,8 +159,31 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
         return;
     }
-    int csum = 0;
+    int csum = 0, zq = 0, nsat = 0;
     float s;
+    // The asymmetric grid of a row's range [lo, hi] (both already widened to
+    // contain 0): S = fl(fl(hi - lo) / 255), 1 for an empty range;
+    // Z = clamp(-128 - rne(fl(lo / S)), -128, 127).
+    auto asym_grid = [&](float lo, float hi) {
+        hi = wave_max_full(hi);
+        lo = -wave_max_full(-lo);
+        s = hi == lo ? 1.0f : (hi - lo) / 255.0f;
+        zq = hi == lo ? 0 : min(max(-128 - (int)__builtin_rintf(lo / s), -128), 127);
+    };
+    auto asym_codes = [&](const Raw8<DT>& r, float inv) {
+        float v[8];
+        widen8<DT>(r, v);
+        return static_codes8(v, s, inv, zq, nsat);
+    };
+    auto range8 = [&](const Raw8<DT>& r, float& lo, float& hi) {
+        float v[8];
+        widen8<DT>(r, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo = fminf(lo, v[j]);
+            hi = fmaxf(hi, v[j]);
+        }
+    };
     // Outlier gather into X_out: lane j fetches x[row, idx[j]] (j < 64; the
     // index is clamped into the row, entries past the count are unset) while
     // the row is being quantized, and stores it, or the zero padding, once
@@ -191,41 +219,60 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             sk[i] = (FULL || c < nch) ? skip_mask<SKIP>(skip, min(c, nch - 1)) : 0u;
         }
         if (gather) gidx = skip.idx[min(lane, skip.max_out - 1)];
-        float amax = 0.0f;
+        float amax = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             if constexpr (SKIP) {
                 raw[i] = zero_skipped<DT>(raw[i], sk[i]);
                 sk[i] = 0;
             }
-            amax = chunk_absmax<DT>(raw[i], sk[i], amax);
+            if constexpr (ASYM)
+                range8(raw[i], lo, hi);  // zeros past the row leave the widened range as it is
+            else
+                amax = chunk_absmax<DT>(raw[i], sk[i], amax);
         }
         if (gather) gval = xr16[min(max(gidx, 0), nch * 8 - 1)];
-        amax = wave_max_full(amax);
-        s = absmax_step(amax);
+        if constexpr (ASYM) {
+            asym_grid(lo, hi);
+        } else {
+            amax = wave_max_full(amax);
+            s = absmax_step(amax);
+        }
         const float inv = 1.0f / s;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
             uint2 code;
-            if constexpr (COLSUM)
+            if constexpr (ASYM)
+                code = asym_codes(raw[i], inv);
+            else if constexpr (COLSUM)
                 code = chunk_codes<DT>(raw[i], sk[i], s, inv, csum);
             else
                 code = chunk_codes_absmax<DT, false>(raw[i], 0u, s, inv);
             if (FULL || c < nch) store_code(c, code);
         }
     } else {
-        float amax = 0.0f;
-        for (int c = lane; c < nch; c += 64)
-            amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
-        amax = wave_max_full(amax);
-        s = absmax_step(amax);
+        float amax = 0.0f, lo = 0.0f, hi = 0.0f;
+        for (int c = lane; c < nch; c += 64) {
+            if constexpr (ASYM)
+                range8(load_raw8<DT>(xr, c), lo, hi);
+            else
+                amax = chunk_absmax<DT>(load_raw8<DT>(xr, c), skip_mask<SKIP>(skip, c), amax);
+        }
+        if constexpr (ASYM) {
+            asym_grid(lo, hi);
+        } else {
+            amax = wave_max_full(amax);
+            s = absmax_step(amax);
+        }
         const float inv = 1.0f / s;
         if (gather) gval = xr16[min(max(skip.idx[min(lane, skip.max_out - 1)], 0), nch * 8 - 1)];
         for (int c = lane; c < nch; c += 64) {
             const Raw8<DT> r = load_raw8<DT>(xr, c);
             const uint32_t m = skip_mask<SKIP>(skip, c);
-            if constexpr (COLSUM)
+            if constexpr (ASYM)
+                store_code(c, asym_codes(r, inv));
+            else if constexpr (COLSUM)
                 store_code(c, chunk_codes<DT>(r, m, s, inv, csum));
             else
                 store_code(c, chunk_codes_absmax<DT, SKIP>(r, m, s, inv));
@@ -236,17 +283,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
     if (lane == 0) scale[row] = s;
     if constexpr (COLSUM) {
         csum = wave_sum(csum);
-        if (lane == 0) colsum[row] = csum;
+        if (lane == 0) rowint[row] = csum;
     }
+    if constexpr (ASYM)
+        if (lane == 0) rowint[row] = zq;
 }
 
 template <int DT, int CPL, bool FULL>
 void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, float* scale,
-                 int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+                 int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const OutlierSkip none{};
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
     const dim3 grid((unsigned)((rows_pad + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (skip)
+    if (asym)
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, true>), grid, dim3(256), 0, st, x,
+                           ldb, rows, nch, q, scale, colsum, none);
+    else if (skip)
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
                            rows, nch, q, scale, colsum, *skip);
     else if (colsum)
@@ -259,34 +311,34 @@ void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, f
 
 template <int DT, int CPL>
 void quant_rows_cpl(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                    int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+                    int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t ldb = ldx * Elem<DT>::bytes;
     const int nch = (int)(K / 8);
     if (CPL > 0 && nch == 64 * CPL)
-        launch_rows<DT, CPL, true>(rows, x, ldb, nch, q, scale, colsum, skip, st);
+        launch_rows<DT, CPL, true>(rows, x, ldb, nch, q, scale, colsum, skip, asym, st);
     else
-        launch_rows<DT, CPL, false>(rows, x, ldb, nch, q, scale, colsum, skip, st);
+        launch_rows<DT, CPL, false>(rows, x, ldb, nch, q, scale, colsum, skip, asym, st);
 }
 
 template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                   int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
+                   int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
     if (per_lane <= 1)
-        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else if (per_lane <= 2)
-        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 2>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else if (per_lane <= 4)
-        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 4>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else if (per_lane <= 8)
-        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 8>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else if (per_lane <= 16)
-        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 16>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else if (per_lane <= kMaxCpl)
-        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, kMaxCpl>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
     else
-        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, st);
+        quant_rows_cpl<DT, 0>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,9 +440,19 @@ void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t l
                        float* scale, int32_t* colsum, const OutlierSkip* skip, hipStream_t st) {
     if (rows <= 0) return;
     switch (dt) {
-        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
-        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
-        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, st); break;
+        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, colsum, skip, false, st); break;
+        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, colsum, skip, false, st); break;
+        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, colsum, skip, false, st); break;
+    }
+}
+
+void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
+                            float* scale, int32_t* zp, hipStream_t st) {
+    if (rows <= 0) return;
+    switch (dt) {
+        case kF32: quant_rows_dt<kF32>(x, rows, K, ldx, q, scale, zp, nullptr, true, st); break;
+        case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, zp, nullptr, true, st); break;
+        default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, zp, nullptr, true, st); break;
     }
 }
 

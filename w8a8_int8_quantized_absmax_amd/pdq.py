@@ -38,6 +38,12 @@ SIGNATURES = {
                                            _vp]),
     "pdq_gemm_static": (ctypes.c_int, [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _i64, _vp,
                                        _i64, _vp, _vp]),
+    "pdq_quantize_per_token_asym": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp,
+                                                   _vp]),
+    "pdq_gemm_per_token_asym": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp,
+                                               _i64, _vp, _vp]),
+    "pdq_linear_prefill_asym": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                               _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "pdq_weight_bytes": (_sz, [_i64, _i64]),
     "pdq_act_bytes": (_sz, [_i64, _i64]),
@@ -245,6 +251,48 @@ def linear_prefill(x, wq, w_scale, bias=None, want_acc: bool = False, out=None):
     _call("pdq_linear_prefill", _p(x), _DT[x.dtype], m, k, _ld(x), _p(wq), _p(w_scale), _p(bias),
           n, _p(xq), _p(xs), _p(y), _ld(y), _p(acc), _stream(x.device))
     return dict(y=y, xq=xq, x_scale=xs, acc=acc)
+
+
+def linear_prefill_asym(x, wq, w_scale, colsum, bias=None, want_acc: bool = False, out=None):
+    """Per-token dynamic asymmetric W8A8 linear -> dict(y bf16, xq, x_scale, x_zp[, acc])."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
+    xq = Codes.empty(m, k, x.device)
+    xs = torch.empty(m, dtype=torch.float32, device=x.device)
+    xz = torch.empty(m, dtype=torch.int32, device=x.device)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
+    _call("pdq_linear_prefill_asym", _p(x), _DT[x.dtype], m, k, _ld(x), _p(wq), _p(w_scale), _p(colsum),
+          _p(bias), n, _p(xq), _p(xs), _p(xz), _p(y), _ld(y), _p(acc), _stream(x.device))
+    return dict(y=y, xq=xq, x_scale=xs, x_zp=xz, acc=acc)
+
+
+def quantize_per_token_asym(x, xq=None, x_scale=None, x_zp=None):
+    """Per-token dynamic asymmetric INT8 -> (xq packed Codes [M,K], x_scale f32 [M], x_zp i32 [M])."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    xq = _codes_out(xq, m, k, x.device)
+    xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    xz = x_zp if x_zp is not None else torch.empty(m, dtype=torch.int32, device=x.device)
+    _call("pdq_quantize_per_token_asym", _p(x), _DT[x.dtype], m, k, _ld(x), _p(xq), _p(xs), _p(xz),
+          _stream(x.device))
+    return xq, xs, xz
+
+
+def gemm_per_token_asym(xq, x_scale, x_zp, wq, w_scale, colsum, bias=None, want_acc: bool = False, out=None):
+    """INT8 GEMM + per-token zero-point correction + dequant epilogue -> dict(y bf16[, acc])."""
+    xq = _codes_in(xq)
+    m, k = xq.shape
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
+    dev = xq.data.device
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+    _call("pdq_gemm_per_token_asym", _p(xq), _p(x_scale), _p(x_zp), m, k, _p(wq), _p(w_scale), _p(colsum),
+          _p(bias), n, _p(y), _ld(y), _p(acc), _stream(dev))
+    return dict(y=y, acc=acc)
 
 
 def linear_decode(x, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None,
