@@ -171,6 +171,23 @@ def bench_prefill(args, torch, pdq, synth):
         pdq._call("pdq_gemm_per_token_asym", pdq._p(xqs[r]), pdq._p(xsc), pdq._p(xz), M, K, pdq._p(wqs[r]),
                   pdq._p(ws), pdq._p(cs), None, N, pdq._p(y), N, None, pdq._stream(x.device))
 
+    # Context, not part of the step: the vendor library's INT8 GEMM (hipBLASLt
+    # through torch._int_mm, INT32 output, no quantization or epilogue) on the
+    # same codes in row-major form, rotated over the same number of copies.
+    ms_lib = None
+    try:
+        a_rm = torch.from_numpy(pdq.Codes(xqs[0], M, K).unpack()).cuda()
+        b_rm = torch.from_numpy(pdq.unpack(wq0, N, K)).cuda()
+        bs = [b_rm] + [b_rm.clone() for _ in range(nrot - 1)]
+
+        def lib_gemm(i):
+            torch._int_mm(a_rm, bs[i % nrot].t())
+
+        ms_lib = timed(lib_gemm, max(args.steps // 2, 10), args.warmup // 2, stream)
+        del bs, a_rm, b_rm
+    except (RuntimeError, TypeError) as e:  # no hipBLASLt INT8 path for this shape or build
+        log(f"[prefill] torch._int_mm reference unavailable: {e}")
+
     asym_steps = max(args.steps // 2, 10)
     ms_step_asym = timed(step_asym, asym_steps, args.warmup // 2, stream)
     ms_quant_asym = timed(quant_asym, asym_steps, args.warmup // 2, stream)
@@ -184,6 +201,7 @@ def bench_prefill(args, torch, pdq, synth):
     del wqs, xs, xqs
     return dict(M=M, K=K, N=N, ms_step=ms_step, ms_gemm=ms_gemm, ms_quant=ms_quant, ops=ops,
                 ms_step_asym=ms_step_asym, ms_quant_asym=ms_quant_asym, ms_gemm_asym=ms_gemm_asym,
+                ms_lib=ms_lib,
                 gemm_tops=gemm_tops, gemm_bytes=gemm_bytes, quant_bytes=quant_bytes,
                 x_host=x_host, w_host=w_host)
 
@@ -414,6 +432,8 @@ def main():
     pre = bench_prefill(args, torch, pdq, synth)
     log(f"[prefill] step {pre['ms_step']*1e3:.1f} us (quant {pre['ms_quant']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm']*1e3:.1f} us = {pre['gemm_tops']:.0f} TOPS)")
+    if pre["ms_lib"] is not None:
+        log(f"[prefill] hipBLASLt INT8 GEMM (torch._int_mm, INT32 out) {pre['ms_lib']*1e3:.1f} us")
     log(f"[prefill asym] step {pre['ms_step_asym']*1e3:.1f} us (quant {pre['ms_quant_asym']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm_asym']*1e3:.1f} us)")
     dec = llm = None
@@ -451,6 +471,10 @@ def main():
                      "us_per_launch": round(pre["ms_gemm"] * 1e3, 2)},
         "prefill_quant": {"us": round(pre["ms_quant"] * 1e3, 2),
                           "GBps": round(pre["quant_bytes"] / (pre["ms_quant"] * 1e-3) / 1e9, 1)},
+        "reference_library_gemm": None if pre["ms_lib"] is None else {
+            "what": "hipBLASLt INT8 GEMM via torch._int_mm on the same codes, INT32 out, no quantization "
+                    "or epilogue", "us": round(pre["ms_lib"] * 1e3, 2),
+            "TOPS": round(pre["ops"] / (pre["ms_lib"] * 1e-3) / 1e12, 1)},
         "prefill_asym": {"us_step": round(pre["ms_step_asym"] * 1e3, 2),
                          "us_quant": round(pre["ms_quant_asym"] * 1e3, 2),
                          "us_gemm": round(pre["ms_gemm_asym"] * 1e3, 2),
