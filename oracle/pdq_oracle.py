@@ -174,6 +174,52 @@ def quantize_static(x, s, z):
 
 
 # ---------------------------------------------------------------------------
+# Static per-tensor symmetric quantization (tensor-wise absmax)
+# ---------------------------------------------------------------------------
+
+def absmax_finalize(state):
+    """S of the tensor-wise absmax grid from a (min, max) range: S = C / 127
+    with C = max(|min|, |max|), the largest magnitude seen; S = 1 if C == 0.
+
+    [LLM.int8] part 1 section 1: absmax quantization maps the tensor's
+    largest magnitude onto 127, one scale for the whole tensor by default
+    (section 3, tensor-wise); taken here with static activation parameters,
+    measured offline over calibration batches (the "traditional W8A8 static
+    quantization" that [PDMIX-term] section 2 sets PDMIX against).
+    """
+    c = max(abs(F32(state[0])), abs(F32(state[1])))
+    return F32(absmax_scale(np.array([c], F32))[0])
+
+
+def calibrate_absmax(batches):
+    state = None
+    for b in batches:
+        state = minmax_update(state, b)
+    return state, absmax_finalize(state)
+
+
+def quantize_static_sym(x, s):
+    """q = clamp(rne(fl(x / S)), -127, 127) with one static S; also counts the
+    values whose rne(x / S) leaves [-127, 127] (inputs beyond the calibrated
+    magnitude, the static-scale saturation risk of [PDMIX-term] 2.4)."""
+    x = _f32(x)
+    r = np.rint(x / F32(s))
+    sat = int(np.count_nonzero(np.abs(r) > QMAX_SYM))
+    return np.clip(r, QMIN_SYM, QMAX_SYM).astype(np.int8), sat
+
+
+def linear_static_sym(x, s, wq, sw, bias=None):
+    """Static tensor-wise symmetric W8A8 linear: y = (S * S_w[n]) * acc (+ bias).
+
+    Returns dict(xq, sat, acc, y32).
+    """
+    xq, sat = quantize_static_sym(x, s)
+    acc = int_matmul(xq, wq)
+    assert np.all(np.abs(acc) < 2**31)
+    return dict(xq=xq, sat=sat, acc=acc, y32=dequantize(acc, F32(s), sw, bias))
+
+
+# ---------------------------------------------------------------------------
 # Per-token dynamic asymmetric quantization (prefill with Z_token)
 # ---------------------------------------------------------------------------
 

@@ -301,6 +301,54 @@ def test_calibration_resume_is_exact():
 
 
 # ---------------------------------------------------------------------------
+# Static tensor-wise symmetric quantization (absmax over calibration batches)
+# ---------------------------------------------------------------------------
+
+def check_tensor_absmax(oracle=O):
+    """The worked example's values as one tensor: C = 2 over both rows, and the
+    page's absmax formula round(127 x / C) (round half to even) gives the codes;
+    a value beyond the calibrated magnitude saturates at +-127 and is counted."""
+    g = golden("llm_int8_worked_example.json")
+    row = g["row_regular_values"]                # [2, -1, 1]
+    second = [1, 0.5, -2]                        # filled in by this test, |v| <= C
+    x = np.array([row, second], F32)
+    _, s = oracle.calibrate_absmax([x[:1], x[1:]])
+    assert s == F32(g["row_absmax_C_x"]) / F32(127)
+    q, sat = oracle.quantize_static_sym(x, s)
+    want = [[round(127 * v / g["row_absmax_C_x"]) for v in r] for r in (row, second)]
+    assert want == [[127, -64, 64], [64, 32, -127]] and q.tolist() == want and sat == 0
+    q2, sat2 = oracle.quantize_static_sym(np.array([[3.0, -3.0, 2.0, -2.0]], F32), s)
+    assert q2.tolist() == [[127, -127, 127, -127]] and sat2 == 2
+
+
+def test_tensor_absmax_worked_example_and_saturation():
+    check_tensor_absmax()
+
+
+def test_tensor_absmax_calibration_is_the_largest_magnitude():
+    batches = [synth.activations(60 + b, 16, 128, [4], 30.0, offset=0.2, dtype="f32") for b in range(5)]
+    batches[3][7, 9] = -500.0  # the largest magnitude, negative, in one batch
+    state, s = O.calibrate_absmax(batches)
+    assert s == F32(500) / F32(127)
+    # a saved state resumes bit-exactly, in any batch order
+    st2, s2 = O.calibrate_absmax(batches[::-1])
+    assert (st2, s2) == (state, s)
+    q, sat = O.quantize_static_sym(batches[3], s)
+    assert sat == 0 and q[7, 9] == -127
+
+
+def test_tensor_absmax_equals_per_token_when_rows_share_the_absmax():
+    x = synth.activations(66, 9, 64, [], dtype="f32")
+    x[:, 5] = 4.0  # every row's absmax, so the tensor's too
+    q_row, s_row = O.quantize_rows_absmax(x)
+    _, s = O.calibrate_absmax([x])
+    q, sat = O.quantize_static_sym(x, s)
+    assert np.all(s_row == s) and np.array_equal(q, q_row) and sat == 0
+    err = np.abs(np.float64(s) * q - x.astype(np.float64))
+    assert np.all(err <= np.float64(s) / 2 * (1 + 2.0**-20))
+
+
+# ---------------------------------------------------------------------------
 # Per-token dynamic asymmetric quantization (the prefill formula with Z_token)
 # ---------------------------------------------------------------------------
 
@@ -495,6 +543,12 @@ def _plus_zero_point(acc, colsum, z):
     return np.asarray(acc, np.int64) + np.int64(z) * np.asarray(colsum, np.int64)[None, :]
 
 
+def _static_sym_asym_clamp(x, s):
+    """Clamped to the asymmetric range [-128, 127]."""
+    r = np.rint(np.asarray(x, F32) / F32(s))
+    return np.clip(r, -128, 127).astype(np.int8), int(np.count_nonzero((r < -128) | (r > 127)))
+
+
 def _plus_zero_point_rows(acc, colsum, z):
     z = np.asarray(z, np.int64)
     if z.ndim == 0:
@@ -546,6 +600,7 @@ def _rowwise_over_all_columns(x, cols):
     (_Mutant(quantize_rows_regular=_rowwise_over_all_columns), check_outlier_example),
     (_Mutant(outlier_columns=_nonstrict_outliers), check_threshold_strict),
     (_Mutant(zero_point_correct=_plus_zero_point_rows), check_prefill_asym),
+    (_Mutant(quantize_static_sym=_static_sym_asym_clamp), check_tensor_absmax),
     (_Mutant(quantize_rows_asym=_asym_rows_unwidened), check_asym_rows),
     (_Mutant(quantize_rows_asym=_asym_rows_zero_point_sign), check_asym_rows),
 ])
