@@ -194,6 +194,36 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
                              void* stream);
 
 /*
+ * Static tensor-wise SYMMETRIC W8A8: [LLM.int8] part 1 section 1 absmax
+ * quantization, one scale for the whole activation tensor (section 3,
+ * tensor-wise), measured offline over calibration batches -- the
+ * "traditional W8A8 static quantization" with static activation parameters
+ * that [PDMIX-term] section 2 sets PDMIX against.  Same kernels as the decode
+ * linear with Z = 0 and the symmetric code range.
+ *
+ * pdq_calibrate_static_sym: updates the same MinMax state as
+ *   pdq_calibrate_static (minmax[2] in/out, initialise to {+INF, -INF});
+ *   when a_scale is non-NULL it is finalised to S = C / 127 with
+ *   C = max(|min|, |max|) (S = 1 if C == 0 or no value was seen).
+ * pdq_quantize_static_sym: xq = clamp(rne(x / S), -127, 127) (packed,
+ *   pdq_act_bytes(M, K) bytes); sat_count (nullable) INCREMENTED by the
+ *   number of values with |rne(x / S)| > 127.
+ * pdq_linear_static_sym: the quantizer then the GEMM, y = bf16((S * S_w[n]) *
+ *   (float)acc [+ bias[n]]) (one launch for M * K <= 8192); acc_out [M, N]
+ *   int32 or NULL.  a_scale > 0 and finite, else PDQ_ERR_UNSUPPORTED.
+ */
+pdq_status pdq_calibrate_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                    float* minmax, float* a_scale, void* stream);
+
+pdq_status pdq_quantize_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   float a_scale, int8_t* xq, uint32_t* sat_count, void* stream);
+
+pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                 float a_scale, const int8_t* wq, const float* w_scale, const float* bias,
+                                 int64_t N, int8_t* xq, uint16_t* y, int64_t ldy, int32_t* acc_out,
+                                 uint32_t* sat_count, void* stream);
+
+/*
  * Prefill linear with per-token dynamic ASYMMETRIC activations: the
  * [PDMIX-term] 2.3 prefill formula taken with its per-token zero point
  * Z_token, Q = clamp(round(X / S_token) + Z_token, -128, 127), both computed
@@ -252,8 +282,9 @@ pdq_status pdq_quantize_static(const void* x, pdq_dtype x_dt, int64_t M, int64_t
                                float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count,
                                void* stream);
 
-/* Skinny INT8 GEMM + zero-point epilogue:
- * y = bf16((S * S_w[n]) * (float)(sum_k xq wq - Z * colsum[n]) [+ bias[n]]). */
+/* INT8 GEMM + zero-point epilogue:
+ * y = bf16((S * S_w[n]) * (float)(sum_k xq wq - Z * colsum[n]) [+ bias[n]]);
+ * w_colsum is required unless a_zp == 0 (then also the static symmetric GEMM). */
 pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale, int32_t a_zp,
                            const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
                            const float* bias, int64_t N, uint16_t* y, int64_t ldy, int32_t* acc_out,

@@ -187,6 +187,8 @@ def absmax_finalize(state):
     measured offline over calibration batches (the "traditional W8A8 static
     quantization" that [PDMIX-term] section 2 sets PDMIX against).
     """
+    if F32(state[0]) > F32(state[1]):  # no value seen yet
+        return F32(1)
     c = max(abs(F32(state[0])), abs(F32(state[1])))
     return F32(absmax_scale(np.array([c], F32))[0])
 

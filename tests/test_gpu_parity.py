@@ -258,6 +258,68 @@ def decode_case(x, w, dtype, s, z, bias=None, exact=True):
     return ref
 
 
+# ---------------------------------------------------------------------------
+# static tensor-wise symmetric (absmax over calibration batches)
+# ---------------------------------------------------------------------------
+
+def static_sym_case(x, w, dtype, s, bias=None):
+    wq, ws, _, (rq, rs, _) = weight_case(w, dtype)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    res = pdq.linear_static_sym(dev(x, dtype), s, wq, ws, b, sat_count=sat, want_acc=True)
+    ref = O.linear_static_sym(x, F32(s), rq, rs, bias)
+    assert codes_equal(res["xq"], ref["xq"])
+    assert int(host(sat)[0]) == ref["sat"]
+    assert np.array_equal(host(res["acc"]), ref["acc"])
+    check_16bit(host(res["y"]), ref["y32"], "bf16", exact=True)
+    return ref
+
+
+def test_static_sym_calibration():
+    batches = [synth.activations(7400 + b, 64, 1024, [3, 700], 100.0, offset=0.1, dtype="bf16") for b in range(6)]
+    mm = pdq.minmax_state("cuda")
+    for i, xb in enumerate(batches):
+        s = pdq.calibrate_static_sym(dev(xb, "bf16"), mm, finalize=i == len(batches) - 1)
+    _, s_ref = O.calibrate_absmax(batches)
+    assert host(s).view(np.uint32)[0] == np.array([s_ref], F32).view(np.uint32)[0]
+    # a fresh state finalised before any batch gives S = 1
+    empty = pdq.minmax_state("cuda")
+    s0 = pdq.calibrate_static_sym(dev(np.zeros((0, 64), F32), "bf16"), empty, finalize=True)
+    assert float(host(s0)[0]) == 1.0 == O.absmax_finalize((np.inf, -np.inf))
+
+
+# One launch (M * K <= 8192), the skinny kernel, and the tiled GEMM (1100 x 2600);
+# the scale comes from calibration rows that do not cover the decode values'
+# largest magnitudes, so some saturate.
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (4, 100, 2048), (37, 1000, 1040), (1100, 2600, 1040)])
+def test_static_sym_linear(dtype, m, n, k):
+    cal = [synth.activations(7500 + b, 32, k, [2], 8.0, dtype=dtype) for b in range(3)]
+    _, s = O.calibrate_absmax(cal)
+    x = synth.activations(7600 + m, m, k, [2, k - 5], 20.0, dtype=dtype)
+    big = 3.0 * max(float(np.abs(c).max()) for c in cal)
+    x[0, 7], x[m - 1, 9] = big, -big
+    x = synth.round_to(x, dtype)
+    ref = static_sym_case(x, synth.weights(7700 + n, n, k, dtype), dtype, s, bias=synth.bias(7800, n))
+    assert ref["sat"] > 0
+    if m * k > 8192:
+        assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+
+
+@pytest.mark.parametrize("m,n,k", [(9, 300, 1040), (1100, 2600, 512)])
+def test_gemm_static_zero_point_zero_needs_no_colsum(m, n, k):
+    """With Z = 0 the static GEMM takes no code sums, on either kernel."""
+    xq = synth.random_int8(7900 + m, (m, k), -127, 127)
+    w = synth.weights(7901, n, k, "bf16")
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, "bf16")
+    codes = pdq.Codes(torch.from_numpy(pack(xq)).cuda(), m, k)
+    a = pdq.gemm_static(codes, F32(0.11), 0, wq, ws, None, want_acc=True)
+    b = pdq.gemm_static(codes, F32(0.11), 0, wq, ws, cs, want_acc=True)
+    acc = O.int_matmul(xq, rq)
+    assert np.array_equal(host(a["acc"]), acc) and torch.equal(a["y"], b["y"])
+    check_16bit(host(a["y"]), O.dequantize(acc, F32(0.11), rs), "bf16", exact=True)
+
+
 @pytest.fixture(scope="module")
 def decode_params():
     c = synth.Decode()

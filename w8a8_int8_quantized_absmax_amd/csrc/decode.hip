@@ -7,6 +7,9 @@
 // notes (part 1 section 2) with a symmetric weight; or, with per-token scales
 // (the same entry's prefill formula, for the per-token GEMM entry points),
 // y = (S_x[m] * S_w[n]) * (float)(acc [- Z_x[m] * colsum[n]]) [+ bias[n]].
+// The static symmetric grid (tensor-wise absmax with a static scale, LLM.int8()
+// notes part 1 section 1) is the static one with Z = 0 and codes clamped to
+// [-127, 127].
 //
 // The weight matrix is read exactly once and is the whole cost (the
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     v4i xcode = v4i{};  // ONEROW: this lane's codes
     if constexpr (FUSED) {
         const float inv = 1.0f / a.s;
+        const int qmin = a.sym ? -127 : -128;
         int nsat = 0;
 #pragma unroll
         for (int i = 0; i < kQ; ++i) {
@@ -248,9 +252,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
                     if (kk < K) {
                         float v[8];
                         widen8<DT>(xa[i], v);
-                        const uint2 lo = static_codes8(v, a.s, inv, a.z, nsat);
+                        const uint2 lo = static_codes8(v, a.s, inv, a.z, nsat, qmin);
                         widen8<DT>(xb[i], v);
-                        const uint2 hi = static_codes8(v, a.s, inv, a.z, nsat);
+                        const uint2 hi = static_codes8(v, a.s, inv, a.z, nsat, qmin);
                         code = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
                     }
                     if (blockIdx.x == 0)

@@ -293,7 +293,7 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
     if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
     if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
         return PDQ_ERR_UNSUPPORTED;
-    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (N > 0 && (!w_scale || (a_zp != 0 && !w_colsum))) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
     if (!aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) || !aligned(y, 2) ||
         !aligned(acc_out, 4))
@@ -314,7 +314,7 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
         g.y = y;
         g.ldy = ldy;
         g.acc_out = acc_out;
-        launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), 1);
+        launch_gemm_i8(g, PDQ_BF16, false, static_cast<hipStream_t>(stream), a_zp != 0 ? 1 : 0);
         return launched();
     }
     DecodeArgs d{};
@@ -326,13 +326,79 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
     d.s = a_scale;
     d.z = a_zp;
     d.sw = w_scale;
-    d.colsum = w_colsum;
+    d.colsum = a_zp != 0 ? w_colsum : nullptr;
     d.bias = bias;
     d.y = y;
     d.ldy = ldy;
     d.acc_out = acc_out;
     launch_decode_gemv(d, static_cast<hipStream_t>(stream));
     return launched();
+}
+
+pdq_status pdq_calibrate_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                    float* minmax, float* a_scale, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!minmax) return PDQ_ERR_NULL;
+    if (!aligned(minmax, 4) || !aligned(a_scale, 4)) return PDQ_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    launch_minmax(x, x_dt, M, K, ldx, minmax, st);
+    if (a_scale) launch_absmax_finalize(minmax, a_scale, st);
+    return launched();
+}
+
+pdq_status pdq_quantize_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   float a_scale, int8_t* xq, uint32_t* sat_count, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!(a_scale > 0.0f) || !isfinite(a_scale)) return PDQ_ERR_UNSUPPORTED;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(sat_count, 4)) return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    launch_quant_static(x, x_dt, M, K, ldx, a_scale, 0, xq, sat_count, static_cast<hipStream_t>(stream),
+                        true);
+    return launched();
+}
+
+pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                 float a_scale, const int8_t* wq, const float* w_scale, const float* bias,
+                                 int64_t N, int8_t* xq, uint16_t* y, int64_t ldy, int32_t* acc_out,
+                                 uint32_t* sat_count, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (!(a_scale > 0.0f) || !isfinite(a_scale)) return PDQ_ERR_UNSUPPORTED;
+    if (N > 0 && !w_scale) return PDQ_ERR_NULL;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(w_scale, 4) || !aligned(bias, 4) || !aligned(y, 2) ||
+        !aligned(acc_out, 4) || !aligned(sat_count, 4))
+        return PDQ_ERR_ALIGN;
+    if (N > 0 && decode_fusable(M, K)) {
+        DecodeArgs d{};
+        d.wq = wq;
+        d.M = (int)M;
+        d.N = (int)N;
+        d.K = (int)K;
+        d.s = a_scale;
+        d.z = 0;
+        d.sym = 1;
+        d.sw = w_scale;
+        d.bias = bias;
+        d.y = y;
+        d.ldy = ldy;
+        d.acc_out = acc_out;
+        d.x = x;
+        d.x_dt = x_dt;
+        d.ldx = ldx;
+        d.xq_out = xq;
+        d.sat = sat_count;
+        launch_decode_fused(d, static_cast<hipStream_t>(stream));
+        return launched();
+    }
+    PDQ_TRY(pdq_quantize_static_sym(x, x_dt, M, K, ldx, a_scale, xq, sat_count, stream));
+    return pdq_gemm_static(xq, M, K, a_scale, 0, wq, w_scale, nullptr, bias, N, y, ldy, acc_out, stream);
 }
 
 pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,

@@ -204,12 +204,13 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
-// Static asymmetric codes of 8 values (decode phase): r = rne(fl(x / s)),
-// pre-clamped to +-512 so that the integer conversion stays in range (the
-// clamped value saturates exactly when the unclamped one does), r' = r + z,
-// code = clamp(r', -128, 127).  Adds the number of r' outside [-128, 127] to
-// nsat.  inv = fl(1 / s).
-__device__ __forceinline__ uint2 static_codes8(const float (&v)[8], float s, float inv, int z, int& nsat) {
+// Static codes of 8 values (decode phase): r = rne(fl(x / s)), pre-clamped to
+// +-512 so that the integer conversion stays in range (the clamped value
+// saturates exactly when the unclamped one does), r' = r + z, code =
+// clamp(r', qmin, 127) with qmin = -128 (asymmetric grid) or -127 (symmetric,
+// z = 0).  Adds the number of r' outside [qmin, 127] to nsat.  inv = fl(1 / s).
+__device__ __forceinline__ uint2 static_codes8(const float (&v)[8], float s, float inv, int z, int& nsat,
+                                               int qmin = -128) {
     float rq[8];
     rne_quotient8<false>(v, s, inv, rq);
     int code[8];
@@ -217,8 +218,8 @@ __device__ __forceinline__ uint2 static_codes8(const float (&v)[8], float s, flo
     for (int j = 0; j < 8; ++j) {
         const float r = fminf(fmaxf(rq[j], -512.0f), 512.0f);
         const int ri = (int)r + z;
-        nsat += (ri < -128) | (ri > 127);
-        code[j] = min(max(ri, -128), 127);
+        nsat += (ri < qmin) | (ri > 127);
+        code[j] = min(max(ri, qmin), 127);
     }
     return make_uint2(pack4_i8(code[0], code[1], code[2], code[3]),
                       pack4_i8(code[4], code[5], code[6], code[7]));

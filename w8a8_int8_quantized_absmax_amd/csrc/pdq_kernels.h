@@ -34,15 +34,18 @@ void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t l
 void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
                             float* scale, int32_t* zp, hipStream_t st);
 
-// Static asymmetric code: q = clamp(rne(x / s) + z, -128, 127), packed,
-// padding zeroed; saturation count added to *sat (nullable).
+// Static code: q = clamp(rne(x / s) + z, -128, 127) (sym: z = 0 and the
+// range [-127, 127]), packed, padding zeroed; saturation count added to *sat
+// (nullable).
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
-                         int8_t* q, uint32_t* sat, hipStream_t st);
+                         int8_t* q, uint32_t* sat, hipStream_t st, bool sym = false);
 
 // MinMax observer update of minmax[2]; optional finalisation to (S, Z).
 void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float* minmax,
                    hipStream_t st);
 void launch_minmax_finalize(const float* minmax, float* a_scale, int32_t* a_zp, hipStream_t st);
+// Tensor-wise absmax scale of the state: max(|min|, |max|) / 127 (1 if 0 or no value seen).
+void launch_absmax_finalize(const float* minmax, float* a_scale, hipStream_t st);
 
 // gemm_i8.hip -------------------------------------------------------------
 struct GemmArgs {
@@ -93,6 +96,7 @@ struct DecodeArgs {
     int64_t ldx;
     int8_t* xq_out;  // packed activation codes, written by workgroup 0 (padding rows by others)
     uint32_t* sat;   // nullable saturation counter
+    int sym;         // symmetric static grid: z = 0, codes clamped to [-127, 127]
 };
 // Activations already quantized (xq).
 void launch_decode_gemv(const DecodeArgs& a, hipStream_t st);

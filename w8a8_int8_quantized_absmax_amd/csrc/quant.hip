@@ -21,7 +21,10 @@
 // Every code matrix is written in the packed tile layout of pdq_device.h,
 // the layout the GEMMs read, padding rows and K values as zeros.
 //  * k_minmax       the MinMax observer of the static calibration, and
-//    k_minmax_finalize its (S, Z) (PDMIX usage guide, section 3).
+//    k_minmax_finalize its (S, Z) (PDMIX usage guide, section 3), or the
+//                   tensor-wise absmax scale S = max(|min|, |max|) / 127 of
+//                   the static symmetric variant (LLM.int8() notes, part 1
+//                   section 1, with a static scale).
 //
 // Every division is the correctly rounded binary32 division and every
 // rounding to an integer is round-half-to-even (v_rndne_f32), so the codes
@@ -346,10 +349,11 @@ void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* 
 // One thread per 8-value chunk of the padded code matrix (rows rounded up to
 // 16, K to 64): chunk (row, col) of the activations, or a zero of the padding.
 // WIDE: the chunk index needs 64 bits.
+// qmin: -128 (asymmetric grid) or -127 (symmetric, z = 0).
 template <int DT, bool WIDE>
 __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x, int64_t ld_bytes,
                                                       int64_t rows, int nch, int cpr, int64_t total,
-                                                      int8_t* __restrict__ q, float s, int z,
+                                                      int8_t* __restrict__ q, float s, int z, int qmin,
                                                       uint32_t* __restrict__ sat) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const float inv = 1.0f / s;
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void k_quant_static(const void* __restrict__ x
         if (row < rows && col < nch) {
             float v[8];
             widen8<DT>(load_raw8<DT>(static_cast<const char*>(x) + row * ld_bytes, col), v);
-            code = static_codes8(v, s, inv, z, nsat);
+            code = static_codes8(v, s, inv, z, nsat, qmin);
         }
         const int ktiles = cpr / 8;
         *reinterpret_cast<uint2*>(q + wpack_block(row / kWGroup, col >> 3, ktiles) +
@@ -419,8 +423,13 @@ __global__ __launch_bounds__(256) void k_minmax(const void* __restrict__ x, int6
 }
 
 __global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restrict__ s_out,
-                                  int32_t* __restrict__ z_out) {
+                                  int32_t* __restrict__ z_out, int sym) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    if (sym) {  // tensor-wise absmax: S = max(|min|, |max|) / 127; 1 before any value
+        const float c = mm[0] > mm[1] ? 0.0f : fmaxf(fabsf(mm[0]), fabsf(mm[1]));
+        *s_out = absmax_step(c);
+        return;
+    }
     const float lo = fminf(mm[0], 0.0f);
     const float hi = fmaxf(mm[1], 0.0f);
     float s = 1.0f;
@@ -458,26 +467,27 @@ void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int6
 
 template <int DT>
 void quant_static_dt(const void* x, int64_t M, int64_t ldb, int nch, int cpr, int64_t total, int8_t* q,
-                     float s, int z, uint32_t* sat, hipStream_t st) {
+                     float s, int z, int qmin, uint32_t* sat, hipStream_t st) {
     const dim3 grid((unsigned)((total + 255) / 256));
     if (total <= 0xffffffffll)
         hipLaunchKernelGGL((k_quant_static<DT, false>), grid, dim3(256), 0, st, x, ldb, M, nch, cpr, total,
-                           q, s, z, sat);
+                           q, s, z, qmin, sat);
     else
         hipLaunchKernelGGL((k_quant_static<DT, true>), grid, dim3(256), 0, st, x, ldb, M, nch, cpr, total,
-                           q, s, z, sat);
+                           q, s, z, qmin, sat);
 }
 
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
-                         int8_t* q, uint32_t* sat, hipStream_t st) {
+                         int8_t* q, uint32_t* sat, hipStream_t st, bool sym) {
     if (M <= 0 || K <= 0) return;
+    const int qmin = sym ? -127 : -128;
     const int nch = (int)(K / 8);
     const int cpr = (int)((K + kWTileK - 1) / kWTileK * 8);  // chunks per padded row
     const int64_t total = (M + kWGroup - 1) / kWGroup * kWGroup * cpr;
     switch (dt) {
-        case kF32: quant_static_dt<kF32>(x, M, ldx * 4, nch, cpr, total, q, s, z, sat, st); break;
-        case kBF16: quant_static_dt<kBF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, sat, st); break;
-        default: quant_static_dt<kF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, sat, st); break;
+        case kF32: quant_static_dt<kF32>(x, M, ldx * 4, nch, cpr, total, q, s, z, qmin, sat, st); break;
+        case kBF16: quant_static_dt<kBF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, qmin, sat, st); break;
+        default: quant_static_dt<kF16>(x, M, ldx * 2, nch, cpr, total, q, s, z, qmin, sat, st); break;
     }
 }
 
@@ -505,7 +515,11 @@ void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, flo
 }
 
 void launch_minmax_finalize(const float* mm, float* a_scale, int32_t* a_zp, hipStream_t st) {
-    hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, a_zp);
+    hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, a_zp, 0);
+}
+
+void launch_absmax_finalize(const float* mm, float* a_scale, hipStream_t st) {
+    hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, nullptr, 1);
 }
 
 }  // namespace pdq
