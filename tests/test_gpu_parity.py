@@ -605,6 +605,43 @@ def test_gemm_ignores_code_padding(m):
         assert np.array_equal(clean, junk)
 
 
+# The largest K the library accepts with the most extreme codes: |acc - Z colsum|
+# reaches 255 * 127 * 65536 = 2122383360, just inside INT32, on the skinny
+# kernel (3 x 20) and the tiled GEMM (4096 x 704), for the static zero point
+# at both ends of its range, for per-token zero points, and symmetric.
+@pytest.mark.parametrize("m,n", [(3, 20), (4096, 704)])
+def test_max_k_extreme_codes(m, n):
+    k = 65536
+    assert pdq.gemm_kernel(m, n) == ("skinny" if m == 3 else "tiled")
+    xq = synth.random_int8(8000 + m, (m, k))
+    xq[0, :], xq[m - 1, :] = -128, 127
+    wq = synth.random_int8(8001 + m, (n, k), -127, 127)
+    wq[0, :], wq[1, :] = 127, -127
+    ws = np.linspace(1e-3, 2e-3, n, dtype=F32)
+    cs = wq.astype(np.int64).sum(axis=1).astype(np.int32)
+    codes = pdq.Codes(torch.from_numpy(pack(xq)).cuda(), m, k)
+    wd = torch.from_numpy(pack_weight(wq)).cuda()
+    wsd, csd = torch.from_numpy(ws).cuda(), torch.from_numpy(cs).cuda()
+    rows = sample_rows(m, 6, 8002)
+    acc = O.int_matmul(xq[rows], wq)
+    assert acc.min() == -128 * 127 * k
+    for z in (127, -128, 0):
+        s = F32(0.05)
+        res = pdq.gemm_static(codes, s, z, wd, wsd, csd, want_acc=True)
+        assert np.array_equal(host(res["acc"])[rows], acc)
+        corr = O.zero_point_correct(acc, cs, z)
+        if z == 127:
+            assert corr.min() == -255 * 127 * k
+        check_16bit(host(res["y"])[rows], O.dequantize(corr, s, ws), "bf16", exact=True)
+    za = np.where(np.arange(m) % 2 == 0, 127, -128).astype(np.int32)
+    sx = np.linspace(0.01, 0.02, m, dtype=F32)
+    res = pdq.gemm_per_token_asym(codes, torch.from_numpy(sx).cuda(), torch.from_numpy(za).cuda(), wd, wsd, csd,
+                                  want_acc=True)
+    assert np.array_equal(host(res["acc"])[rows], acc)
+    corr = O.zero_point_correct(acc, cs, za[rows])
+    check_16bit(host(res["y"])[rows], O.dequantize(corr, sx[rows], ws), "bf16", exact=True)
+
+
 def test_per_token_rounding_near_ties():
     rows = []
     for c in (127.0, 1.0, 3.3, 0.021, 5e4, 2.0):
