@@ -517,6 +517,53 @@ def test_outlier_llm_int8_full_sampled():
 # building blocks: quantize once, GEMM against several weights
 # ---------------------------------------------------------------------------
 
+def test_decoder_block_linear_set():
+    """The decoder-block workload at full size: QKV 4096->12288, O 4096->4096,
+    gate+up 4096->28672, down 14336->4096, one INT8 weight copy per linear
+    serving both phases.  Prefill: 8192 tokens per-token dynamic (codes and
+    scales of every token; accumulators and outputs on sampled tokens).
+    Calibration: 50 batches of 512 tokens.  Decode: all 256 steps at batch 32
+    through the same weight buffers (codes and saturation counts of every
+    step; accumulators and outputs of sampled steps)."""
+    c = synth.DecoderBlock()
+    check_steps = {0, 1, 127, c.decode_steps - 1}
+    for l, (name, n, k) in enumerate(c.linears):
+        print(f"[block] {name}: {n} x {k}", flush=True)
+        wq, ws, cs, (rq, rs, rc) = weight_case(c.w(l), c.dtype)
+        x = c.prefill_x(l)
+        res = pdq.linear_prefill(dev(x, c.dtype), wq, ws, want_acc=True)
+        xq_ref, sx_ref = O.quantize_rows_absmax(x)
+        assert codes_equal(res["xq"], xq_ref)
+        assert np.array_equal(host(res["x_scale"]).view(np.uint32), sx_ref.view(np.uint32))
+        rows = sample_rows(c.prefill_tokens, 12, 9000 + l)
+        acc = O.int_matmul(xq_ref[rows], rq)
+        assert np.array_equal(host(res["acc"])[rows], acc)
+        check_16bit(host(res["y"])[rows], O.dequantize(acc, sx_ref[rows], rs), "bf16", exact=True)
+        del x, res, xq_ref
+        cal = [c.calib(l, b) for b in range(50)]
+        mm = pdq.minmax_state("cuda")
+        for b, xb in enumerate(cal):
+            out = pdq.calibrate_static(dev(xb, c.dtype), mm, finalize=b == len(cal) - 1)
+        _, s, z = O.calibrate(cal)
+        del cal
+        assert host(out[0]).view(np.uint32)[0] == np.array([s], F32).view(np.uint32)[0] and int(host(out[1])[0]) == z
+        sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+        total_sat = 0
+        for t in range(c.decode_steps):
+            xt = c.decode_x(l, t)
+            want_acc = t in check_steps
+            res = pdq.linear_decode(dev(xt, c.dtype), s, z, wq, ws, cs, sat_count=sat, want_acc=want_acc)
+            q_ref, sat_ref = O.quantize_static(xt, s, z)
+            total_sat += sat_ref
+            assert codes_equal(res["xq"], q_ref), t
+            if want_acc:
+                ref = O.linear_decode(xt, s, z, rq, rs, rc)
+                assert np.array_equal(host(res["acc"]), ref["acc"])
+                check_16bit(host(res["y"]), ref["y32"], "bf16", exact=True)
+        assert int(host(sat)[0]) == total_sat
+        print(f"[block] {name}: S={s} Z={z}, {total_sat} saturated decode values", flush=True)
+
+
 def test_per_token_blocks_shared_activation():
     x = synth.activations(6000, 200, 1024, [7, 900], 100.0, dtype="bf16")
     xq, xs = pdq.quantize_per_token(dev(x, "bf16"))
