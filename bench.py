@@ -14,7 +14,10 @@ Also measured in the same run and reported under "prefill_asym", "decode" and
 decode linear 4096 -> 4096 at M in {1, 8, 32, 64}
 (HBM GB/s of the skinny GEMM against 8 TB/s, weights rotated over >= 1 GiB of
 copies so that no cache serves them), and the LLM.int8() decomposition
-2048 x (8192 -> 28672) in fp16 with threshold 6.0.
+2048 x (8192 -> 28672) in fp16 with threshold 6.0; and under "decoder_block"
+the block's four linears (QKV, O, gate+up, down at hidden 4096) on one shared
+INT8 weight copy each: a prefill pass over 8192 tokens and 256 decode steps
+at batch 32.
 
 cpu_baseline: the CPU oracle timed on the host on the same prefill workload.
 
@@ -348,6 +351,66 @@ def bench_sweep(args, torch, pdq, synth):
     return dict(S=s, Z=z, K=K, N=N, per_m=rows)
 
 
+def bench_block(args, torch, pdq, synth):
+    """The decoder-block linear set (QKV 4096->12288, O 4096->4096, gate+up
+    4096->28672, down 14336->4096), one shared INT8 weight copy per linear:
+    a prefill pass over 8192 tokens (per-token dynamic) and decode steps at
+    batch 32 (per-tensor static, calibrated on 50 batches of 512 tokens per
+    linear), weights rotated over 4 copies of the set (~1 GB)."""
+    c = synth.DecoderBlock()
+    nrot = 4
+    lin = []
+    for l, (name, n, k) in enumerate(c.linears):
+        wq, ws, cs = pdq.quantize_weight(torch.from_numpy(c.w(l)).to(torch.bfloat16).cuda())
+        mm = pdq.minmax_state("cuda")
+        for b in range(50):
+            out = pdq.calibrate_static(torch.from_numpy(c.calib(l, b)).to(torch.bfloat16).cuda(), mm,
+                                       finalize=b == 49)
+        s, z = float(out[0].item()), int(out[1].item())
+        lin.append(dict(name=name, n=n, k=k, wqs=[wq] + [wq.clone() for _ in range(nrot - 1)], ws=ws, cs=cs,
+                        s=s, z=z))
+        log(f"[block] {name} {n}x{k}: S={s:.5f} Z={z}")
+    stream = torch.cuda.current_stream()
+    # prefill: the four linears on 8192 tokens each
+    M = c.prefill_tokens
+    for l, d in enumerate(lin):
+        d["x"] = torch.from_numpy(c.prefill_x(l)).to(torch.bfloat16).cuda()
+        d["xq"] = torch.empty(pdq.act_bytes(M, d["k"]), dtype=torch.int8, device="cuda")
+        d["xs"] = torch.empty(M, dtype=torch.float32, device="cuda")
+        d["y"] = torch.empty((M, d["n"]), dtype=torch.bfloat16, device="cuda")
+
+    def prefill(i):
+        for d in lin:
+            pdq._call("pdq_linear_prefill", pdq._p(d["x"]), pdq.BF16, M, d["k"], d["k"], pdq._p(d["wqs"][i % nrot]),
+                      pdq._p(d["ws"]), None, d["n"], pdq._p(d["xq"]), pdq._p(d["xs"]), pdq._p(d["y"]), d["n"], None,
+                      pdq._stream(d["x"].device))
+
+    ms_prefill = timed(prefill, max(args.steps // 5, 5), max(args.warmup // 10, 3), stream)
+    ops = sum(2.0 * M * d["n"] * d["k"] for d in lin)
+    for d in lin:
+        del d["x"], d["xq"], d["xs"], d["y"]
+    # decode: 256 steps at batch 32, each step the four linears on its own inputs
+    B, T = c.decode_batch, c.decode_steps
+    for l, d in enumerate(lin):
+        d["xt"] = torch.from_numpy(np.stack([c.decode_x(l, t) for t in range(T)])).to(torch.bfloat16).cuda()
+        d["xq"] = torch.empty(pdq.act_bytes(B, d["k"]), dtype=torch.int8, device="cuda")
+        d["y"] = torch.empty((B, d["n"]), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        for d in lin:
+            x = d["xt"][t]
+            pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, B, d["k"], d["k"], d["s"], d["z"],
+                      pdq._p(d["wqs"][t % nrot]), pdq._p(d["ws"]), pdq._p(d["cs"]), None, d["n"], pdq._p(d["xq"]),
+                      pdq._p(d["y"]), d["n"], None, None, pdq._stream(x.device))
+
+    ms_step = graph_timed(step, T, 2, stream)
+    wbytes = sum(d["n"] * d["k"] for d in lin)
+    step_bytes = sum(d["n"] * d["k"] + 2 * B * d["k"] + 2 * B * d["n"] + 8 * d["n"] for d in lin)
+    del lin
+    return dict(ms_prefill=ms_prefill, prefill_ops=ops, ms_step=ms_step, weight_bytes=wbytes,
+                step_bytes=step_bytes, steps=T, batch=B, tokens=M)
+
+
 def bench_llm_int8(args, torch, pdq, synth):
     c = synth.LlmInt8()
     M, K, N = c.M, c.K, c.N
@@ -449,7 +512,7 @@ def main():
         log(f"[prefill] hipBLASLt INT8 GEMM (torch._int_mm, INT32 out) {pre['ms_lib']*1e3:.1f} us")
     log(f"[prefill asym] step {pre['ms_step_asym']*1e3:.1f} us (quant {pre['ms_quant_asym']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm_asym']*1e3:.1f} us)")
-    dec = llm = None
+    dec = llm = blk = None
     if args.only == "all":
         dec = bench_decode(args, torch, pdq, synth)
         for m, r in dec["per_batch"].items():
@@ -460,6 +523,11 @@ def main():
                 f"{r['us_call_static_sym_graph']:.2f} us")
         llm = bench_llm_int8(args, torch, pdq, synth)
         log(f"[llm.int8] {llm['ms']*1e3:.1f} us, {llm['int8_tops']:.0f} TOPS, |O|={llm['n_outlier']}")
+        blk = bench_block(args, torch, pdq, synth)
+        log(f"[block] prefill of 4 linears x {blk['tokens']} tokens {blk['ms_prefill']*1e3:.0f} us = "
+            f"{blk['prefill_ops'] / (blk['ms_prefill'] * 1e-3) / 1e12:.0f} TOPS; decode step (4 linears, "
+            f"batch {blk['batch']}) {blk['ms_step']*1e3:.1f} us = "
+            f"{blk['step_bytes'] / (blk['ms_step'] * 1e-3) / 1e9:.0f} GB/s")
 
     value = pre["ops"] / (pre["ms_step"] * 1e-3) / 1e12
     out = {
@@ -503,6 +571,17 @@ def main():
         out["llm_int8"] = {"us": round(llm["ms"] * 1e3, 1), "int8_TOPS": round(llm["int8_tops"], 1),
                            "frac": round(llm["int8_tops"] / PEAK_INT8_TOPS, 4),
                            "n_outlier": llm["n_outlier"], "side_GFLOP": round(llm["side_flops"] / 1e9, 3)}
+    if blk:
+        out["decoder_block"] = {
+            "workload": "QKV 4096->12288, O 4096->4096, gate+up 4096->28672, down 14336->4096; bf16 in/out",
+            "prefill_us": round(blk["ms_prefill"] * 1e3, 1), "prefill_tokens": blk["tokens"],
+            "prefill_TOPS": round(blk["prefill_ops"] / (blk["ms_prefill"] * 1e-3) / 1e12, 1),
+            "prefill_frac": round(blk["prefill_ops"] / (blk["ms_prefill"] * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "decode_us_per_step": round(blk["ms_step"] * 1e3, 2), "decode_batch": blk["batch"],
+            "decode_steps_per_replay": blk["steps"],
+            "decode_GBps": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9, 1),
+            "decode_frac": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "int8_weight_MB": round(blk["weight_bytes"] / 1e6, 1)}
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(pre)
