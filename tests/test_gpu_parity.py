@@ -71,12 +71,14 @@ def test_prefill_tiny_f32():
     prefill_case(c.x(), c.w(), "f32", bias=c.bias())
 
 
-# (1100, 2600, 1040) runs on the tiled GEMM, the others on the skinny kernel.
+# (2048, 2600, 1040) runs on the tiled GEMM, the others on the skinny kernel
+# ((200, 4100) with 32 channels per workgroup, the last one's second group
+# past N).
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(300, 700, 1040), (1, 257, 128), (257, 1, 16), (513, 256, 2048),
-                                   (1100, 2600, 1040)])
+                                   (200, 4100, 1040), (2048, 2600, 1040)])
 def test_prefill_ragged(dtype, m, n, k):
-    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
     x = synth.activations(2000 + m, m, k, [0, k - 1, k // 3], 100.0, dtype=dtype)
     if m > 2:
         x[2, :] = 0.0  # all-zero token: scale 1, codes 0
@@ -87,12 +89,12 @@ def test_prefill_ragged(dtype, m, n, k):
 # K tiles of 64: every count modulo the depth of the tiled GEMM's LDS ring
 # (four) and of the skinny kernel's batches (two in flight of up to eight
 # tiles per wavefront, four wavefronts), whole and ragged, with and without
-# bias; M x N = 1100 x 2600 runs on the tiled GEMM, 300 x 520 on the skinny
-# kernel.
-@pytest.mark.parametrize("m,n", [(1100, 2600), (300, 520)])
+# bias; M x N = 2048 x 2600 runs on the tiled GEMM, 300 x 520 (16 channels per
+# workgroup) and 256 x 4112 (32) on the skinny kernel.
+@pytest.mark.parametrize("m,n", [(2048, 2600), (300, 520), (256, 4112)])
 @pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 336, 640, 656, 1216, 1280, 2112, 4160])
 def test_prefill_k_depths(m, n, k):
-    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
     x = synth.activations(2300 + k, m, k, [1, k - 2], 100.0, dtype="bf16")
     w = synth.weights(2400 + k, n, k, "bf16")
     bias = synth.bias(2500 + k, n) if k % 128 == 0 else None
@@ -107,7 +109,8 @@ def test_prefill_k_depths(m, n, k):
 # Per-token codes at decode sizes: the weight-streaming kernel runs with
 # per-row scales in its epilogue.
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (17, 4096, 4096), (64, 520, 2048), (65, 520, 2048),
-                                   (130, 700, 1040), (600, 1000, 1040), (256, 4096, 4096)])
+                                   (130, 700, 1040), (600, 1000, 1040), (256, 4096, 4096), (200, 4100, 1040),
+                                   (32, 12300, 512)])
 def test_per_token_skinny(m, n, k):
     assert pdq.gemm_kernel(m, n) == "skinny"
     x = synth.activations(2600 + m, m, k, [0, k - 1], 100.0, dtype="bf16")
@@ -134,12 +137,13 @@ def prefill_asym_case(x, w, dtype, bias=None, rows=None):
     return res
 
 
-# Both GEMM kernels: (1100, 2600) runs on the tiled one, the others on the skinny one.
+# Both GEMM kernels: (2048, 2600) runs on the tiled one, the others on the
+# skinny one ((200, 4100) with 32 channels per workgroup).
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (37, 520, 2048), (300, 700, 1040), (257, 1, 16),
-                                   (1100, 2600, 1040)])
+                                   (200, 4100, 1040), (2048, 2600, 1040)])
 def test_prefill_asym_ragged(dtype, m, n, k):
-    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
     x = synth.activations(7000 + m, m, k, [0, k - 1, k // 3], 100.0, offset=0.3, dtype=dtype)
     if m > 5:
         x[2, :] = 0.0                # empty range: S = 1, Z = 0
@@ -288,11 +292,11 @@ def test_static_sym_calibration():
     assert float(host(s0)[0]) == 1.0 == O.absmax_finalize((np.inf, -np.inf))
 
 
-# One launch (M * K <= 8192), the skinny kernel, and the tiled GEMM (1100 x 2600);
+# One launch (M * K <= 8192), the skinny kernel, and the tiled GEMM (2048 x 2600);
 # the scale comes from calibration rows that do not cover the decode values'
 # largest magnitudes, so some saturate.
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (4, 100, 2048), (37, 1000, 1040), (1100, 2600, 1040)])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (4, 100, 2048), (37, 1000, 1040), (2048, 2600, 1040)])
 def test_static_sym_linear(dtype, m, n, k):
     cal = [synth.activations(7500 + b, 32, k, [2], 8.0, dtype=dtype) for b in range(3)]
     _, s = O.calibrate_absmax(cal)
@@ -303,10 +307,10 @@ def test_static_sym_linear(dtype, m, n, k):
     ref = static_sym_case(x, synth.weights(7700 + n, n, k, dtype), dtype, s, bias=synth.bias(7800, n))
     assert ref["sat"] > 0
     if m * k > 8192:
-        assert pdq.gemm_kernel(m, n) == ("tiled" if m == 1100 else "skinny")
+        assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
 
 
-@pytest.mark.parametrize("m,n,k", [(9, 300, 1040), (1100, 2600, 512)])
+@pytest.mark.parametrize("m,n,k", [(9, 300, 1040), (2048, 2600, 512)])
 def test_gemm_static_zero_point_zero_needs_no_colsum(m, n, k):
     """With Z = 0 the static GEMM takes no code sums, on either kernel."""
     xq = synth.random_int8(7900 + m, (m, k), -127, 127)
@@ -359,11 +363,12 @@ def test_decode_fused_shapes(dtype, m, n, k):
 
 
 # Static codes past 64 rows: the zero-point correction in the epilogue of
-# the skinny kernel (the first three) and of the tiled GEMM (the others).
-@pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096),
-                                   (1100, 2600, 1040), (700, 4096, 4096), (2000, 1500, 2048)])
+# the skinny kernel (the first four; 300 x 4100 with 32 channels per
+# workgroup) and of the tiled GEMM (the others).
+@pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096), (300, 4100, 1040),
+                                   (2048, 2600, 1040), (1600, 4096, 2048), (3000, 1500, 2048)])
 def test_static_large_m(m, n, k):
-    assert pdq.gemm_kernel(m, n) == ("tiled" if m in (1100, 700, 2000) else "skinny")
+    assert pdq.gemm_kernel(m, n) == ("tiled" if m in (2048, 1600, 3000) else "skinny")
     cal = [synth.activations(4900 + b, 64, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16") for b in range(3)]
     _, s, z = O.calibrate(cal)
     x = synth.activations(4950 + m, m, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16")
@@ -628,12 +633,14 @@ def _near_ties(s, kmax, ulps=3):
     return np.concatenate(vals).astype(F32)
 
 
-@pytest.mark.parametrize("m", [1, 5, 37, 70, 300])
-def test_gemm_ignores_code_padding(m):
-    """Only the codes reach the results: the GEMMs give the same bits when the
+@pytest.mark.parametrize("m,n", [(1, 200), (5, 200), (37, 200), (70, 200), (300, 200), (300, 4100),
+                                 (2050, 2600)])
+def test_gemm_ignores_code_padding(m, n):
+    """Only the codes reach the results: the GEMMs (skinny with 16 and 32
+    channels per workgroup, tiled for 2050 x 2600) give the same bits when the
     padding of the packed activations (rows past M, K values past K) holds
     arbitrary bytes instead of zeros."""
-    n, k = 200, 1040
+    k = 1040
     xq = synth.random_int8(6300 + m, (m, k))
     img = pack(xq)
     pad = pack(np.ones((m, k), np.int8)) == 0
@@ -654,9 +661,9 @@ def test_gemm_ignores_code_padding(m):
 
 # The largest K the library accepts with the most extreme codes: |acc - Z colsum|
 # reaches 255 * 127 * 65536 = 2122383360, just inside INT32, on the skinny
-# kernel (3 x 20) and the tiled GEMM (4096 x 704), for the static zero point
+# kernel (3 x 20) and the tiled GEMM (4096 x 1408), for the static zero point
 # at both ends of its range, for per-token zero points, and symmetric.
-@pytest.mark.parametrize("m,n", [(3, 20), (4096, 704)])
+@pytest.mark.parametrize("m,n", [(3, 20), (4096, 1408)])
 def test_max_k_extreme_codes(m, n):
     k = 65536
     assert pdq.gemm_kernel(m, n) == ("skinny" if m == 3 else "tiled")

@@ -13,9 +13,10 @@
 //
 // The weight matrix is read exactly once and is the whole cost (the
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
-// bandwidth-bound).  Each 256-thread workgroup owns 16 weight channels; its
-// four wavefronts interleave over the K tiles of the packed weight (wavefront
-// w takes tiles w, w + 4, ...) and multiply with v_mfma_i32_16x16x64_i8,
+// bandwidth-bound).  Each 256-thread workgroup owns 16 weight channels (32
+// when there are workgroups enough to spare); its four wavefronts interleave
+// over the K tiles of the packed weight (wavefront w takes tiles w, w + 4,
+// ...) and multiply with v_mfma_i32_16x16x64_i8,
 // weight channels as the row operand, activation rows as the column operand.
 // In the packed layout the 16 channels' K tile is one contiguous 1 KB block
 // (and all of them one contiguous run), so lane l loads its fragment (channel
@@ -77,34 +78,41 @@ __device__ __forceinline__ EpiOps load_epi(const DecodeArgs& a, int n0, int lane
     return e;
 }
 
-// Sum of the four wavefronts' partial accumulators and the epilogue: register
-// block mb holds activation rows mbase + 16 mb .. + 16, and wavefront mb
-// finishes it.
-template <int NMB>
-__device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i (&acc)[NMB],
-                                                 const EpiOps& e, int n0, int mbase,
-                                                 v4i (&red)[4][NMB][64]) {
+// Sum of the four wavefronts' partial accumulators and the epilogue: block
+// (g, mb) holds weight channels n0 + 16 g .. + 16 and activation rows
+// mbase + 16 mb .. + 16, and wavefront (g NMB + mb) % 4 finishes it.
+template <int NG, int NMB>
+__device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i (&acc)[NG][NMB],
+                                                 const EpiOps (&e)[NG], int n0, int mbase,
+                                                 v4i (&red)[4][NG * NMB][64]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) red[wave][mb][lane] = acc[mb];
-    __syncthreads();
-    if (wave >= NMB) return;
-    const v4i tot = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
-    const int m = mbase + wave * 16 + (lane & 15);
-    if (m >= a.M) return;
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 4 * (lane >> 4) + r;
-        if (n < a.N) {
-            const int raw = tot[r];
-            if (a.acc_out) a.acc_out[(size_t)m * a.N + n] = raw;
-            // per-token: (S_x[m] * S_w[n]) * (acc [- Z_x[m] colsum[n]]);
-            // static: (S * S_w[n]) * (acc - Z colsum[n])
-            const int corr = a.za ? raw - a.za[m] * e.cs[r] : (a.sa ? raw : raw - a.z * e.cs[r]);
-            const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e.sw[r]);
-            float y = __fmul_rn(t, (float)corr);
-            if (a.bias) y = __fadd_rn(y, e.bias[r]);
-            a.y[(size_t)m * a.ldy + n] = f32_to_bf16(y);
+        for (int mb = 0; mb < NMB; ++mb) red[wave][g * NMB + mb][lane] = acc[g][mb];
+    __syncthreads();
+#pragma unroll
+    for (int blk = 0; blk < NG * NMB; ++blk) {
+        if (blk % 4 != wave) continue;  // wavefront-uniform
+        constexpr int kNMB = NMB;
+        const int g = blk / kNMB, mb = blk % kNMB;
+        const v4i tot = red[0][blk][lane] + red[1][blk][lane] + red[2][blk][lane] + red[3][blk][lane];
+        const int m = mbase + mb * 16 + (lane & 15);
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 16 * g + 4 * (lane >> 4) + r;
+            if (n < a.N) {
+                const int raw = tot[r];
+                if (a.acc_out) a.acc_out[(size_t)m * a.N + n] = raw;
+                // per-token: (S_x[m] * S_w[n]) * (acc [- Z_x[m] colsum[n]]);
+                // static: (S * S_w[n]) * (acc - Z colsum[n])
+                const int corr = a.za ? raw - a.za[m] * e[g].cs[r] : (a.sa ? raw : raw - a.z * e[g].cs[r]);
+                const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e[g].sw[r]);
+                float y = __fmul_rn(t, (float)corr);
+                if (a.bias) y = __fadd_rn(y, e[g].bias[r]);
+                a.y[(size_t)m * a.ldy + n] = f32_to_bf16(y);
+            }
         }
     }
 }
@@ -130,18 +138,25 @@ constexpr int kFusedWave = kFusedBytes / 4 + 16 * 64;
 // its wavefront, quarter l / 16) into registers, and for tile j the lanes
 // 16 r -- the only ones whose MFMA column is the activation row -- take
 // quarter r from lane 16 r + j of their DPP row: no LDS round trip.
-template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false>
+//
+// NG: 16-channel groups per workgroup (2 when there are workgroups enough to
+// spare: the activation fragments then serve 32 channels per load).
+template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false, int NG = 1>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
-    constexpr int KB = NMB == 1 ? 8 : (NMB == 2 ? 6 : 4);  // K tiles per batch
-    __shared__ v4i red[4][NMB][64];
+    static_assert(!FUSED || NG == 1, "the one-launch path has one channel group");
+    // K tiles per batch: about 5 fragments per tile and batch, two batches in flight
+    constexpr int KB = NG == 1 ? (NMB == 1 ? 8 : (NMB == 2 ? 6 : 4)) : (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3));
+    __shared__ v4i red[4][NG * NMB][64];
     __shared__ __attribute__((aligned(16))) int8_t xs[FUSED ? 4 : 1][FUSED ? kFusedWave : 16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = a.M, K = a.K;
-    const int n0 = blockIdx.x * kRows;
+    const int n0 = blockIdx.x * kRows * NG;
     const int mbase = blockIdx.y * kMRows;
     const int nsteps = (K + 63) / 64;  // K tiles
     const int kl = 16 * (lane >> 4);
-    const EpiOps e = load_epi(a, n0, lane);
+    EpiOps e[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) e[g] = load_epi(a, n0 + kRows * g, lane);
     __builtin_amdgcn_sched_barrier(0);
 
     // FUSED: each wavefront quantizes exactly the activations of its own K
@@ -177,8 +192,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // this lane's weight fragment in K tile s: wp + s * kWBlock
-    const int8_t* wp = a.wq + wpack_block(n0 / kWGroup, 0, nsteps) + wpack_pos(lane & 15, lane >> 4);
+    // this lane's weight fragment of group g in K tile s: wp[g] + s * kWBlock
+    // (a group past the last is clamped onto it: its outputs are not stored)
+    const int8_t* wp[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        wp[g] = a.wq + wpack_block(min(n0 / kWGroup + g, (a.N - 1) / kWGroup), 0, nsteps) +
+                wpack_pos(lane & 15, lane >> 4);
     // this lane's activation fragment of register block mb in K tile s:
     // xp[mb] + s * kWBlock (row lane % 16 of the block, clamped into M)
     const int8_t* xp[NMB];
@@ -193,23 +213,26 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     const int nbatch = (tsteps + KB - 1) / KB;
 
     struct Frags {
-        v4i w[KB];
+        v4i w[NG][KB];
         v4i x[FUSED ? 1 : NMB][KB];
     };
     auto load = [&](int b, Frags& f) {
 #pragma unroll
         for (int i = 0; i < KB; ++i) {
             const int s = min(wave + 4 * (b * KB + i), nsteps - 1);
-            f.w[i] = *reinterpret_cast<const v4i*>(wp + (size_t)s * kWBlock);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) f.w[g][i] = *reinterpret_cast<const v4i*>(wp[g] + (size_t)s * kWBlock);
             if constexpr (!FUSED) {
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) f.x[mb][i] = *reinterpret_cast<const v4i*>(xp[mb] + (size_t)s * kWBlock);
             }
         }
     };
-    v4i acc[NMB];
+    v4i acc[NG][NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] = v4i{};
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[g][mb] = v4i{};
     auto compute = [&](int b, const Frags& f) {
         // FUSED: the batch's activation fragments from LDS first, then the MFMAs
         v4i xv[FUSED ? KB : 1];
@@ -222,11 +245,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
         for (int i = 0; i < KB; ++i) {
             if (b * KB + i < tsteps) {  // wavefront-uniform
                 if constexpr (FUSED) {
-                    acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], xv[i], acc[0], 0, 0, 0);
+                    acc[0][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[0][i], xv[i], acc[0][0], 0, 0, 0);
                 } else {
 #pragma unroll
-                    for (int mb = 0; mb < NMB; ++mb)
-                        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], f.x[mb][i], acc[mb], 0, 0, 0);
+                    for (int g = 0; g < NG; ++g)
+#pragma unroll
+                        for (int mb = 0; mb < NMB; ++mb)
+                            acc[g][mb] =
+                                __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[g][i], f.x[mb][i], acc[g][mb], 0, 0, 0);
                 }
             }
         }
@@ -293,7 +319,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
                                 row_shl<B * KB + 6>(xcode), row_shl<B * KB + 7>(xcode)};
 #pragma unroll
             for (int i = 0; i < KB; ++i)
-                if (B * KB + i < tsteps) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], xv[i], acc[0], 0, 0, 0);
+                if (B * KB + i < tsteps)
+                    acc[0][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[0][i], xv[i], acc[0][0], 0, 0, 0);
         };
         run(std::integral_constant<int, 0>{}, f0);
         run(std::integral_constant<int, 1>{}, f1);
@@ -322,13 +349,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
             if (b + 1 < nbatch) compute(b + 1, f1);
         }
     }
-    reduce_and_store<NMB>(a, acc, e, n0, mbase, red);
+    reduce_and_store<NG, NMB>(a, acc, e, n0, mbase, red);
 }
 
-template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false>
+template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false, int NG = 1>
 void launch_k(const DecodeArgs& a, hipStream_t st) {
-    const dim3 grid((a.N + kRows - 1) / kRows, FUSED ? 1 : (a.M + kMRows - 1) / kMRows);
-    hipLaunchKernelGGL((k_decode<NMB, FUSED, DT, kQ, ONEROW>), grid, dim3(256), 0, st, a);
+    const dim3 grid((a.N + kRows * NG - 1) / (kRows * NG), FUSED ? 1 : (a.M + kMRows - 1) / kMRows);
+    hipLaunchKernelGGL((k_decode<NMB, FUSED, DT, kQ, ONEROW, NG>), grid, dim3(256), 0, st, a);
 }
 
 // One-launch path: kQ = 16-value chunks per lane = ceil(M x ceil(tiles / 4) x 4 / 64).
@@ -356,15 +383,30 @@ void launch_decode_fused(const DecodeArgs& a, hipStream_t st) {
     }
 }
 
-void launch_decode_gemv(const DecodeArgs& a, hipStream_t st) {
-    if (a.M <= 0 || a.N <= 0) return;
+// 32 channels per workgroup halve the activation fragments each channel
+// costs, but also the number of workgroups: worth it from about one and a
+// half workgroups per CU (256 CUs).
+bool decode_wide_groups(int64_t M, int64_t N) {
+    return (N + 2 * kRows - 1) / (2 * kRows) * ((M + kMRows - 1) / kMRows) >= 384;
+}
+
+template <int NG>
+void launch_gemv_ng(const DecodeArgs& a, hipStream_t st) {
     const int mrows = a.M < kMRows ? a.M : kMRows;
     switch ((mrows + 15) / 16) {
-        case 1: launch_k<1, false, kBF16>(a, st); break;
-        case 2: launch_k<2, false, kBF16>(a, st); break;
-        case 3: launch_k<3, false, kBF16>(a, st); break;
-        default: launch_k<4, false, kBF16>(a, st); break;
+        case 1: launch_k<1, false, kBF16, 1, false, NG>(a, st); break;
+        case 2: launch_k<2, false, kBF16, 1, false, NG>(a, st); break;
+        case 3: launch_k<3, false, kBF16, 1, false, NG>(a, st); break;
+        default: launch_k<4, false, kBF16, 1, false, NG>(a, st); break;
     }
+}
+
+void launch_decode_gemv(const DecodeArgs& a, hipStream_t st) {
+    if (a.M <= 0 || a.N <= 0) return;
+    if (decode_wide_groups(a.M, a.N))
+        launch_gemv_ng<2>(a, st);
+    else
+        launch_gemv_ng<1>(a, st);
 }
 
 }  // namespace pdq

@@ -16,17 +16,19 @@ constexpr int64_t kMaxK = 65536;        // |sum_k (q_x - Z) q_w| < 255 * 127 * K
 constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
 // Which kernel runs an M x N INT8 GEMM, whichever quantization scheme
 // produced the codes: the skinny (weight-streaming) kernel of decode.hip or
-// the 256 x 256-tile GEMM.  The skinny kernel runs ceil(N / 16) x
-// ceil(M / 64) workgroups, each one pass over the K tiles of 16 weight
-// channels for up to 64 activation rows, and costs about 4 us plus 4.7 us per
-// 256 of them; the tiled GEMM costs about 52 us per round of 256 tiles, however
-// few tiles the round holds (both measured on MI355X at K = 4096; K scales
-// both alike).  Up to 64 rows the skinny kernel always runs.
+// the 256 x 256-tile GEMM.  The skinny kernel's work is ceil(N / 16) x
+// ceil(M / 64) units, each one pass over the K tiles of 16 weight channels
+// for up to 64 activation rows, and costs about 4 us plus 4.7 us per 256 of
+// them with 16 channels per workgroup, 3.6 us with 32; the tiled GEMM costs
+// about 52 us per round of 256 tiles, however few tiles the round holds (all
+// measured on MI355X at K = 4096; K scales both alike).  Up to 64 rows the
+// skinny kernel always runs.
 bool skinny_gemm(int64_t M, int64_t N) {
     if (M <= 64) return true;
     const double units = (double)((N + 15) / 16) * (double)((M + 63) / 64);
     const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
-    return 4.0 + 4.7 * units / 256.0 < 52.0 * ceil(tiles / 256.0);
+    const double per256 = decode_wide_groups(M, N) ? 3.6 : 4.7;
+    return 4.0 + per256 * units / 256.0 < 52.0 * ceil(tiles / 256.0);
 }
 
 int elem_bytes(int dt) { return dt == PDQ_F32 ? 4 : 2; }

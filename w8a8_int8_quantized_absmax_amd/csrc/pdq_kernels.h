@@ -98,8 +98,10 @@ struct DecodeArgs {
     uint32_t* sat;   // nullable saturation counter
     int sym;         // symmetric static grid: z = 0, codes clamped to [-127, 127]
 };
-// Activations already quantized (xq).
+// Activations already quantized (xq); 16 or 32 channels per workgroup
+// (decode_wide_groups).
 void launch_decode_gemv(const DecodeArgs& a, hipStream_t st);
+bool decode_wide_groups(int64_t M, int64_t N);
 // Static quantization fused into the GEMM; only when decode_fusable(M, K).
 bool decode_fusable(int64_t M, int64_t K);
 void launch_decode_fused(const DecodeArgs& a, hipStream_t st);
