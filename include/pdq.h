@@ -35,10 +35,12 @@
  *     never synchronises: all work is enqueued on `stream` (a hipStream_t;
  *     NULL means the null stream), and buffers must stay valid until that
  *     work has completed.
- *   - Matrices are row-major.  Leading dimensions (ld*) are in elements.
- *     Inner dimension K must be a multiple of 16; every base pointer and
- *     every row pitch (ld * element size) of a K-wide operand must be a
- *     multiple of 16 bytes.  Sizes may be 0 (nothing is written then).
+ *   - Floating-point matrices are row-major; leading dimensions (ld*) are in
+ *     elements.  INT8 matrices (weights wq, activation codes xq) are in the
+ *     packed tile layout described at pdq_quantize_weight.  Inner dimension K
+ *     must be a multiple of 16 (at most 65536); every base pointer and every
+ *     row pitch (ld * element size) of a K-wide operand must be a multiple of
+ *     16 bytes.  Sizes may be 0 (nothing is written then).
  *   - Every argument check runs on the host before anything is enqueued; on
  *     error nothing is launched and no output is touched.  After the
  *     launches, a HIP launch error is reported as PDQ_ERR_HIP.
@@ -112,8 +114,8 @@ size_t pdq_act_bytes(int64_t M, int64_t K);
  * quantizer into the skinny kernel; pdq_linear_int8_outlier always runs the
  * tiled one).  Both give the same bits.  -1 when M < 1 or N < 1.
  *   PDQ_GEMM_SKINNY  one pass over the weight per 64 activation rows,
- *                    16 channels per workgroup (all M <= 64, and larger M
- *                    while that is estimated to be faster)
+ *                    16 or 32 channels per workgroup (all M <= 64, and
+ *                    larger M while that is estimated to be faster)
  *   PDQ_GEMM_TILED   256 x 256 output tiles staged through LDS
  */
 enum { PDQ_GEMM_SKINNY = 0, PDQ_GEMM_TILED = 1 };
@@ -172,7 +174,7 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
  * calibration did not cover; [LLM.int8] part 1 section 2 four-term expansion
  * reduced to a symmetric weight: acc' = acc - Z * colsum[n].
  *
- *   x          [M, K] of x_dt, row pitch ldx (any M; built for M <= 64)
+ *   x          [M, K] of x_dt, row pitch ldx (any M; decode batches are small)
  *   a_scale    S > 0 and finite; a_zp Z in [-128, 127] (host values, from
  *              pdq_calibrate_static)
  *   wq, w_scale, w_colsum  from pdq_quantize_weight (w_colsum required)

@@ -173,3 +173,64 @@ def test_unpack_weight_inverts_the_layout():
     image = pack_weight(codes)
     base = (1 * 2 + 1) * 1024 + 5 * 64 + 3 * 16
     assert image[base:base + 16].tolist() == list(range(1, 17))
+
+
+def pre_asym(L, x=P, dt=1, M=8, K=64, ldx=64, wq=P, ws=P, cs=P, bias=None, N=16, xq=P, xs=P, xz=P, y=P,
+             ldy=16, acc=None):
+    return L.pdq_linear_prefill_asym(x, dt, M, K, ldx, wq, ws, cs, bias, N, xq, xs, xz, y, ldy, acc, None)
+
+
+def test_prefill_asym_validation(L):
+    assert pre_asym(L, dt=9) == DTYPE
+    assert pre_asym(L, K=24, ldx=24) == SHAPE
+    assert pre_asym(L, ldy=8) == SHAPE
+    assert pre_asym(L, cs=None) == NULL        # the zero point needs the code sums
+    assert pre_asym(L, xz=None) == NULL
+    assert pre_asym(L, xs=None) == NULL
+    assert pre_asym(L, xq=None) == NULL
+    assert pre_asym(L, xz=P + 2) == ALIGN
+    assert pre_asym(L, M=0) == OK
+    q = L.pdq_quantize_per_token_asym
+    assert q(P, 1, 4, 64, 64, P, P, None, None) == NULL
+    assert q(P, 1, 4, 64, 64, P + 8, P, P, None) == ALIGN
+    g = L.pdq_gemm_per_token_asym
+    assert g(P, P, None, 4, 64, P, P, P, None, 16, P, 16, None, None) == NULL
+    assert g(P, P, P, 4, 64, P, P, None, None, 16, P, 16, None, None) == NULL
+    assert g(P, P, P, 0, 64, P, P, P, None, 16, P, 16, None, None) == OK
+
+
+def test_static_sym_validation(L):
+    lin = L.pdq_linear_static_sym
+
+    def call(x=P, dt=1, M=4, K=64, s=0.5, ws=P, xq=P, y=P, ldy=16, sat=None):
+        return lin(x, dt, M, K, K, s, P, ws, None, 16, xq, y, ldy, None, sat, None)
+
+    assert call(dt=4) == DTYPE
+    assert call(K=20) == SHAPE
+    assert call(ldy=3) == SHAPE
+    for s in (0.0, -2.0, float("inf"), float("nan")):
+        assert call(s=s) == UNSUP
+    assert call(ws=None) == NULL
+    assert call(xq=None) == NULL
+    assert call(sat=P + 1) == ALIGN
+    assert call(M=0) == OK
+    cal = L.pdq_calibrate_static_sym
+    assert cal(P, 1, 4, 64, 64, None, None, None) == NULL
+    assert cal(P, 1, 4, 64, 64, P, P + 2, None) == ALIGN
+    qs = L.pdq_quantize_static_sym
+    assert qs(P, 1, 4, 64, 64, 0.0, P, None, None) == UNSUP
+    assert qs(P, 1, 4, 64, 64, 1.0, None, None, None) == NULL
+    # the static GEMM needs code sums only for a nonzero zero point
+    gs = L.pdq_gemm_static
+    assert gs(P, 4, 64, 0.5, 3, P, P, None, None, 16, P, 16, None, None) == NULL
+    assert gs(P, 0, 64, 0.5, 0, P, P, None, None, 16, P, 16, None, None) == OK
+
+
+def test_gemm_kernel_choice(L):
+    k = L.pdq_gemm_kernel
+    assert k(0, 16) == -1 and k(16, 0) == -1
+    for m in (1, 17, 64):                       # decode batches: always the skinny kernel
+        assert k(m, 4096) == 0 and k(m, 28672) == 0
+    assert k(4096, 11008) == 1                  # the 7B prefill linear: tiled
+    assert k(8192, 4096) == 1
+    assert k(256, 4096) == 0                    # a few hundred rows of a 4096-wide weight
