@@ -190,13 +190,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
     // Outlier gather into X_out: lane j fetches x[row, idx[j]] (j < 64; the
     // index is clamped into the row, entries past the count are unset) while
     // the row is being quantized, and stores it, or the zero padding, once
-    // the count is known to fit.
+    // the count is known to fit.  The index and the count are loaded before
+    // the row, so that the dependent load of the value waits for them alone.
     const bool gather = SKIP && DT != kF32 && skip.xo != nullptr && skip.max_out > 0;
     const uint16_t* xr16 = reinterpret_cast<const uint16_t*>(xr);
-    int gidx = 0;
+    int gidx = 0, gcnt = 0;
     uint16_t gval = 0;
+    if (gather) {
+        gidx = skip.idx[min(lane, skip.max_out - 1)];
+        gcnt = *skip.count;
+    }
     auto gather_store = [&]() {
-        const int cnt = *skip.count;
+        const int cnt = gcnt;
         if (cnt > skip.max_out) return;
         uint16_t* xo_row = skip.xo + row * skip.P;
         const int used = (cnt + 15) / 16 * 16;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             }
             sk[i] = (FULL || c < nch) ? skip_mask<SKIP>(skip, min(c, nch - 1)) : 0u;
         }
-        if (gather) gidx = skip.idx[min(lane, skip.max_out - 1)];
+        if (gather) gval = xr16[min(max(gidx, 0), nch * 8 - 1)];
         float amax = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -234,7 +239,6 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             else
                 amax = chunk_absmax<DT>(raw[i], sk[i], amax);
         }
-        if (gather) gval = xr16[min(max(gidx, 0), nch * 8 - 1)];
         if constexpr (ASYM) {
             asym_grid(lo, hi);
         } else {
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
             s = absmax_step(amax);
         }
         const float inv = 1.0f / s;
-        if (gather) gval = xr16[min(max(skip.idx[min(lane, skip.max_out - 1)], 0), nch * 8 - 1)];
+        if (gather) gval = xr16[min(max(gidx, 0), nch * 8 - 1)];
         for (int c = lane; c < nch; c += 64) {
             const Raw8<DT> r = load_raw8<DT>(xr, c);
             const uint32_t m = skip_mask<SKIP>(skip, c);
