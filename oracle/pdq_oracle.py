@@ -157,20 +157,21 @@ def calibrate(batches):
     return state, s, z
 
 
-def quantize_static(x, s, z):
+def quantize_static(x, s, z, qmin=QMIN_ASYM):
     """q = clamp(rne(fl(x / S)) + Z, -128, 127); also counts saturations.
 
     [PDMIX-term] 2.3, decode formula; 2.4: static decode scales can saturate
     on out-of-distribution inputs, so the count of values whose unclamped
     code r' = rne(x/S) + Z falls outside [-128, 127] is returned.  The float
     quotient is limited to +-512 before conversion to an integer; this
-    changes neither the clamped code nor the saturation verdict.
+    changes neither the clamped code nor the saturation verdict.  qmin =
+    -127 gives the narrow range [-127, 127] of the zero-point grid below.
     """
     x = _f32(x)
     r = np.rint(x / F32(s))
     r = np.clip(r, -512, 512).astype(np.int64) + int(z)
-    sat = int(np.count_nonzero((r < QMIN_ASYM) | (r > QMAX_ASYM)))
-    return np.clip(r, QMIN_ASYM, QMAX_ASYM).astype(np.int8), sat
+    sat = int(np.count_nonzero((r < qmin) | (r > QMAX_ASYM)))
+    return np.clip(r, qmin, QMAX_ASYM).astype(np.int8), sat
 
 
 # ---------------------------------------------------------------------------
@@ -219,6 +220,54 @@ def linear_static_sym(x, s, wq, sw, bias=None):
     acc = int_matmul(xq, wq)
     assert np.all(np.abs(acc) < 2**31)
     return dict(xq=xq, sat=sat, acc=acc, y32=dequantize(acc, F32(s), sw, bias))
+
+
+# ---------------------------------------------------------------------------
+# Static tensor-wise zero-point quantization (254 levels)
+# ---------------------------------------------------------------------------
+
+def zeropoint_finalize(state):
+    """(S, Z) of the zero-point grid of [LLM.int8] part 1 section 2: the range
+    is spread over 2 * 127 steps, nd_x = 254 / (max - min), i.e. a step
+    S = (max - min) / 254, and the minimum lands on -127, so that codes fill
+    [-127, 127].  The page's own formulas for the zero point and the code are
+    garbled; taken here in the same form as the decode phase's grid (range
+    widened to contain 0, codes rne(x / S) + Z): Z = clamp(-127 - rne(lo /
+    S), -127, 127); S = 1 and Z = 0 for an empty range.
+    """
+    lo = min(F32(state[0]), F32(0))
+    hi = max(F32(state[1]), F32(0))
+    if hi == lo:
+        return F32(1), 0
+    s = F32(F32(hi - lo) / F32(2 * QMAX_SYM))
+    z = QMIN_SYM - int(np.rint(F32(lo / s)))
+    return s, int(min(max(z, QMIN_SYM), QMAX_SYM))
+
+
+def calibrate_zeropoint(batches):
+    state = None
+    for b in batches:
+        state = minmax_update(state, b)
+    s, z = zeropoint_finalize(state)
+    return state, s, z
+
+
+def quantize_zeropoint(x, s, z):
+    """q = clamp(rne(fl(x / S)) + Z, -127, 127) and the saturation count."""
+    return quantize_static(x, s, z, qmin=QMIN_SYM)
+
+
+def linear_zeropoint(x, s, z, wq, sw, colsum, bias=None):
+    """Static tensor-wise zero-point W8A8 linear: y = (S * S_w[n]) * (acc - Z * colsum[n]).
+
+    The GEMM removes the zero point through the weight code sums, the
+    four-term expansion of [LLM.int8] part 1 section 2 with a symmetric
+    weight.  Returns dict(xq, sat, acc (raw), y32).
+    """
+    xq, sat = quantize_zeropoint(x, s, z)
+    acc = int_matmul(xq, wq)
+    acc_c = zero_point_correct(acc, colsum, z)
+    return dict(xq=xq, sat=sat, acc=acc, y32=dequantize(acc_c, F32(s), sw, bias))
 
 
 # ---------------------------------------------------------------------------

@@ -349,6 +349,57 @@ def test_tensor_absmax_equals_per_token_when_rows_share_the_absmax():
 
 
 # ---------------------------------------------------------------------------
+# Static tensor-wise zero-point quantization (254 levels)
+# ---------------------------------------------------------------------------
+
+def check_zeropoint(oracle=O):
+    """Closed forms of the 254-step grid, derived by hand: the calibrated range
+    (widened to contain 0) spans 2 * 127 steps with its low end on -127."""
+    cases = [([-1, 0, 1, 2], 3, -42, [-1, 0, 1, 2, 3, -2], [-127, -42, 43, 127, 127, -127], 2),
+             ([0, 0.5, 1], 1, -127, [0, 0.5, 1], [-127, 0, 127], 0),
+             ([-2, -1], 2, 127, [-2, -1, 0], [-127, 0, 127], 0),
+             ([0, 0], None, 0, [0, 0], [0, 0], 0)]
+    for cal, width, z_want, x, q_want, sat_want in cases:
+        _, s, z = oracle.calibrate_zeropoint([np.array([cal], F32)])
+        assert z == z_want
+        if width is None:
+            assert s == 1
+        else:
+            assert abs(float(s) * 254 - width) <= width * 2.0**-23
+        q, sat = oracle.quantize_zeropoint(np.array([x], F32), s, z)
+        assert q.tolist() == [q_want] and sat == sat_want
+
+
+def test_zeropoint_closed_forms():
+    check_zeropoint()
+
+
+def test_zeropoint_symmetric_range_is_the_absmax_grid():
+    """Over a range symmetric about 0 the zero-point grid is the tensor-wise
+    absmax grid: S = 2c / 254 = c / 127 (both correctly rounded), Z = 0."""
+    x = synth.activations(70, 12, 96, [4], 10.0, dtype="f32")
+    c = float(np.abs(x).max())
+    x[0, 0], x[1, 1] = c, -c
+    _, s, z = O.calibrate_zeropoint([x])
+    _, s_abs = O.calibrate_absmax([x])
+    assert (s, z) == (s_abs, 0)
+    q, sat = O.quantize_zeropoint(x, s, z)
+    q_abs, sat_abs = O.quantize_static_sym(x, s_abs)
+    assert np.array_equal(q, q_abs) and sat == sat_abs == 0
+
+
+def test_zeropoint_error_bound_and_ends():
+    cal = [synth.activations(71 + b, 16, 128, [5], 30.0, offset=0.7, dtype="f32") for b in range(4)]
+    state, s, z = O.calibrate_zeropoint(cal)
+    xa = np.concatenate(cal)
+    q, sat = O.quantize_zeropoint(xa, s, z)
+    assert sat == 0
+    err = np.abs(np.float64(s) * (q.astype(np.int64) - z) - xa.astype(np.float64))
+    assert np.all(err <= np.float64(s) / 2 * (1 + 2.0**-18))
+    assert q.min() == -127 and q.max() == 127
+
+
+# ---------------------------------------------------------------------------
 # Per-token dynamic asymmetric quantization (the prefill formula with Z_token)
 # ---------------------------------------------------------------------------
 
@@ -549,6 +600,20 @@ def _static_sym_asym_clamp(x, s):
     return np.clip(r, -128, 127).astype(np.int8), int(np.count_nonzero((r < -128) | (r > 127)))
 
 
+def _zeropoint_255_levels(state):
+    """255 steps instead of 254."""
+    lo, hi = min(F32(state[0]), F32(0)), max(F32(state[1]), F32(0))
+    if hi == lo:
+        return F32(1), 0
+    s = F32(F32(hi - lo) / F32(255))
+    return s, int(min(max(-127 - int(np.rint(F32(lo / s))), -127), 127))
+
+
+def _zeropoint_wide_clamp(x, s, z):
+    """Clamped to [-128, 127]."""
+    return O.quantize_static(x, s, z)
+
+
 def _plus_zero_point_rows(acc, colsum, z):
     z = np.asarray(z, np.int64)
     if z.ndim == 0:
@@ -601,6 +666,9 @@ def _rowwise_over_all_columns(x, cols):
     (_Mutant(outlier_columns=_nonstrict_outliers), check_threshold_strict),
     (_Mutant(zero_point_correct=_plus_zero_point_rows), check_prefill_asym),
     (_Mutant(quantize_static_sym=_static_sym_asym_clamp), check_tensor_absmax),
+    (_Mutant(zeropoint_finalize=_zeropoint_255_levels,
+             calibrate_zeropoint=lambda b: (None, *_zeropoint_255_levels(O.calibrate(b)[0]))), check_zeropoint),
+    (_Mutant(quantize_zeropoint=_zeropoint_wide_clamp), check_zeropoint),
     (_Mutant(quantize_rows_asym=_asym_rows_unwidened), check_asym_rows),
     (_Mutant(quantize_rows_asym=_asym_rows_zero_point_sign), check_asym_rows),
 ])
