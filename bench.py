@@ -225,6 +225,12 @@ def bench_decode(args, torch, pdq, synth):
         s_sym_t = pdq.calibrate_static_sym(torch.from_numpy(c.calib(b)).to(torch.bfloat16).cuda(), mm_sym,
                                            finalize=b == c.n_calib - 1)
     s_sym = float(s_sym_t.item())
+    # and the 254-level zero-point grid's (S, Z)
+    mm_zp = pdq.minmax_state("cuda")
+    for b in range(c.n_calib):
+        zp_out = pdq.calibrate_zeropoint(torch.from_numpy(c.calib(b)).to(torch.bfloat16).cuda(), mm_zp,
+                                         finalize=b == c.n_calib - 1)
+    s_zp, z_zp = float(zp_out[0].item()), int(zp_out[1].item())
     wq0, ws, cs = pdq.quantize_weight(torch.from_numpy(c.w()).to(torch.bfloat16).cuda())
     nrot = 64  # 64 x 16.8 MB = 1.07 GB of INT8 weights
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
@@ -268,6 +274,12 @@ def bench_decode(args, torch, pdq, synth):
                       pdq._p(ws), None, N, pdq._p(xq), pdq._p(y), N, None, None, pdq._stream(x.device))
 
         ms_sym_g = graph_timed(call_sym, nrot, max(args.steps // 2, 10), stream)
+
+        def call_zp(i):
+            pdq._call("pdq_linear_zeropoint", pdq._p(x), pdq.BF16, m, K, K, s_zp, z_zp, pdq._p(wqs[i % nrot]),
+                      pdq._p(ws), pdq._p(cs), None, N, pdq._p(xq), pdq._p(y), N, None, None, pdq._stream(x.device))
+
+        ms_zp_g = graph_timed(call_zp, nrot, max(args.steps // 2, 10), stream)
         # algorithmic bytes: int8 W once, bf16 X, bf16 Y, w_scale + colsum
         call_bytes = N * K + 2 * m * K + 2 * m * N + 8 * N
         gemv_bytes = N * K + m * K + 2 * m * N + 8 * N
@@ -280,9 +292,9 @@ def bench_decode(args, torch, pdq, synth):
                            gemv_graph_frac=gemv_bytes / (ms_gemv_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            gemv_frac=gemv_bytes / (ms_gemv * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            saturated=nsat, saturated_frac=nsat / (m * K),
-                           us_call_static_sym_graph=ms_sym_g * 1e3)
+                           us_call_static_sym_graph=ms_sym_g * 1e3, us_call_zeropoint_graph=ms_zp_g * 1e3)
     del wqs
-    return dict(S=s, Z=z, S_sym=s_sym, K=K, N=N, per_batch=res)
+    return dict(S=s, Z=z, S_sym=s_sym, S_zp=s_zp, Z_zp=z_zp, K=K, N=N, per_batch=res)
 
 
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
@@ -520,7 +532,7 @@ def main():
                 f"{r['gemv_GBps']:.0f} GB/s; from a graph: call {r['us_call_graph']:.2f} us "
                 f"({r['call_graph_GBps']:.0f} GB/s), GEMV {r['us_gemv_graph']:.2f} us "
                 f"({r['gemv_graph_GBps']:.0f} GB/s); saturated {r['saturated']}; static symmetric call "
-                f"{r['us_call_static_sym_graph']:.2f} us")
+                f"{r['us_call_static_sym_graph']:.2f} us, zero-point call {r['us_call_zeropoint_graph']:.2f} us")
         llm = bench_llm_int8(args, torch, pdq, synth)
         log(f"[llm.int8] {llm['ms']*1e3:.1f} us, {llm['int8_tops']:.0f} TOPS, |O|={llm['n_outlier']}")
         blk = bench_block(args, torch, pdq, synth)
@@ -565,6 +577,7 @@ def main():
     }
     if dec:
         out["decode"] = {"unit": "GB/s", "peak": PEAK_HBM_GBS, "S": dec["S"], "Z": dec["Z"], "S_sym": dec["S_sym"],
+                         "S_zeropoint": dec["S_zp"], "Z_zeropoint": dec["Z_zp"],
                          "per_batch": {m: {k: round(v, 5) if isinstance(v, float) else v
                                            for k, v in r.items()} for m, r in dec["per_batch"].items()}}
     if llm:

@@ -226,6 +226,37 @@ pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64
                                  uint32_t* sat_count, void* stream);
 
 /*
+ * Static tensor-wise ZERO-POINT W8A8 with 254 levels: [LLM.int8] part 1
+ * section 2 zero-point quantization, nd_x = 2 * 127 / (max - min), taken
+ * tensor-wise with a static scale like the symmetric variant above.  The
+ * page's formulas for the zero point and the code are garbled; read in the
+ * decode grid's form: over the calibrated range [lo, hi] = [min(min, 0),
+ * max(max, 0)], S = (hi - lo) / 254 (1 if hi == lo), Z = clamp(-127 - rne(lo
+ * / S), -127, 127), codes clamp(rne(x / S) + Z, -127, 127); the GEMM removes
+ * Z through the weight code sums (the four-term expansion with a symmetric
+ * weight): y = bf16((S * S_w[n]) * (float)(acc - Z * colsum[n]) [+ bias[n]]).
+ *
+ * pdq_calibrate_zeropoint: the MinMax state as pdq_calibrate_static; a_scale
+ *   and a_zp (both or neither) receive the finalised (S, Z).
+ * pdq_quantize_zeropoint: xq packed (pdq_act_bytes(M, K) bytes); sat_count
+ *   (nullable) INCREMENTED by the number of rne(x / S) + Z outside [-127, 127].
+ * pdq_linear_zeropoint: quantizer + GEMM (one launch for M * K <= 8192);
+ *   w_colsum required; acc_out [M, N] int32 (raw acc) or NULL.
+ *   a_scale > 0 and finite and a_zp in [-127, 127], else PDQ_ERR_UNSUPPORTED.
+ */
+pdq_status pdq_calibrate_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   float* minmax, float* a_scale, int32_t* a_zp, void* stream);
+
+pdq_status pdq_quantize_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                  float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count, void* stream);
+
+pdq_status pdq_linear_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                float a_scale, int32_t a_zp, const int8_t* wq, const float* w_scale,
+                                const int32_t* w_colsum, const float* bias, int64_t N, int8_t* xq,
+                                uint16_t* y, int64_t ldy, int32_t* acc_out, uint32_t* sat_count,
+                                void* stream);
+
+/*
  * Prefill linear with per-token dynamic ASYMMETRIC activations: the
  * [PDMIX-term] 2.3 prefill formula taken with its per-token zero point
  * Z_token, Q = clamp(round(X / S_token) + Z_token, -128, 127), both computed

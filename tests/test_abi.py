@@ -234,3 +234,26 @@ def test_gemm_kernel_choice(L):
     assert k(4096, 11008) == 1                  # the 7B prefill linear: tiled
     assert k(8192, 4096) == 1
     assert k(256, 4096) == 0                    # a few hundred rows of a 4096-wide weight
+
+
+def test_zeropoint_validation(L):
+    lin = L.pdq_linear_zeropoint
+
+    def call(dt=1, M=4, K=64, s=0.5, z=-3, cs=P, xq=P, y=P, sat=None):
+        return lin(P, dt, M, K, K, s, z, P, P, cs, None, 16, xq, y, 16, None, sat, None)
+
+    assert call(dt=7) == DTYPE
+    assert call(K=40) == SHAPE
+    assert call(z=-128) == UNSUP            # the zero-point grid's codes stop at -127
+    assert call(z=128) == UNSUP
+    assert call(s=0.0) == UNSUP
+    assert call(cs=None) == NULL
+    assert call(xq=None) == NULL
+    assert call(sat=P + 1) == ALIGN
+    assert call(M=0) == OK
+    cal = L.pdq_calibrate_zeropoint
+    assert cal(P, 1, 4, 64, 64, P, P, None, None) == NULL    # scale without zero point
+    assert cal(P, 1, 4, 64, 64, None, None, None, None) == NULL
+    q = L.pdq_quantize_zeropoint
+    assert q(P, 1, 4, 64, 64, 1.0, 127, None, None, None) == NULL
+    assert q(P, 1, 4, 64, 64, 1.0, -128, P, None, None) == UNSUP

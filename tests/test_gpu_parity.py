@@ -310,6 +310,47 @@ def test_static_sym_linear(dtype, m, n, k):
         assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
 
 
+# ---------------------------------------------------------------------------
+# static tensor-wise zero-point grid (254 levels)
+# ---------------------------------------------------------------------------
+
+def test_zeropoint_calibration():
+    batches = [synth.activations(8100 + b, 64, 1024, [3, 700], 100.0, offset=0.4, dtype="bf16") for b in range(6)]
+    mm = pdq.minmax_state("cuda")
+    for i, xb in enumerate(batches):
+        out = pdq.calibrate_zeropoint(dev(xb, "bf16"), mm, finalize=i == len(batches) - 1)
+    _, s, z = O.calibrate_zeropoint(batches)
+    assert host(out[0]).view(np.uint32)[0] == np.array([s], F32).view(np.uint32)[0] and int(host(out[1])[0]) == z
+
+
+# One launch (M * K <= 8192), the skinny kernel (16 and 32 channels per
+# workgroup) and the tiled GEMM; decode values beyond the calibrated range
+# saturate at both ends.
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (4, 100, 2048), (37, 1000, 1040), (300, 4100, 1040),
+                                   (2048, 2600, 1040)])
+def test_zeropoint_linear(dtype, m, n, k):
+    cal = [synth.activations(8200 + b, 32, k, [2], 8.0, offset=0.5, dtype=dtype) for b in range(3)]
+    _, s, z = O.calibrate_zeropoint(cal)
+    x = synth.activations(8300 + m, m, k, [2, k - 5], 20.0, offset=0.5, dtype=dtype)
+    big = 3.0 * max(float(np.abs(c).max()) for c in cal)
+    x[0, 7], x[m - 1, 9] = big, -big
+    x = synth.round_to(x, dtype)
+    w = synth.weights(8400 + n, n, k, dtype)
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, dtype)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b = synth.bias(8500, n)
+    res = pdq.linear_zeropoint(dev(x, dtype), s, z, wq, ws, cs, torch.from_numpy(b).cuda(), sat_count=sat,
+                               want_acc=True)
+    ref = O.linear_zeropoint(x, F32(s), z, rq, rs, rc, b)
+    assert codes_equal(res["xq"], ref["xq"])
+    assert int(host(sat)[0]) == ref["sat"] > 0
+    assert np.array_equal(host(res["acc"]), ref["acc"])
+    check_16bit(host(res["y"]), ref["y32"], "bf16", exact=True)
+    if m * k > 8192:
+        assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
+
+
 @pytest.mark.parametrize("m,n,k", [(9, 300, 1040), (2048, 2600, 512)])
 def test_gemm_static_zero_point_zero_needs_no_colsum(m, n, k):
     """With Z = 0 the static GEMM takes no code sums, on either kernel."""

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     v4i xcode = v4i{};  // ONEROW: this lane's codes
     if constexpr (FUSED) {
         const float inv = 1.0f / a.s;
-        const int qmin = a.sym ? -127 : -128;
+        const int qmin = a.narrow ? -127 : -128;
         int nsat = 0;
 #pragma unroll
         for (int i = 0; i < kQ; ++i) {

@@ -385,7 +385,7 @@ pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64
         d.K = (int)K;
         d.s = a_scale;
         d.z = 0;
-        d.sym = 1;
+        d.narrow = 1;
         d.sw = w_scale;
         d.bias = bias;
         d.y = y;
@@ -401,6 +401,75 @@ pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64
     }
     PDQ_TRY(pdq_quantize_static_sym(x, x_dt, M, K, ldx, a_scale, xq, sat_count, stream));
     return pdq_gemm_static(xq, M, K, a_scale, 0, wq, w_scale, nullptr, bias, N, y, ldy, acc_out, stream);
+}
+
+pdq_status pdq_calibrate_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                   float* minmax, float* a_scale, int32_t* a_zp, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!minmax) return PDQ_ERR_NULL;
+    if ((a_scale == nullptr) != (a_zp == nullptr)) return PDQ_ERR_NULL;
+    if (!aligned(minmax, 4) || !aligned(a_scale, 4) || !aligned(a_zp, 4)) return PDQ_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    launch_minmax(x, x_dt, M, K, ldx, minmax, st);
+    if (a_scale) launch_zeropoint_finalize(minmax, a_scale, a_zp, st);
+    return launched();
+}
+
+pdq_status pdq_quantize_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                  float a_scale, int32_t a_zp, int8_t* xq, uint32_t* sat_count, void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -127 || a_zp > 127) return PDQ_ERR_UNSUPPORTED;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(sat_count, 4)) return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    launch_quant_static(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, static_cast<hipStream_t>(stream),
+                        true);
+    return launched();
+}
+
+pdq_status pdq_linear_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                                float a_scale, int32_t a_zp, const int8_t* wq, const float* w_scale,
+                                const int32_t* w_colsum, const float* bias, int64_t N, int8_t* xq,
+                                uint16_t* y, int64_t ldy, int32_t* acc_out, uint32_t* sat_count,
+                                void* stream) {
+    if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -127 || a_zp > 127) return PDQ_ERR_UNSUPPORTED;
+    if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
+    if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(acc_out, 4) || !aligned(sat_count, 4))
+        return PDQ_ERR_ALIGN;
+    if (N > 0 && decode_fusable(M, K)) {
+        DecodeArgs d{};
+        d.wq = wq;
+        d.M = (int)M;
+        d.N = (int)N;
+        d.K = (int)K;
+        d.s = a_scale;
+        d.z = a_zp;
+        d.narrow = 1;
+        d.sw = w_scale;
+        d.colsum = w_colsum;
+        d.bias = bias;
+        d.y = y;
+        d.ldy = ldy;
+        d.acc_out = acc_out;
+        d.x = x;
+        d.x_dt = x_dt;
+        d.ldx = ldx;
+        d.xq_out = xq;
+        d.sat = sat_count;
+        launch_decode_fused(d, static_cast<hipStream_t>(stream));
+        return launched();
+    }
+    PDQ_TRY(pdq_quantize_zeropoint(x, x_dt, M, K, ldx, a_scale, a_zp, xq, sat_count, stream));
+    return pdq_gemm_static(xq, M, K, a_scale, a_zp, wq, w_scale, w_colsum, bias, N, y, ldy, acc_out, stream);
 }
 
 pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,

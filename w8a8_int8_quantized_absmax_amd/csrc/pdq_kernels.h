@@ -34,11 +34,11 @@ void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t l
 void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
                             float* scale, int32_t* zp, hipStream_t st);
 
-// Static code: q = clamp(rne(x / s) + z, -128, 127) (sym: z = 0 and the
-// range [-127, 127]), packed, padding zeroed; saturation count added to *sat
+// Static code: q = clamp(rne(x / s) + z, -128, 127) (narrow: the range
+// [-127, 127]), packed, padding zeroed; saturation count added to *sat
 // (nullable).
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
-                         int8_t* q, uint32_t* sat, hipStream_t st, bool sym = false);
+                         int8_t* q, uint32_t* sat, hipStream_t st, bool narrow = false);
 
 // MinMax observer update of minmax[2]; optional finalisation to (S, Z).
 void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float* minmax,
@@ -46,6 +46,8 @@ void launch_minmax(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, flo
 void launch_minmax_finalize(const float* minmax, float* a_scale, int32_t* a_zp, hipStream_t st);
 // Tensor-wise absmax scale of the state: max(|min|, |max|) / 127 (1 if 0 or no value seen).
 void launch_absmax_finalize(const float* minmax, float* a_scale, hipStream_t st);
+// (S, Z) of the 254-step zero-point grid on [-127, 127] of the state's range.
+void launch_zeropoint_finalize(const float* minmax, float* a_scale, int32_t* a_zp, hipStream_t st);
 
 // gemm_i8.hip -------------------------------------------------------------
 struct GemmArgs {
@@ -96,7 +98,7 @@ struct DecodeArgs {
     int64_t ldx;
     int8_t* xq_out;  // packed activation codes, written by workgroup 0 (padding rows by others)
     uint32_t* sat;   // nullable saturation counter
-    int sym;         // symmetric static grid: z = 0, codes clamped to [-127, 127]
+    int narrow;      // codes clamped to [-127, 127] (symmetric or zero-point grid)
 };
 // Activations already quantized (xq); 16 or 32 channels per workgroup
 // (decode_wide_groups).

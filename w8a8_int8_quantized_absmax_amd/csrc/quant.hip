@@ -24,7 +24,8 @@
 //    k_minmax_finalize its (S, Z) (PDMIX usage guide, section 3), or the
 //                   tensor-wise absmax scale S = max(|min|, |max|) / 127 of
 //                   the static symmetric variant (LLM.int8() notes, part 1
-//                   section 1, with a static scale).
+//                   section 1, with a static scale), or the (S, Z) of the
+//                   254-step zero-point grid (same notes, section 2).
 //
 // Every division is the correctly rounded binary32 division and every
 // rounding to an integer is round-half-to-even (v_rndne_f32), so the codes
@@ -426,22 +427,27 @@ __global__ __launch_bounds__(256) void k_minmax(const void* __restrict__ x, int6
     }
 }
 
+// grid 0: the decode phase's asymmetric grid, 255 steps on [-128, 127];
+// 1: tensor-wise absmax, S = max(|min|, |max|) / 127 (1 before any value);
+// 2: the zero-point grid of 254 steps on [-127, 127].
 __global__ void k_minmax_finalize(const float* __restrict__ mm, float* __restrict__ s_out,
-                                  int32_t* __restrict__ z_out, int sym) {
+                                  int32_t* __restrict__ z_out, int grid) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    if (sym) {  // tensor-wise absmax: S = max(|min|, |max|) / 127; 1 before any value
+    if (grid == 1) {
         const float c = mm[0] > mm[1] ? 0.0f : fmaxf(fabsf(mm[0]), fabsf(mm[1]));
         *s_out = absmax_step(c);
         return;
     }
+    const int qmin = grid == 2 ? -127 : -128;
+    const float steps = grid == 2 ? 254.0f : 255.0f;
     const float lo = fminf(mm[0], 0.0f);
     const float hi = fmaxf(mm[1], 0.0f);
     float s = 1.0f;
     int z = 0;
     if (hi != lo) {
-        s = (hi - lo) / 255.0f;
-        z = -128 - (int)__builtin_rintf(lo / s);
-        z = min(max(z, -128), 127);
+        s = (hi - lo) / steps;
+        z = qmin - (int)__builtin_rintf(lo / s);
+        z = min(max(z, qmin), 127);
     }
     *s_out = s;
     *z_out = z;
@@ -482,9 +488,9 @@ void quant_static_dt(const void* x, int64_t M, int64_t ldb, int nch, int cpr, in
 }
 
 void launch_quant_static(const void* x, int dt, int64_t M, int64_t K, int64_t ldx, float s, int z,
-                         int8_t* q, uint32_t* sat, hipStream_t st, bool sym) {
+                         int8_t* q, uint32_t* sat, hipStream_t st, bool narrow) {
     if (M <= 0 || K <= 0) return;
-    const int qmin = sym ? -127 : -128;
+    const int qmin = narrow ? -127 : -128;
     const int nch = (int)(K / 8);
     const int cpr = (int)((K + kWTileK - 1) / kWTileK * 8);  // chunks per padded row
     const int64_t total = (M + kWGroup - 1) / kWGroup * kWGroup * cpr;
@@ -524,6 +530,10 @@ void launch_minmax_finalize(const float* mm, float* a_scale, int32_t* a_zp, hipS
 
 void launch_absmax_finalize(const float* mm, float* a_scale, hipStream_t st) {
     hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, nullptr, 1);
+}
+
+void launch_zeropoint_finalize(const float* mm, float* a_scale, int32_t* a_zp, hipStream_t st) {
+    hipLaunchKernelGGL(k_minmax_finalize, dim3(1), dim3(64), 0, st, mm, a_scale, a_zp, 2);
 }
 
 }  // namespace pdq

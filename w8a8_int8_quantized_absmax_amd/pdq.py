@@ -48,6 +48,10 @@ SIGNATURES = {
     "pdq_quantize_static_sym": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp, _vp]),
     "pdq_linear_static_sym": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _i64,
                                              _vp, _vp, _i64, _vp, _vp, _vp]),
+    "pdq_calibrate_zeropoint": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "pdq_quantize_zeropoint": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp]),
+    "pdq_linear_zeropoint": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp,
+                                            _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "pdq_weight_bytes": (_sz, [_i64, _i64]),
     "pdq_act_bytes": (_sz, [_i64, _i64]),
@@ -346,6 +350,44 @@ def linear_static_sym(x, a_scale: float, wq, w_scale, bias=None, sat_count=None,
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
     _call("pdq_linear_static_sym", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), _p(wq), _p(w_scale),
           _p(bias), n, _p(xq), _p(y), _ld(y), _p(acc), _p(sat_count), _stream(x.device))
+    return dict(y=y, xq=xq, acc=acc)
+
+
+def calibrate_zeropoint(x: torch.Tensor, minmax: torch.Tensor, finalize: bool = False):
+    """Update the MinMax state with batch x; if finalize, return the 254-level zero-point grid's (S, Z) device tensors."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    s = z = None
+    if finalize:
+        s = torch.empty(1, dtype=torch.float32, device=x.device)
+        z = torch.empty(1, dtype=torch.int32, device=x.device)
+    _call("pdq_calibrate_zeropoint", _p(x), _DT[x.dtype], m, k, _ld(x), _p(minmax), _p(s), _p(z),
+          _stream(x.device))
+    return (s, z) if finalize else None
+
+
+def quantize_zeropoint(x, a_scale: float, a_zp: int, xq=None, sat_count=None):
+    """Static tensor-wise zero-point INT8 (254 levels) -> xq packed Codes [M,K]."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    xq = _codes_out(xq, m, k, x.device)
+    _call("pdq_quantize_zeropoint", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp), _p(xq),
+          _p(sat_count), _stream(x.device))
+    return xq
+
+
+def linear_zeropoint(x, a_scale: float, a_zp: int, wq, w_scale, colsum, bias=None, sat_count=None,
+                     want_acc: bool = False, out=None, xq=None):
+    """Static tensor-wise zero-point W8A8 linear (254 levels) -> dict(y bf16, xq[, acc])."""
+    _check_mat(x, "x")
+    m, k = x.shape
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
+    xq = _codes_out(xq, m, k, x.device)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if want_acc else None
+    _call("pdq_linear_zeropoint", _p(x), _DT[x.dtype], m, k, _ld(x), float(a_scale), int(a_zp), _p(wq),
+          _p(w_scale), _p(colsum), _p(bias), n, _p(xq), _p(y), _ld(y), _p(acc), _p(sat_count), _stream(x.device))
     return dict(y=y, xq=xq, acc=acc)
 
 
