@@ -754,6 +754,26 @@ def test_per_token_rounding_near_ties():
     assert codes_equal(xq, q_ref)
 
 
+def test_per_token_asym_rounding_near_ties():
+    """Per-token asymmetric codes for values a few ulps around every half-step
+    of each token's own grid (the range ends placed in the row)."""
+    rows = []
+    for lo, hi in ((-1.0, 2.0), (0.0, 3.3), (-0.021, 0.0), (-5e4, 7e3), (-2.0, 2.0), (-0.7, 1e-3)):
+        lo, hi = F32(lo), F32(hi)
+        s = F32(F32(hi - lo) / F32(255))
+        v = _near_ties(s, 255)
+        v = v[(v > lo) & (v < hi)]
+        row = np.zeros(4096, F32)
+        row[: v.size] = v[:4094]
+        row[-2], row[-1] = lo, hi
+        rows.append(row)
+    x = np.stack(rows)
+    xq, xs, xz = pdq.quantize_per_token_asym(dev(x, "f32"))
+    q_ref, s_ref, z_ref = O.quantize_rows_asym(x)
+    assert np.array_equal(host(xs), s_ref) and np.array_equal(host(xz), z_ref)
+    assert codes_equal(xq, q_ref)
+
+
 @pytest.mark.parametrize("s", [0.5, 3.3963, 17.25, 1e-3])
 def test_decode_fused_rounding_near_ties(s):
     # the same tie-straddling inputs through the one-launch decode path (16 rows

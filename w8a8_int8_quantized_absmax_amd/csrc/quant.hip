@@ -131,6 +131,36 @@ __device__ __forceinline__ uint2 chunk_codes_absmax(const Raw8<DT>& r, uint32_t 
     return make_uint2(__builtin_amdgcn_perm(t1, t0, 0x05040100u), __builtin_amdgcn_perm(t3, t2, 0x05040100u));
 }
 
+// Codes of one chunk on a row's own asymmetric grid: clamp(rne(fl(x / s)) +
+// z, -128, 127), where every value of the row lies in the grid's range, so
+// |x / s| <= 255.  Same single-FMA rounding as chunk_codes_absmax: x * inv is
+// within 2^-23 |x / s| <= 2^-15 of x / s and fl(x / s) within 2^-16, so
+// rounding x * inv gives rne(fl(x / s)) unless x * inv lies within 2^-14 of a
+// half-integer; when any value of the wavefront is within 2^-13, the chunk
+// takes the correctly rounded division.  The integer is read from b's
+// encoding (b - 1.5 * 2^23 in two's complement), then z added and clamped.
+template <int DT>
+__device__ __forceinline__ uint2 chunk_codes_asym(const Raw8<DT>& r, float s, float inv, int z) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    float v[8], b[8];
+    widen8<DT>(r, v);
+    float dmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        b[j] = __builtin_fmaf(v[j], inv, kMagic);
+        dmax = fmaxf(dmax, fabsf(__builtin_fmaf(v[j], inv, -(b[j] - kMagic))));
+    }
+    if (__builtin_expect(__any(dmax >= 0.5f - 0x1p-13f), 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = v[j] / s + kMagic;  // exact: |v / s| <= 256
+    }
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        c[j] = min(max((int)(__float_as_uint(b[j]) - __float_as_uint(kMagic)) + z, -128), 127);
+    return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+}
+
 // One wavefront per row.  CPL > 0: each lane keeps CPL chunks of 8 elements
 // in registers (one HBM read), issued together and unconditionally (FULL: the
 // row is exactly CPL wavefront-wide chunks; otherwise lanes past the row
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
         return;
     }
-    int csum = 0, zq = 0, nsat = 0;
+    int csum = 0, zq = 0;
     float s;
     // The asymmetric grid of a row's range [lo, hi] (both already widened to
     // contain 0): S = fl(fl(hi - lo) / 255), 1 for an empty range;
@@ -174,11 +204,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         s = hi == lo ? 1.0f : (hi - lo) / 255.0f;
         zq = hi == lo ? 0 : min(max(-128 - (int)__builtin_rintf(lo / s), -128), 127);
     };
-    auto asym_codes = [&](const Raw8<DT>& r, float inv) {
-        float v[8];
-        widen8<DT>(r, v);
-        return static_codes8(v, s, inv, zq, nsat);
-    };
+    auto asym_codes = [&](const Raw8<DT>& r, float inv) { return chunk_codes_asym<DT>(r, s, inv, zq); };
     auto range8 = [&](const Raw8<DT>& r, float& lo, float& hi) {
         float v[8];
         widen8<DT>(r, v);
