@@ -31,7 +31,7 @@ multiply-add: t = fl(S_x * S_w), y = fl(t * fl(float(acc'))), then
 fl(y + bias).  The 16-bit side product of the outlier decomposition is
 evaluated in binary64.
 
-Readings where the pages are silent or garbled (each listed in the design doc):
+Readings where the pages are silent or garbled:
   * round() is round-half-to-even (np.rint);
   * symmetric codes are clamped to [-127, 127] ([LLM.int8] part 1 section 1
     gives that range); asymmetric codes to [-128, 127] ([PDMIX-term] 2.3);
