@@ -198,10 +198,10 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
 /*
  * Static tensor-wise SYMMETRIC W8A8: [LLM.int8] part 1 section 1 absmax
  * quantization, one scale for the whole activation tensor (section 3,
- * tensor-wise), measured offline over calibration batches -- the
- * "traditional W8A8 static quantization" with static activation parameters
- * that [PDMIX-term] section 2 sets PDMIX against.  Same kernels as the decode
- * linear with Z = 0 and the symmetric code range.
+ * tensor-wise), measured offline over calibration batches: the conventional
+ * static W8A8 scheme, with static activation scales, that [PDMIX-term]
+ * section 2 compares PDMIX with.  Same kernels as the decode linear with
+ * Z = 0 and the symmetric code range.
  *
  * pdq_calibrate_static_sym: updates the same MinMax state as
  *   pdq_calibrate_static (minmax[2] in/out, initialise to {+INF, -INF});

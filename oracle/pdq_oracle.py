@@ -185,8 +185,9 @@ def absmax_finalize(state):
     [LLM.int8] part 1 section 1: absmax quantization maps the tensor's
     largest magnitude onto 127, one scale for the whole tensor by default
     (section 3, tensor-wise); taken here with static activation parameters,
-    measured offline over calibration batches (the "traditional W8A8 static
-    quantization" that [PDMIX-term] section 2 sets PDMIX against).
+    measured offline over calibration batches: the conventional static W8A8
+    scheme, with static activation scales, that [PDMIX-term] section 2
+    compares PDMIX with.
     """
     if F32(state[0]) > F32(state[1]):  # no value seen yet
         return F32(1)
