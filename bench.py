@@ -363,6 +363,51 @@ def bench_sweep(args, torch, pdq, synth):
     return dict(S=s, Z=z, K=K, N=N, per_m=rows)
 
 
+TILE_SWEEP_N = (8192, 9216, 10240, 11008, 12288)
+
+
+def bench_tile_sweep(args, torch, pdq, synth):
+    """The prefill INT8 GEMM (M = K = 4096, the prefill workload's codes) at several
+    N: 512 .. 768 tiles of 256 x 256, i.e. 2 .. 3 rounds of one tile per CU on the
+    256 CUs.  Each N is timed with HIP events over 60 launches rotating 4 weight
+    copies, once with N rising and once with N falling (the clock drifts with the
+    board's thermal state)."""
+    c = synth.Prefill7B()
+    M, K = c.M, c.K
+    x = torch.from_numpy(c.x()).to(torch.bfloat16).cuda()
+    w_host = torch.from_numpy(c.w()).to(torch.bfloat16)
+    nmax = max(TILE_SWEEP_N)
+    reps = -(-nmax // w_host.shape[0])
+    w_all = torch.cat([w_host] * reps, 0)[:nmax].cuda()  # rows repeat: same distribution
+    xq = torch.empty(pdq.act_bytes(M, K), dtype=torch.int8, device="cuda")
+    xsc = torch.empty(M, dtype=torch.float32, device="cuda")
+    pdq.quantize_per_token(x, xq=xq, x_scale=xsc)
+    xqs = [xq] + [xq.clone() for _ in range(3)]
+    stream = torch.cuda.current_stream()
+    weights = {}
+    for n in TILE_SWEEP_N:
+        wq0, wsc, _ = pdq.quantize_weight(w_all[:n].contiguous())
+        weights[n] = ([wq0] + [wq0.clone() for _ in range(3)], wsc)
+    rows = {}
+    for direction, order in (("up", TILE_SWEEP_N), ("down", TILE_SWEEP_N[::-1])):
+        for n in order:
+            wqs, wsc = weights[n]
+            y = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+
+            def gemm(i):
+                r = i % 4
+                pdq._call("pdq_gemm_per_token", pdq._p(xqs[r]), pdq._p(xsc), M, K, pdq._p(wqs[r]),
+                          pdq._p(wsc), None, n, pdq._p(y), n, None, pdq._stream(x.device))
+
+            us = timed(gemm, 60, 10, stream) * 1e3
+            tiles = -(-M // 256) * -(-n // 256)
+            r = rows.setdefault(str(n), {"tiles": tiles, "rounds": round(tiles / 256, 4)})
+            r["us_" + direction] = round(us, 2)
+            r["TOPS_" + direction] = round(2.0 * M * n * K / (us * 1e-6) / 1e12, 1)
+            log(f"[tile sweep] N={n} ({tiles} tiles, {tiles / 256:.3f} rounds) {direction}: {us:.1f} us")
+    return dict(M=M, K=K, per_n=rows)
+
+
 def bench_block(args, torch, pdq, synth):
     """The decoder-block linear set (QKV 4096->12288, O 4096->4096, gate+up
     4096->28672, down 14336->4096), one shared INT8 weight copy per linear:
@@ -484,10 +529,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)  # ~13 ms of prefill steps: the clock settles first
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="prefill: the headline line without the other workloads; decode: only the decode "
+                         "measurements, in a line of their own (for counter collection)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline run: the per-token vs static C_s / C_g sweep over "
                          "M on the decode linear (one JSON line of its own)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead of the headline run: the prefill INT8 GEMM at N = 8192 .. 12288 "
+                         "(2 .. 3 rounds of 256 x 256 tiles on 256 CUs), one JSON line of its own")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run a fill and a plain device copy of this many MiB (known HBM "
                          "traffic, for scaling hardware byte counters)")
@@ -511,6 +561,13 @@ def main():
                                      "M": list(SWEEP_M)},
                           "S": sw["S"], "Z": sw["Z"], "per_m": sw["per_m"]}), flush=True)
         return
+    if args.tile_sweep:
+        ts = bench_tile_sweep(args, torch, pdq, synth)
+        print(json.dumps({"metric": "gemm_us_vs_tiles", "unit": "us", "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": "prefill INT8 GEMM 4096 x 4096 -> N, per-token codes",
+                                     "M": ts["M"], "K": ts["K"], "N": list(TILE_SWEEP_N)},
+                          "per_n": ts["per_n"]}), flush=True)
+        return
     if args.copy_probe:
         # known traffic: the fill kernel writes size bytes, the copy kernel
         # reads size bytes and writes size bytes (far more than the 256 MB MALL)
@@ -522,6 +579,12 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    if args.only == "decode":
+        dec = bench_decode(args, torch, pdq, synth)
+        print(json.dumps({"metric": "decode GB/s", "unit": "GB/s", "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": "decode linear 4096 -> 4096, static per-tensor INT8"},
+                          "decode": dec}), flush=True)
+        return
     pre = bench_prefill(args, torch, pdq, synth)
     log(f"[prefill] step {pre['ms_step']*1e3:.1f} us (quant {pre['ms_quant']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm']*1e3:.1f} us = {pre['gemm_tops']:.0f} TOPS)")

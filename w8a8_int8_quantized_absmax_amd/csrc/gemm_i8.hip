@@ -396,7 +396,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         convert(std::false_type{});
     __syncthreads();
     // 256 rows x 32 chunks of 8 outputs; consecutive threads take consecutive
-    // chunks of a row.
+    // chunks of a row.  A chunk is read as two 8-byte halves; 32 lanes (one
+    // row, 512 bytes) share one pass over the 64 banks, so lanes 16..31 of each
+    // half-wave read their upper half first: lanes j and j + 16 then hit
+    // banks 4j, 4j + 1 and 4j + 2, 4j + 3 instead of the same pair.
     uint16_t* y = static_cast<uint16_t*>(a.y);
     const bool vec = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (a.ldy % 8 == 0);
 #pragma unroll 4
@@ -405,7 +408,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         const int m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
         const uint2* src = reinterpret_cast<const uint2*>(yrow(ml) + nl * 2);
-        const uint2 lo = src[0], hi = src[1];
+        const int first = (c >> 4) & 1;
+        const uint2 p0 = src[first], p1 = src[first ^ 1];
+        const uint2 lo = first ? p1 : p0, hi = first ? p0 : p1;
         uint16_t* dst = y + (size_t)m * a.ldy + n;
         if (vec && n + 8 <= N) {
             *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
