@@ -20,6 +20,9 @@ in the order the pages give them.  Sources (cited by title and section):
                 (four-term expansion), section 3 granularity; part 2
                 "vector-wise quantization", the four-step flow (1)-(4), the
                 "16-bit decomposition" and "mixed-precision decomposition".
+  [HW-accel]    "Hardware acceleration of quantized operations" (apxml
+                course, chapter 2): the role of compilers and runtime
+                libraries (kernel fusion).
 
 Precision.  The quantization decisions (scales, integer codes, zero point)
 are taken in IEEE binary32 exactly as written: S = fl(C / 127) with a
@@ -454,6 +457,82 @@ def linear_int8_outlier(x, w16, wq, sw, threshold, bias=None):
     if bias is not None:
         y = y + _f32(bias).astype(np.float64)[None, :]
     return dict(cols=cols, xq=xq, x_scale=sx, acc=acc, y64=y)
+
+
+# ---------------------------------------------------------------------------
+# Fused producer: SiLU(gate) * up, then per-token INT8
+# ---------------------------------------------------------------------------
+
+def silu(g) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + e^-g) in binary64, no rounding to a
+    narrower type.
+
+    The pages define no activation function; this is the textbook SiLU (the
+    gate of a SwiGLU MLP, whose product with the up projection is the input
+    of the down projection).  The pages ask for the quantizer to be fused
+    into the kernel that produces its input ([HW-accel], the role of
+    compilers and runtime libraries: kernel fusion to cut memory traffic and
+    launches).  For g -> -inf, e^-g overflows to inf and the quotient is -0,
+    the limit of g * sigmoid(g).
+    """
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """Round binary64 values straight to bfloat16 (nearest, ties to even),
+    returned as binary32 (every bfloat16 value is one).
+
+    bfloat16 has 8 significant bits and binary32's exponent range: a value
+    m * 2^e (0.5 <= |m| < 1) is rounded to a multiple of 2^(e - 8); below the
+    smallest normal 2^-126 the spacing stays 2^-133.  One rounding from the
+    binary64 value: rounding to binary32 first and then to bfloat16 would
+    round twice and can land on the wrong side of a tie.  Values that round
+    beyond the largest bfloat16 become infinite.
+    """
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)
+    ex = np.maximum(e, -125)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.ldexp(np.rint(np.ldexp(v, 8 - ex)), ex - 8)
+        r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
+    return r.astype(F32)
+
+
+def silu_mul(gate, up, dtype="bf16") -> np.ndarray:
+    """h = SiLU(gate) * up, evaluated in binary64 and rounded once to the
+    producer's 16-bit type ("bf16" or "f16"); returned as binary32.
+
+    Reading: the fused kernel hands the quantizer the same h that an unfused
+    SiLU-and-multiply kernel would have written to memory in the model's
+    16-bit type, so that fusing changes where h lives (registers instead of
+    HBM), not the codes.
+    """
+    v = silu(gate) * np.asarray(up, np.float64)
+    if dtype == "f16":
+        return v.astype(np.float16).astype(F32)
+    return round_to_bf16(v)
+
+
+def silu_mul_quantize_per_token(gate, up, dtype="bf16"):
+    """SiLU(gate) * up quantized per token: returns (h, q, S).
+
+    The per-token dynamic symmetric quantizer of prefill ([PDMIX-term] 2.3)
+    applied to the fused producer's output h (see silu_mul).
+    """
+    h = silu_mul(gate, up, dtype)
+    q, s = quantize_rows_absmax(h)
+    return h, q, s
+
+
+def linear_prefill_silu_mul(gate, up, wq, sw, bias=None, dtype="bf16"):
+    """Prefill linear whose input is SiLU(gate) * up (a down projection):
+    returns dict(h, xq, x_scale, acc, y32)."""
+    h, xq, sx = silu_mul_quantize_per_token(gate, up, dtype)
+    acc = int_matmul(xq, wq)
+    assert np.all(np.abs(acc) < 2**31)
+    return dict(h=h, xq=xq, x_scale=sx, acc=acc, y32=dequantize(acc, sx, sw, bias))
 
 
 # ---------------------------------------------------------------------------

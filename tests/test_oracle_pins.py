@@ -7,7 +7,10 @@ Python integers/floats on tiny inputs.  The last block plants plausible
 mistakes into a copy of the oracle and shows that a pin catches each one.
 """
 import json
+import math
 import os
+from decimal import Decimal, localcontext
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -568,6 +571,152 @@ def test_outlier_decomposition_reconstructs_matmul():
 
 
 # ---------------------------------------------------------------------------
+# Fused SiLU * up producer: pinned to an exact evaluation of the definition
+# (decimal exponential, correctly rounded at 60 digits, then an exact
+# rational rounding to the 16-bit type) -- no numpy in the reference path
+# ---------------------------------------------------------------------------
+
+def _exact_round(v: Fraction, sig: int, emin: int, emax: int, near=None) -> float:
+    """Round an exact rational to a binary format with `sig` significant bits,
+    smallest normal 2^emin and largest finite value below 2^emax, ties to even.
+    near: a list that receives whether v lies within 2^-50 |v| of a tie (where
+    a binary64 evaluation may round either way)."""
+    if v == 0:
+        if near is not None:
+            near.append(False)
+        return 0.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^(e-1) <= a < 2^(e+1)
+    if Fraction(2) ** e <= a:
+        e += 1                                                 # now 2^(e-1) <= a < 2^e
+    e = max(e, emin + 1)                                       # subnormals keep the smallest spacing
+    step = Fraction(2) ** (e - sig)
+    q = a / step
+    n = q.numerator // q.denominator
+    rem = q - n
+    if near is not None:
+        near.append(abs(rem - Fraction(1, 2)) * step <= a / 2 ** 50)
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * step
+    out = math.inf if r >= Fraction(2) ** emax else float(r)
+    return out if v > 0 else -out
+
+
+def _exact_bf16(v: Fraction, near=None) -> float:
+    return _exact_round(v, 8, -126, 128, near)
+
+
+def _exact_f16(v: Fraction, near=None) -> float:
+    return _exact_round(v, 11, -14, 16, near)
+
+
+def _silu_mul_exact(g: float, u: float, rnd=_exact_bf16, near=None) -> float:
+    """SiLU(g) * u rounded once to the 16-bit type.  SiLU(g) is transcendental
+    for g != 0, so the exact product is never a tie, but it can lie closer to
+    one than binary64 resolves (SiLU(g) = g to binary64 precision for g > 37),
+    which `near` reports."""
+    with localcontext() as ctx:
+        ctx.prec = 60
+        G, U = Decimal(float(g)), Decimal(float(u))
+        if G < -10000:  # |SiLU(g) * u| < 10^-4000: zero with the product's sign
+            if near is not None:
+                near.append(False)
+            return math.copysign(0.0, -float(u))
+        return rnd(Fraction(G / (1 + (-G).exp()) * U), near)
+
+
+def _agree_off_ties(got, g, u, rnd):
+    """got equals the exactly rounded SiLU(g) * u, except within binary64's
+    resolution of a tie, where it must be one of the two neighbours."""
+    for a, b, x in zip(g, u, got):
+        near = []
+        want = _silu_mul_exact(a, b, rnd, near)
+        if near[0]:
+            lo = _silu_mul_exact(a, float(b) * (1 - 2.0 ** -40), rnd)
+            hi = _silu_mul_exact(a, float(b) * (1 + 2.0 ** -40), rnd)
+            assert x in (lo, hi), (a, b, x, lo, hi)
+        else:
+            assert x == want, (a, b, x, want)
+
+
+def _bf16_values(rng, n, lo_exp, hi_exp):
+    """Random bfloat16 values (as float32) with magnitudes 2^[lo_exp, hi_exp), both signs."""
+    mag = 2.0 ** rng.uniform(lo_exp, hi_exp, n) * rng.choice([-1.0, 1.0], n)
+    return O.bf16_bits_to_f32(O.to_bf16_bits(mag.astype(np.float32)))
+
+
+def _double_rounding_cases(n=2_000_000, seed=11):
+    """(g, u) pairs whose binary64 product SiLU(g) * u lies within half a
+    binary32 unit of a bfloat16 tie: rounding to binary32 first lands on the
+    tie, so only a single rounding gets them right."""
+    rng = np.random.default_rng(seed)
+    g = _bf16_values(rng, n, -4, 4).astype(np.float64)
+    u = _bf16_values(rng, n, -4, 4).astype(np.float64)
+    v = g / (1.0 + np.exp(-g)) * u
+    m, e = np.frexp(v)
+    t = np.ldexp(v, 8 - e)                  # bfloat16 units
+    dist = np.abs(t - np.floor(t) - 0.5)    # distance to a tie, in bfloat16 units
+    pick = np.nonzero(dist < 2.0 ** -17)[0]
+    return g[pick], u[pick]
+
+
+def check_silu_mul(oracle=O):
+    rng = np.random.default_rng(5)
+    g = np.concatenate([_bf16_values(rng, 150, -6, 7), [0.0, -0.0, 1.0, -1.0, 88.0, -88.0, 100.0, -100.0,
+                                                         1000.0, -1000.0, 3.0e38, -3.0e38]])
+    u = np.concatenate([_bf16_values(rng, 150, -6, 7), [2.5, 1.0, 1.0, 1.0, -1.5, 1.0, 1.0, 3.0,
+                                                         1.0, 7.0, 1.0, 0.5]])
+    dg, du = _double_rounding_cases()
+    assert len(dg) >= 3
+    g = np.concatenate([g, dg[:40]]).astype(np.float32)
+    u = np.concatenate([u, du[:40]]).astype(np.float32)
+    _agree_off_ties(oracle.silu_mul(g[None, :], u[None, :])[0], g, u, _exact_bf16)
+    _agree_off_ties(oracle.silu_mul(g[None, :150], u[None, :150], "f16")[0], g[:150], u[:150], _exact_f16)
+
+
+def test_silu_mul_is_the_exactly_rounded_definition():
+    check_silu_mul()
+
+
+def test_silu_textbook_values():
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(1.0) - 0.7310585786300049) < 1e-16      # sigmoid(1)
+    assert abs(O.silu(-1.0) + 0.2689414213699951) < 1e-16     # -sigmoid(-1)
+    x = np.linspace(-30, 30, 601)
+    assert np.allclose(O.silu(x) - O.silu(-x), x, rtol=1e-15, atol=1e-14)   # sigmoid(x) + sigmoid(-x) = 1
+    assert O.silu(1000.0) == 1000.0 and O.silu(-1000.0) == 0.0 and math.copysign(1, O.silu(-1000.0)) < 0
+
+
+def test_round_to_bf16_ties_ranges_and_double_rounding():
+    r = O.round_to_bf16
+    assert r(1.0) == 1.0 and r(1.0 + 2 ** -7) == 1.0 + 2 ** -7
+    assert r(1.0 + 2 ** -8) == 1.0                        # tie -> even
+    assert r(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6          # tie -> even (upwards)
+    assert r(1.0 + 2 ** -8 + 2 ** -40) == 1.0 + 2 ** -7   # just past the tie: a binary32 detour would say 1.0
+    assert r(2.0 ** -133) == 2.0 ** -133 and r(2.0 ** -134) == 0.0 and r(3 * 2.0 ** -134) == 2.0 ** -132
+    big = (2 - 2 ** -7) * 2.0 ** 127
+    assert r(big) == np.float32(big) and r(2.0 ** 128) == np.inf and r(-(2.0 ** 128)) == -np.inf
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(20000) * 2.0 ** rng.integers(-60, 60, 20000)).astype(np.float32)
+    assert np.array_equal(r(v.astype(np.float64)).view(np.uint32) >> 16, O.to_bf16_bits(v).astype(np.uint32))
+
+
+def test_silu_mul_quantize_error_bound():
+    rng = np.random.default_rng(8)
+    g = _bf16_values(rng, 4 * 96, -3, 3).reshape(4, 96)
+    u = _bf16_values(rng, 4 * 96, -3, 3).reshape(4, 96)
+    h, q, s = O.silu_mul_quantize_per_token(g, u)
+    for hr, gr, ur in zip(h, g, u):
+        _agree_off_ties(hr, gr, ur, _exact_bf16)
+    want = h
+    c = np.max(np.abs(want.astype(np.float64)), axis=1)
+    assert np.all(np.max(np.abs(q.astype(np.int32)), axis=1) == 127)
+    assert np.all(np.abs(want - q * s[:, None].astype(np.float64)) <= s[:, None] / 2 * (1 + 1e-6))
+    assert np.allclose(s, c / 127, rtol=2 ** -23)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: a copy of the oracle with one plausible error each
 # ---------------------------------------------------------------------------
 
@@ -658,7 +807,25 @@ def _rowwise_over_all_columns(x, cols):
     return q, s
 
 
+def _silu_mul_flipped_sigmoid(g, u, dtype="bf16"):
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return O.round_to_bf16(g / (1.0 + np.exp(g)) * np.asarray(u, np.float64))
+
+
+def _silu_mul_without_up(g, u, dtype="bf16"):
+    return O.round_to_bf16(O.silu(g))
+
+
+def _silu_mul_via_binary32(g, u, dtype="bf16"):
+    v = (O.silu(g) * np.asarray(u, np.float64)).astype(np.float32)
+    return O.bf16_bits_to_f32(O.to_bf16_bits(v))
+
+
 @pytest.mark.parametrize("mutant,check", [
+    (_Mutant(silu_mul=_silu_mul_flipped_sigmoid), check_silu_mul),
+    (_Mutant(silu_mul=_silu_mul_without_up), check_silu_mul),
+    (_Mutant(silu_mul=_silu_mul_via_binary32), check_silu_mul),
     (_Mutant(quantize_rows_absmax=_half_up_rows), check_worked_row),
     (_Mutant(quantize_rows_absmax=_truncating_rows), check_worked_row),
     (_Mutant(zero_point_correct=_plus_zero_point), check_four_term),
