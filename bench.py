@@ -17,7 +17,9 @@ copies so that no cache serves them), and the LLM.int8() decomposition
 2048 x (8192 -> 28672) in fp16 with threshold 6.0; and under "decoder_block"
 the block's four linears (QKV, O, gate+up, down at hidden 4096) on one shared
 INT8 weight copy each: a prefill pass over 8192 tokens and 256 decode steps
-at batch 32.
+at batch 32; under "silu_mul_quant" the down projection's input SiLU(gate) * up
+(8192 x 14336) quantized by the fused kernel, against the unfused pair, and the
+whole down projection.
 
 cpu_baseline: the CPU oracle timed on the host on the same prefill workload.
 
@@ -363,6 +365,47 @@ def bench_sweep(args, torch, pdq, synth):
     return dict(S=s, Z=z, K=K, N=N, per_m=rows)
 
 
+def bench_silu_mul(args, torch, pdq, synth):
+    """The down projection's input of the decoder block: h = SiLU(gate) * up over
+    8192 tokens x 14336, quantized per token by the fused kernel (gate and up
+    read once, codes written, h never stored), against the same result formed
+    unfused (torch's SiLU and multiply writing bf16 h, then the library's
+    per-token quantizer reading it back), and the whole down projection
+    (fused quantizer + INT8 GEMM 14336 -> 4096)."""
+    c = synth.DecoderBlock()
+    g, u = c.down_gate_up()
+    M, K = g.shape
+    gu = torch.from_numpy(np.concatenate([g, u], axis=1)).to(torch.bfloat16).cuda()  # [M, 2K]
+    del g, u
+    gate, up = gu[:, :K], gu[:, K:]
+    _, n_down, _ = c.linears[3]
+    wq, ws, _ = pdq.quantize_weight(torch.from_numpy(c.w(3)).to(torch.bfloat16).cuda())
+    xq = pdq.Codes.empty(M, K, "cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, n_down), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    dv = pdq._stream(gu.device)
+
+    def fused(i):
+        pdq._call("pdq_silu_mul_quantize_per_token", pdq._p(gate), pdq._p(up), pdq.BF16, M, K, 2 * K, 2 * K,
+                  pdq._p(xq), pdq._p(xs), None, 0, dv)
+
+    def unfused(i):
+        h = torch.nn.functional.silu(gate) * up
+        pdq._call("pdq_quantize_per_token", pdq._p(h), pdq.BF16, M, K, K, pdq._p(xq), pdq._p(xs), dv)
+
+    def linear(i):
+        pdq._call("pdq_linear_prefill_silu_mul", pdq._p(gate), pdq._p(up), pdq.BF16, M, K, 2 * K, 2 * K,
+                  pdq._p(wq), pdq._p(ws), None, n_down, pdq._p(xq), pdq._p(xs), pdq._p(y), n_down, None, dv)
+
+    ms_fused = timed(fused, 20, 5, stream)
+    ms_unfused = timed(unfused, 10, 3, stream)
+    ms_linear = timed(linear, 10, 3, stream)
+    nbytes = 2 * M * K * 2 + M * K + 4 * M
+    return dict(M=M, K=K, N=n_down, ms_fused=ms_fused, ms_unfused=ms_unfused, ms_linear=ms_linear,
+                bytes=nbytes, ops=2.0 * M * n_down * K)
+
+
 TILE_SWEEP_N = (8192, 9216, 10240, 11008, 12288)
 
 
@@ -529,9 +572,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)  # ~13 ms of prefill steps: the clock settles first
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "silu"], default="all",
                     help="prefill: the headline line without the other workloads; decode: only the decode "
-                         "measurements, in a line of their own (for counter collection)")
+                         "measurements, in a line of their own (for counter collection); silu: only the "
+                         "fused SiLU*up quantizer and its down projection")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline run: the per-token vs static C_s / C_g sweep over "
                          "M on the decode linear (one JSON line of its own)")
@@ -579,6 +623,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    if args.only == "silu":
+        smq = bench_silu_mul(args, torch, pdq, synth)
+        print(json.dumps({"metric": "fused SiLU*up + per-token INT8 GB/s", "unit": "GB/s", "n_gpus": 1,
+                          "data": "synthetic", "config": {"workload": "decoder block down-projection input "
+                                                                      "8192 x 14336 bf16"},
+                          "fused_us": round(smq["ms_fused"] * 1e3, 2),
+                          "fused_GBps": round(smq["bytes"] / (smq["ms_fused"] * 1e-3) / 1e9, 1),
+                          "unfused_us": round(smq["ms_unfused"] * 1e3, 2),
+                          "down_projection_us": round(smq["ms_linear"] * 1e3, 1)}), flush=True)
+        return
     if args.only == "decode":
         dec = bench_decode(args, torch, pdq, synth)
         print(json.dumps({"metric": "decode GB/s", "unit": "GB/s", "n_gpus": 1, "data": "synthetic",
@@ -592,7 +646,7 @@ def main():
         log(f"[prefill] hipBLASLt INT8 GEMM (torch._int_mm, INT32 out) {pre['ms_lib']*1e3:.1f} us")
     log(f"[prefill asym] step {pre['ms_step_asym']*1e3:.1f} us (quant {pre['ms_quant_asym']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm_asym']*1e3:.1f} us)")
-    dec = llm = blk = None
+    dec = llm = blk = smq = None
     if args.only == "all":
         dec = bench_decode(args, torch, pdq, synth)
         for m, r in dec["per_batch"].items():
@@ -608,6 +662,10 @@ def main():
             f"{blk['prefill_ops'] / (blk['ms_prefill'] * 1e-3) / 1e12:.0f} TOPS; decode step (4 linears, "
             f"batch {blk['batch']}) {blk['ms_step']*1e3:.1f} us = "
             f"{blk['step_bytes'] / (blk['ms_step'] * 1e-3) / 1e9:.0f} GB/s")
+        smq = bench_silu_mul(args, torch, pdq, synth)
+        log(f"[silu*up quant] fused {smq['ms_fused']*1e3:.1f} us = "
+            f"{smq['bytes'] / (smq['ms_fused'] * 1e-3) / 1e9:.0f} GB/s; unfused (torch SiLU*up + quantizer) "
+            f"{smq['ms_unfused']*1e3:.1f} us; down projection {smq['ms_linear']*1e3:.1f} us")
 
     value = pre["ops"] / (pre["ms_step"] * 1e-3) / 1e12
     out = {
@@ -663,6 +721,17 @@ def main():
             "decode_GBps": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9, 1),
             "decode_frac": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "int8_weight_MB": round(blk["weight_bytes"] / 1e6, 1)}
+    if smq:
+        out["silu_mul_quant"] = {
+            "workload": f"h = SiLU(gate) * up, {smq['M']} tokens x {smq['K']} (gate and up: halves of one "
+                        f"bf16 [M, 2K] buffer), per-token INT8; then the down projection {smq['K']}->{smq['N']}",
+            "fused_us": round(smq["ms_fused"] * 1e3, 2),
+            "fused_GBps": round(smq["bytes"] / (smq["ms_fused"] * 1e-3) / 1e9, 1),
+            "fused_frac": round(smq["bytes"] / (smq["ms_fused"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_MB": round(smq["bytes"] / 1e6, 1),
+            "unfused_torch_silu_mul_plus_quantizer_us": round(smq["ms_unfused"] * 1e3, 2),
+            "down_projection_us": round(smq["ms_linear"] * 1e3, 1),
+            "down_projection_TOPS": round(smq["ops"] / (smq["ms_linear"] * 1e-3) / 1e12, 1)}
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(pre)

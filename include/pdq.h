@@ -18,6 +18,9 @@
  *                 its four-term expansion, section 3 granularity; part 2
  *                 vector-wise quantization, the four-step INT8 flow, the 16-bit
  *                 decomposition and the mixed-precision decomposition.
+ *   [HW-accel]    "Hardware acceleration of quantized operations" (apxml course,
+ *                 chapter 2): the role of compilers and runtime libraries
+ *                 (kernel fusion: fewer memory round trips and launches).
  *
  * Arithmetic (identical on every entry point):
  *   rne(v)            round to nearest integer, ties to even
@@ -322,6 +325,41 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
                            const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
                            const float* bias, int64_t N, uint16_t* y, int64_t ldy, int32_t* acc_out,
                            void* stream);
+
+/*
+ * Fused producer + per-token quantizer for the input of an MLP down
+ * projection: h = SiLU(gate) * up is formed in registers and quantized per
+ * token, instead of being written to memory by one kernel and read back by
+ * the quantizer ([HW-accel], kernel fusion).  SiLU(g) = g * sigmoid(g), the
+ * gate of a SwiGLU MLP (the pages define no activation function; this is the
+ * textbook one).  Each element is computed in binary32 -- e = 2^(-|g| log2 e)
+ * and r = 1 / (1 + e) on the hardware exp2 and reciprocal (1 ulp each),
+ * sigmoid = (g >= 0 ? r : e * r), h = (g * sigmoid) * up; relative error
+ * below (1.5 |g| + 8) 2^-24 for |g| < 87 -- and then rounded to dt, so that h
+ * is the value an unfused kernel of that dtype would store (up to that error
+ * next to a tie of dt).  The codes are exactly those of
+ * pdq_quantize_per_token applied to h.
+ *
+ *   gate, up     [M, K] of dt (BF16 or F16; F32 is rejected), row pitches
+ *                ldg, ldu (e.g. the two halves of a fused gate/up GEMM
+ *                output [M, 2K]: up = gate + K, ldg = ldu = 2K)
+ *   xq           packed int8 codes out (pdq_act_bytes(M, K) bytes)
+ *   x_scale      [M] float out: max_k |h[m,k]| / 127 (1 for an all-zero row)
+ *   h            [M, K] of dt out, row pitch ldh, or NULL: also store h
+ *                (must not overlap gate or up)
+ */
+pdq_status pdq_silu_mul_quantize_per_token(const void* gate, const void* up, pdq_dtype dt, int64_t M,
+                                           int64_t K, int64_t ldg, int64_t ldu, int8_t* xq,
+                                           float* x_scale, uint16_t* h, int64_t ldh, void* stream);
+
+/* pdq_silu_mul_quantize_per_token (h not stored) followed by pdq_gemm_per_token: the
+ * down projection y = bf16((S_x[m] * S_w[n]) * (float)(sum_k xq wq) [+ bias[n]]) of
+ * h = SiLU(gate) * up, with K the intermediate size.  Other arguments as in
+ * pdq_linear_prefill. */
+pdq_status pdq_linear_prefill_silu_mul(const void* gate, const void* up, pdq_dtype dt, int64_t M, int64_t K,
+                                       int64_t ldg, int64_t ldu, const int8_t* wq, const float* w_scale,
+                                       const float* bias, int64_t N, int8_t* xq, float* x_scale,
+                                       uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream);
 
 /*
  * LLM.int8() vector-wise quantization with the 16-bit outlier decomposition.

@@ -257,3 +257,33 @@ def test_zeropoint_validation(L):
     q = L.pdq_quantize_zeropoint
     assert q(P, 1, 4, 64, 64, 1.0, 127, None, None, None) == NULL
     assert q(P, 1, 4, 64, 64, 1.0, -128, P, None, None) == UNSUP
+
+
+def test_silu_mul_validation(L):
+    q = L.pdq_silu_mul_quantize_per_token
+
+    def call(dt=1, M=4, K=64, ldg=128, ldu=128, xq=P, xs=P, h=None, ldh=0):
+        return q(P, P + 128, dt, M, K, ldg, ldu, xq, xs, h, ldh, None)
+
+    assert call(dt=0) == DTYPE                # binary32 producers are not accepted
+    assert call(dt=5) == DTYPE
+    assert call(K=40, ldg=40, ldu=40) == SHAPE
+    assert call(ldu=32) == SHAPE
+    assert call(xq=None) == NULL
+    assert call(xs=None) == NULL
+    assert call(ldg=68) == ALIGN              # row pitch of 136 bytes
+    assert call(h=P, ldh=32) == SHAPE
+    assert call(h=P + 2, ldh=64) == ALIGN
+    assert call(M=0) == OK
+    lin = L.pdq_linear_prefill_silu_mul
+
+    def lcall(dt=2, M=4, K=64, ws=P, xq=P, y=P, ldy=16):
+        return lin(P, P, dt, M, K, K, K, P, ws, None, 16, xq, P, y, ldy, None, None)
+
+    assert lcall(dt=0) == DTYPE
+    assert lcall(K=24) == SHAPE
+    assert lcall(ldy=8) == SHAPE
+    assert lcall(ws=None) == NULL
+    assert lcall(y=None) == NULL
+    assert lcall(xq=None) == NULL
+    assert lcall(M=0) == OK

@@ -805,3 +805,114 @@ def test_static_rounding_near_ties(s):
         q_ref, sat_ref = O.quantize_static(v, s, z)
         assert codes_equal(xq, q_ref)
         assert int(host(sat)[0]) == sat_ref
+
+
+# ---------------------------------------------------------------------------
+# Fused SiLU(gate) * up producer + per-token quantizer
+# ---------------------------------------------------------------------------
+
+def check_silu_mul_h(hv, g, u, dtype):
+    """The GPU's h equals the oracle's (binary64, rounded once) except next to a
+    tie of the 16-bit type, where the binary32 evaluation may take the other
+    neighbour: its relative error is below (1.5 |g| + 8) 2^-24 (the rounded
+    exponent argument, the hardware exp2 and reciprocal at 1 ulp each, three
+    products), and only values that close to a tie may differ."""
+    ref = O.silu_mul(g, u, dtype)
+    bad = hv != ref
+    n = int(bad.sum())
+    assert n <= max(8, hv.size // 1000), n
+    if n:
+        v = O.silu(g[bad]) * u[bad].astype(np.float64)
+        sig, emin = (8, -126) if dtype == "bf16" else (11, -14)
+        _, e = np.frexp(v)
+        step = np.ldexp(1.0, np.maximum(e, emin + 1) - sig)
+        t = v / step
+        fl = np.floor(t)
+        window = (1.5 * np.abs(g[bad].astype(np.float64)) + 8) * 2.0 ** -24 * np.abs(v)
+        assert np.all(np.abs(t - fl - 0.5) * step <= window)
+        assert np.all((hv[bad] == fl * step) | (hv[bad] == (fl + 1) * step))
+
+
+def _h_values(h, dtype):
+    b = host(h)
+    return O.bf16_bits_to_f32(b) if dtype == "bf16" else b.view(np.float16).astype(np.float32)
+
+
+def silu_mul_case(g, u, dtype, halves=False, rows=None):
+    m, k = g.shape
+    if halves:  # the two halves of one [M, 2K] gate/up buffer
+        gu = dev(np.concatenate([g, u], axis=1), dtype)
+        gd, ud = gu[:, :k], gu[:, k:]
+    else:
+        gd, ud = dev(g, dtype), dev(u, dtype)
+    h = torch.empty((m, k), dtype=gd.dtype, device="cuda")
+    xq, xs = pdq.silu_mul_quantize_per_token(gd, ud, h=h)
+    hv = _h_values(h, dtype)
+    r = np.arange(m) if rows is None else rows
+    check_silu_mul_h(hv[r], g[r], u[r], dtype)
+    q_ref, s_ref = O.quantize_rows_absmax(hv)
+    assert codes_equal(xq, q_ref)
+    assert np.array_equal(host(xs).view(np.uint32), s_ref.view(np.uint32))
+    xq2, xs2 = pdq.silu_mul_quantize_per_token(gd, ud)  # h not stored: same codes
+    nb = pdq.act_bytes(m, k)
+    assert torch.equal(xq2.data[:nb], xq.data[:nb]) and torch.equal(xs2, xs)
+    return hv, q_ref, s_ref
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,m,k", [
+    ("bf16", 1, 16), ("bf16", 37, 1040), ("bf16", 64, 4096), ("bf16", 19, 11008), ("bf16", 5, 16384),
+    ("bf16", 3, 20480), ("f16", 33, 2048), ("f16", 17, 14336), ("bf16", 2, 40960), ("f16", 1, 65536),
+])
+def test_silu_mul_quant_shapes(dtype, m, k):
+    g, u = synth.swiglu_inputs(9000 + m, m, k, dtype)
+    silu_mul_case(g, u, dtype)
+
+
+@pytest.mark.gpu
+def test_silu_mul_quant_gate_up_halves_and_empty():
+    g, u = synth.swiglu_inputs(9100, 20, 2048, "bf16")
+    silu_mul_case(g, u, "bf16", halves=True)
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    xq, xs = pdq.silu_mul_quantize_per_token(e, e)
+    assert xs.numel() == 0
+
+
+@pytest.mark.gpu
+def test_silu_mul_quant_extremes():
+    k = 256
+    g, u = synth.swiglu_inputs(9200, 4, k, "bf16")
+    g[0, :8] = [0.0, -0.0, 100.0, -100.0, 1000.0, -1000.0, 3.0e38, -3.0e38]
+    u[0, :8] = [5.0, -5.0, 1.0, 1.0, -2.0, 1.0, 0.5, 1.0]
+    g[1] = 0.0                      # all-zero row: scale 1, codes 0
+    g[2, :] = 40.0                  # SiLU(g) = g to binary32: exact products, ties possible
+    u[2, :] = synth.round_to(np.linspace(-3, 3, k, dtype=np.float32), "bf16")
+    g, u = synth.round_to(g, "bf16"), synth.round_to(u, "bf16")
+    hv, q, s = silu_mul_case(g, u, "bf16")
+    assert s[1] == 1.0 and not q[1].any()
+
+
+@pytest.mark.gpu
+def test_silu_mul_quant_down_projection_full_sampled():
+    c = synth.DecoderBlock()
+    g, u = c.down_gate_up()
+    silu_mul_case(g, u, c.dtype, halves=True, rows=sample_rows(g.shape[0], 32, 7))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("m,n,k", [(40, 96, 1040), (300, 520, 2048), (2, 4096, 14336)])
+def test_linear_prefill_silu_mul(m, n, k):
+    g, u = synth.swiglu_inputs(9300 + m, m, k, "bf16")
+    w = synth.weights(9400 + m, n, k, "bf16")
+    wq, ws, _, (rq, rs, _) = weight_case(w, "bf16")
+    gd, ud = dev(g, "bf16"), dev(u, "bf16")
+    h = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    pdq.silu_mul_quantize_per_token(gd, ud, h=h)
+    hv = _h_values(h, "bf16")
+    check_silu_mul_h(hv, g, u, "bf16")
+    q_ref, s_ref = O.quantize_rows_absmax(hv)
+    res = pdq.linear_prefill_silu_mul(gd, ud, wq, ws, want_acc=True)
+    assert codes_equal(res["xq"], q_ref)
+    acc_ref = O.int_matmul(q_ref, rq)
+    assert np.array_equal(host(res["acc"]), acc_ref)
+    check_16bit(host(res["y"]), O.dequantize(acc_ref, s_ref, rs), "bf16", True)

@@ -191,6 +191,39 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
     return pdq_gemm_per_token(xq, x_scale, M, K, wq, w_scale, bias, N, y, ldy, acc_out, stream);
 }
 
+pdq_status pdq_silu_mul_quantize_per_token(const void* gate, const void* up, pdq_dtype dt, int64_t M,
+                                           int64_t K, int64_t ldg, int64_t ldu, int8_t* xq,
+                                           float* x_scale, uint16_t* h, int64_t ldh, void* stream) {
+    if (dt != PDQ_BF16 && dt != PDQ_F16) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(gate, 2, M, K, ldg));
+    PDQ_TRY(check_operand(up, 2, M, K, ldu));
+    if (h) PDQ_TRY(check_operand(h, 2, M, K, ldh));
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4)) return PDQ_ERR_ALIGN;
+    if (M == 0) return PDQ_OK;
+    launch_silu_mul_quant(gate, ldg, up, ldu, dt, M, K, xq, x_scale, h, ldh, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_linear_prefill_silu_mul(const void* gate, const void* up, pdq_dtype dt, int64_t M, int64_t K,
+                                       int64_t ldg, int64_t ldu, const int8_t* wq, const float* w_scale,
+                                       const float* bias, int64_t N, int8_t* xq, float* x_scale,
+                                       uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream) {
+    if (dt != PDQ_BF16 && dt != PDQ_F16) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(gate, 2, M, K, ldg));
+    PDQ_TRY(check_operand(up, 2, M, K, ldu));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N > 0 && !w_scale) return PDQ_ERR_NULL;
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(acc_out, 4))
+        return PDQ_ERR_ALIGN;
+    PDQ_TRY(pdq_silu_mul_quantize_per_token(gate, up, dt, M, K, ldg, ldu, xq, x_scale, nullptr, 0, stream));
+    return pdq_gemm_per_token(xq, x_scale, M, K, wq, w_scale, bias, N, y, ldy, acc_out, stream);
+}
+
 pdq_status pdq_quantize_per_token_asym(const void* x, pdq_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
                                        int8_t* xq, float* x_scale, int32_t* x_zp, void* stream) {
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;

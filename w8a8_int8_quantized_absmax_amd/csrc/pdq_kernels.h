@@ -34,6 +34,12 @@ void launch_quant_rows(const void* x, int dt, int64_t rows, int64_t K, int64_t l
 void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int64_t ldx, int8_t* q,
                             float* scale, int32_t* zp, hipStream_t st);
 
+// Fused SwiGLU producer + per-token quantizer (16-bit dt only): h = SiLU(gate)
+// * up rounded to dt, then exactly launch_quant_rows' codes and scales of h;
+// h also stored when h != nullptr (row pitch ldh).  ld* in elements.
+void launch_silu_mul_quant(const void* gate, int64_t ldg, const void* up, int64_t ldu, int dt, int64_t rows,
+                           int64_t K, int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st);
+
 // Static code: q = clamp(rne(x / s) + z, -128, 127) (narrow: the range
 // [-127, 127]), packed, padding zeroed; saturation count added to *sat
 // (nullable).

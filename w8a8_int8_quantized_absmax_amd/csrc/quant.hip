@@ -18,6 +18,13 @@
 //                   (PDMIX terminology entry, section 2.3 decode formula),
 //                   with the saturation count of section 2.4.
 //
+//  * k_silu_mul_quant  the per-token quantizer fused into the producer of its
+//                   input: h = SiLU(gate) * up of a SwiGLU MLP, rounded to the
+//                   16-bit type, quantized like k_quant_rows without h ever
+//                   leaving registers ("Hardware acceleration of quantized
+//                   operations", role of compilers and runtime libraries:
+//                   kernel fusion).
+//
 // Every code matrix is written in the packed tile layout of pdq_device.h,
 // the layout the GEMMs read, padding rows and K values as zeros.
 //  * k_minmax       the MinMax observer of the static calibration, and
@@ -323,6 +330,209 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         if (lane == 0) rowint[row] = zq;
 }
 
+// h = SiLU(g) * u for one chunk in binary32, rounded to DT (nearest even).
+// e = 2^(-|g| log2(e)) on the hardware exponential (v_exp_f32), r = 1 / (1 + e)
+// on the hardware reciprocal (v_rcp_f32, 1 ulp); sigmoid(g) = r for g >= 0 and
+// e r for g < 0.  e <= 1, so nothing overflows, and SiLU(g) -> -0 as g ->
+// -inf.  Relative error of the binary32 h: the rounded exponent argument
+// contributes |g| 2^-24 (for g >= 0 damped by e / (1 + e)), exp2 and the
+// reciprocal 1 ulp each, the three products half an ulp each -- within
+// (1.5 |g| + 8) 2^-24 while e is a normal number (|g| < 87).  Two
+// transcendental instructions per element instead of the library exponential
+// and a correctly rounded division keep the kernel on the memory roofline.
+template <int DT>
+__device__ __forceinline__ Raw8<DT> silu_mul8(const Raw8<DT>& g, const Raw8<DT>& u) {
+    constexpr float kLog2e = 1.44269504088896340736f;
+    float gv[8], uv[8];
+    widen8<DT>(g, gv);
+    widen8<DT>(u, uv);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        float p[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float x = gv[j + t];
+            const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+            const float r = __builtin_amdgcn_rcpf(1.0f + e);
+            const float sg = x >= 0.0f ? r : e * r;
+            p[t] = (x * sg) * uv[j + t];
+        }
+        w[j / 2] = f32x2_to_16<DT>(p[0], p[1]);
+    }
+    Raw8<DT> h;
+    h.w[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    return h;
+}
+
+// One wavefront per row, as k_quant_rows, for rows up to 64 * 8 * 8 values:
+// CPL > 0 keeps the row's h in registers (gate and up read from HBM once);
+// CPL == 0 (rows longer than 256 * 8 * 16 values) forms h twice, for the
+// absmax and for the codes -- the same operations, so the same bits.  h_out
+// (nullable) receives h.
+template <int DT, int CPL, bool FULL>
+__global__ __launch_bounds__(256, 2) void k_silu_mul_quant(const void* __restrict__ gate, int64_t ldg_bytes,
+                                                        const void* __restrict__ up, int64_t ldu_bytes,
+                                                        int64_t rows, int nch, int8_t* __restrict__ q,
+                                                        float* __restrict__ scale, void* __restrict__ h_out,
+                                                        int64_t ldh_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= (rows + kWGroup - 1) / kWGroup * kWGroup) return;
+    const int ktiles = (nch + 7) / 8;
+    int8_t* const qg = q + wpack_block(row / kWGroup, 0, ktiles);
+    const int rg = (int)(row % kWGroup);
+    auto store_code = [&](int c, uint2 code) {
+        *reinterpret_cast<uint2*>(qg + (int64_t)(c >> 3) * kWBlock + wpack_pos(rg, (c & 7) >> 1) + ((c & 1) << 3)) =
+            code;
+    };
+    if (row >= rows) {
+        for (int c = lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));
+        return;
+    }
+    const char* gr = static_cast<const char*>(gate) + row * ldg_bytes;
+    const char* ur = static_cast<const char*>(up) + row * ldu_bytes;
+    uint4* hr = h_out ? reinterpret_cast<uint4*>(static_cast<char*>(h_out) + row * ldh_bytes) : nullptr;
+    float amax = 0.0f, s, inv;
+    if constexpr (CPL > 0) {
+        Raw8<DT> hv[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const int cc = FULL ? c : min(c, nch - 1);
+            hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
+            if (!FULL && c >= nch) hv[i] = zero_raw8<DT>();
+            amax = chunk_absmax<DT>(hv[i], 0u, amax);
+        }
+        amax = wave_max_full(amax);
+        s = absmax_step(amax);
+        inv = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const uint2 code = chunk_codes_absmax<DT, false>(hv[i], 0u, s, inv);
+            if (FULL || c < nch) {
+                store_code(c, code);
+                if (hr) hr[c] = hv[i].w[0];
+            }
+        }
+    } else {
+        for (int c = lane; c < nch; c += 64)
+            amax = chunk_absmax<DT>(silu_mul8<DT>(load_raw8<DT>(gr, c), load_raw8<DT>(ur, c)), 0u, amax);
+        amax = wave_max_full(amax);
+        s = absmax_step(amax);
+        inv = 1.0f / s;
+        for (int c = lane; c < nch; c += 64) {
+            const Raw8<DT> hc = silu_mul8<DT>(load_raw8<DT>(gr, c), load_raw8<DT>(ur, c));
+            store_code(c, chunk_codes_absmax<DT, false>(hc, 0u, s, inv));
+            if (hr) hr[c] = hc.w[0];
+        }
+    }
+    for (int c = nch + lane; c < ktiles * 8; c += 64) store_code(c, make_uint2(0u, 0u));  // K padding
+    if (lane == 0) scale[row] = s;
+}
+
+// Rows longer than 64 * 8 * 8 values: one workgroup per row, CPT chunks per
+// thread, the row's absmax reduced across the four wavefronts through LDS.
+// Fewer registers per thread than a wavefront per row, so that several rows
+// are in flight per CU while others compute.  The absmax, the scale and the
+// codes are the same as k_silu_mul_quant's (max is exact in any order).
+template <int DT, int CPT>
+__global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restrict__ gate, int64_t ldg_bytes,
+                                                           const void* __restrict__ up, int64_t ldu_bytes,
+                                                           int64_t rows, int nch, int8_t* __restrict__ q,
+                                                           float* __restrict__ scale, void* __restrict__ h_out,
+                                                           int64_t ldh_bytes) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int ktiles = (nch + 7) / 8;
+    int8_t* const qg = q + wpack_block(row / kWGroup, 0, ktiles);
+    const int rg = (int)(row % kWGroup);
+    auto store_code = [&](int c, uint2 code) {
+        *reinterpret_cast<uint2*>(qg + (int64_t)(c >> 3) * kWBlock + wpack_pos(rg, (c & 7) >> 1) + ((c & 1) << 3)) =
+            code;
+    };
+    if (row >= rows) {  // padding row of the last 16-row group (whole workgroup)
+        for (int c = tid; c < ktiles * 8; c += 256) store_code(c, make_uint2(0u, 0u));
+        return;
+    }
+    const char* gr = static_cast<const char*>(gate) + row * ldg_bytes;
+    const char* ur = static_cast<const char*>(up) + row * ldu_bytes;
+    uint4* hr = h_out ? reinterpret_cast<uint4*>(static_cast<char*>(h_out) + row * ldh_bytes) : nullptr;
+    Raw8<DT> hv[CPT];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + 256 * i;
+        const int cc = min(c, nch - 1);
+        hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
+        if (c >= nch) hv[i] = zero_raw8<DT>();
+        amax = chunk_absmax<DT>(hv[i], 0u, amax);
+    }
+    __shared__ float s_max[4];
+    amax = wave_max_full(amax);
+    if (lane == 0) s_max[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const float s = absmax_step(amax);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + 256 * i;
+        const uint2 code = chunk_codes_absmax<DT, false>(hv[i], 0u, s, inv);
+        if (c < nch) {
+            store_code(c, code);
+            if (hr) hr[c] = hv[i].w[0];
+        }
+    }
+    for (int c = nch + tid; c < ktiles * 8; c += 256) store_code(c, make_uint2(0u, 0u));  // K padding
+    if (tid == 0) scale[row] = s;
+}
+
+template <int DT, int CPT>
+void silu_mul_quant_wg(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int nch,
+                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
+    const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
+    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate, ldg * 2,
+                       up, ldu * 2, rows, nch, q, scale, h, ldh * 2);
+}
+
+template <int DT, int CPL>
+void silu_mul_quant_cpl(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int nch,
+                        int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
+    const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
+    const dim3 grid((unsigned)((rows_pad + kRowsPerBlock - 1) / kRowsPerBlock));
+    if (CPL > 0 && nch == 64 * CPL)
+        hipLaunchKernelGGL((k_silu_mul_quant<DT, CPL, true>), grid, dim3(256), 0, st, gate, ldg * 2, up,
+                           ldu * 2, rows, nch, q, scale, h, ldh * 2);
+    else
+        hipLaunchKernelGGL((k_silu_mul_quant<DT, CPL, false>), grid, dim3(256), 0, st, gate, ldg * 2, up,
+                           ldu * 2, rows, nch, q, scale, h, ldh * 2);
+}
+
+template <int DT>
+void silu_mul_quant_dt(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int64_t K,
+                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
+    const int nch = (int)(K / 8);
+    const int64_t per_lane = (nch + 63) / 64;
+    if (per_lane <= 1)
+        silu_mul_quant_cpl<DT, 1>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 2)
+        silu_mul_quant_cpl<DT, 2>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 4)
+        silu_mul_quant_cpl<DT, 4>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 8)
+        silu_mul_quant_cpl<DT, 8>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 16)
+        silu_mul_quant_wg<DT, 4>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 32)
+        silu_mul_quant_wg<DT, 8>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else if (per_lane <= 64)
+        silu_mul_quant_wg<DT, 16>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+    else
+        silu_mul_quant_cpl<DT, 0>(gate, ldg, up, ldu, rows, nch, q, scale, h, ldh, st);
+}
+
 template <int DT, int CPL, bool FULL>
 void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, float* scale,
                  int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
@@ -499,6 +709,15 @@ void launch_quant_rows_asym(const void* x, int dt, int64_t rows, int64_t K, int6
         case kBF16: quant_rows_dt<kBF16>(x, rows, K, ldx, q, scale, zp, nullptr, true, st); break;
         default: quant_rows_dt<kF16>(x, rows, K, ldx, q, scale, zp, nullptr, true, st); break;
     }
+}
+
+void launch_silu_mul_quant(const void* gate, int64_t ldg, const void* up, int64_t ldu, int dt, int64_t rows,
+                           int64_t K, int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
+    if (rows <= 0) return;
+    if (dt == kF16)
+        silu_mul_quant_dt<kF16>(gate, ldg, up, ldu, rows, K, q, scale, h, ldh, st);
+    else
+        silu_mul_quant_dt<kBF16>(gate, ldg, up, ldu, rows, K, q, scale, h, ldh, st);
 }
 
 template <int DT>

@@ -52,6 +52,10 @@ SIGNATURES = {
     "pdq_quantize_zeropoint": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp]),
     "pdq_linear_zeropoint": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp,
                                             _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "pdq_silu_mul_quantize_per_token": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _vp,
+                                                       _vp, _i64, _vp]),
+    "pdq_linear_prefill_silu_mul": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                                   _i64, _vp, _vp, _vp, _i64, _vp, _vp]),
     "pdq_linear_int8_outlier_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "pdq_weight_bytes": (_sz, [_i64, _i64]),
     "pdq_act_bytes": (_sz, [_i64, _i64]),
@@ -428,6 +432,48 @@ def quantize_per_token(x, xq=None, x_scale=None):
     xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=x.device)
     _call("pdq_quantize_per_token", _p(x), _DT[x.dtype], m, k, _ld(x), _p(xq), _p(xs), _stream(x.device))
     return xq, xs
+
+
+_HALF = (torch.bfloat16, torch.float16)
+
+
+def _check_gate_up(gate, up):
+    _check_mat(gate, "gate", _HALF)
+    _check_mat(up, "up", _HALF)
+    if up.shape != gate.shape or up.dtype != gate.dtype:
+        raise ValueError("gate and up must have the same shape and dtype")
+    return gate.shape
+
+
+def silu_mul_quantize_per_token(gate, up, xq=None, x_scale=None, h=None):
+    """h = SiLU(gate) * up (rounded to gate's 16-bit dtype) quantized per token
+    -> (xq packed Codes [M,K], x_scale f32 [M]).  h: optional [M,K] tensor of
+    that dtype that also receives the product."""
+    m, k = _check_gate_up(gate, up)
+    xq = _codes_out(xq, m, k, gate.device)
+    xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=gate.device)
+    if h is not None:
+        _check_mat(h, "h", (gate.dtype,))
+        if h.shape != gate.shape:
+            raise ValueError("h must have gate's shape")
+    _call("pdq_silu_mul_quantize_per_token", _p(gate), _p(up), _DT[gate.dtype], m, k, _ld(gate), _ld(up),
+          _p(xq), _p(xs), _p(h), _ld(h) if h is not None else 0, _stream(gate.device))
+    return xq, xs
+
+
+def linear_prefill_silu_mul(gate, up, wq, w_scale, bias=None, want_acc: bool = False, out=None):
+    """Down projection of h = SiLU(gate) * up, per-token dynamic symmetric W8A8
+    -> dict(y bf16, xq, x_scale[, acc]); K is the intermediate size."""
+    m, k = _check_gate_up(gate, up)
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
+    xq = Codes.empty(m, k, gate.device)
+    xs = torch.empty(m, dtype=torch.float32, device=gate.device)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=gate.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=gate.device) if want_acc else None
+    _call("pdq_linear_prefill_silu_mul", _p(gate), _p(up), _DT[gate.dtype], m, k, _ld(gate), _ld(up), _p(wq),
+          _p(w_scale), _p(bias), n, _p(xq), _p(xs), _p(y), _ld(y), _p(acc), _stream(gate.device))
+    return dict(y=y, xq=xq, x_scale=xs, acc=acc)
 
 
 def gemm_per_token(xq, x_scale, wq, w_scale, bias=None, want_acc: bool = False, out=None):

@@ -53,6 +53,14 @@ def normal(seed: int, shape, std: float = 1.0) -> np.ndarray:
     return x
 
 
+def swiglu_inputs(seed: int, m: int, k: int, dtype: str = "bf16", gate_std: float = 2.0,
+                  up_std: float = 1.0):
+    """Gate and up projections of a SwiGLU MLP (the two halves of a gate/up GEMM
+    output), [m, k] each: independent normals rounded to dtype."""
+    return (round_to(normal(seed, (m, k), gate_std), dtype),
+            round_to(normal(seed + 1, (m, k), up_std), dtype))
+
+
 def choose_channels(seed: int, k: int, count: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return np.sort(rng.choice(k, size=count, replace=False)).astype(np.int64)
@@ -213,6 +221,12 @@ class DecoderBlock:
         _, _, k = self.linears[l]
         return activations(6000 + 100 * l + b, 512, k, self.channels(l, k), 100.0, offset=0.1,
                            dtype=self.dtype)
+
+    def down_gate_up(self, rows: int | None = None):
+        """Input of the down projection before the activation: gate and up
+        [rows, intermediate] (intermediate = the down projection's K)."""
+        _, _, k = self.linears[3]
+        return swiglu_inputs(530, rows or self.prefill_tokens, k, self.dtype)
 
     def decode_x(self, l: int, t: int):
         _, _, k = self.linears[l]
