@@ -916,3 +916,18 @@ def test_linear_prefill_silu_mul(m, n, k):
     acc_ref = O.int_matmul(q_ref, rq)
     assert np.array_equal(host(res["acc"]), acc_ref)
     check_16bit(host(res["y"]), O.dequantize(acc_ref, s_ref, rs), "bf16", True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,m,k", [
+    ("bf16", 21, 4112), ("f16", 17, 8192), ("bf16", 33, 14336), ("f32", 5, 20480), ("bf16", 3, 32768),
+    ("bf16", 2, 40960),
+])
+def test_quantize_per_token_long_rows(dtype, m, k):
+    """Rows beyond 4096 values: a workgroup per row up to 32768, then a
+    wavefront streaming the row twice; codes and scales exactly the oracle's."""
+    x = synth.activations(9500 + m, m, k, synth.choose_channels(9600 + m, k, 6), 100.0, dtype=dtype)
+    xq, xs = pdq.quantize_per_token(dev(x, dtype))
+    q_ref, s_ref = O.quantize_rows_absmax(x)
+    assert codes_equal(xq, q_ref)
+    assert np.array_equal(host(xs).view(np.uint32), s_ref.view(np.uint32))

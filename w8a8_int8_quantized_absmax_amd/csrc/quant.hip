@@ -436,8 +436,10 @@ __global__ __launch_bounds__(256, 2) void k_silu_mul_quant(const void* __restric
 // thread, the row's absmax reduced across the four wavefronts through LDS.
 // Fewer registers per thread than a wavefront per row, so that several rows
 // are in flight per CU while others compute.  The absmax, the scale and the
-// codes are the same as k_silu_mul_quant's (max is exact in any order).
-template <int DT, int CPT>
+// codes are the same as with a wavefront per row (max is exact in any order).
+// SILU: the row is h = SiLU(gate) * up (gate = x); otherwise the row of x
+// itself, the plain per-token quantizer of k_quant_rows (DT may be binary32).
+template <int DT, int CPT, bool SILU>
 __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restrict__ gate, int64_t ldg_bytes,
                                                            const void* __restrict__ up, int64_t ldu_bytes,
                                                            int64_t rows, int nch, int8_t* __restrict__ q,
@@ -465,7 +467,10 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
     for (int i = 0; i < CPT; ++i) {
         const int c = tid + 256 * i;
         const int cc = min(c, nch - 1);
-        hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
+        if constexpr (SILU)
+            hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
+        else
+            hv[i] = load_raw8<DT>(gr, cc);
         if (c >= nch) hv[i] = zero_raw8<DT>();
         amax = chunk_absmax<DT>(hv[i], 0u, amax);
     }
@@ -482,19 +487,21 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
         const uint2 code = chunk_codes_absmax<DT, false>(hv[i], 0u, s, inv);
         if (c < nch) {
             store_code(c, code);
-            if (hr) hr[c] = hv[i].w[0];
+            if constexpr (SILU)
+                if (hr) hr[c] = hv[i].w[0];
         }
     }
     for (int c = nch + tid; c < ktiles * 8; c += 256) store_code(c, make_uint2(0u, 0u));  // K padding
     if (tid == 0) scale[row] = s;
 }
 
-template <int DT, int CPT>
+template <int DT, int CPT, bool SILU = true>
 void silu_mul_quant_wg(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int nch,
                        int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
-    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate, ldg * 2,
-                       up, ldu * 2, rows, nch, q, scale, h, ldh * 2);
+    constexpr int eb = Elem<DT>::bytes;
+    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, SILU>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate,
+                       ldg * eb, up, ldu * eb, rows, nch, q, scale, h, ldh * eb);
 }
 
 template <int DT, int CPL>
@@ -568,6 +575,17 @@ template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                    int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
+    if (!skip && !colsum && !asym && per_lane > 8 && per_lane <= 64) {
+        // the plain per-token quantizer of long rows: a workgroup per row
+        const int nch = (int)(K / 8);
+        if (per_lane <= 16)
+            silu_mul_quant_wg<DT, 4, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        else if (per_lane <= 32)
+            silu_mul_quant_wg<DT, 8, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        else
+            silu_mul_quant_wg<DT, 16, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        return;
+    }
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
     if (per_lane <= 1)
         quant_rows_cpl<DT, 1>(x, rows, K, ldx, q, scale, colsum, skip, asym, st);
