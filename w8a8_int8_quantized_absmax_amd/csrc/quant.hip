@@ -575,10 +575,13 @@ template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                    int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
-    if (!skip && !colsum && !asym && per_lane > 8 && per_lane <= 64) {
-        // the plain per-token quantizer of long rows: a workgroup per row
+    if (!skip && !colsum && !asym && per_lane > 4 && per_lane <= 64) {
+        // the plain per-token quantizer of rows longer than 2048 values: a
+        // workgroup per row (more rows in flight per CU than a wavefront per row)
         const int nch = (int)(K / 8);
-        if (per_lane <= 16)
+        if (per_lane <= 8)
+            silu_mul_quant_wg<DT, 2, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        else if (per_lane <= 16)
             silu_mul_quant_wg<DT, 4, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
         else if (per_lane <= 32)
             silu_mul_quant_wg<DT, 8, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
