@@ -931,3 +931,21 @@ def test_quantize_per_token_long_rows(dtype, m, k):
     q_ref, s_ref = O.quantize_rows_absmax(x)
     assert codes_equal(xq, q_ref)
     assert np.array_equal(host(xs).view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,m,k", [
+    ("bf16", 21, 4112), ("f16", 9, 8192), ("bf16", 33, 14336), ("f32", 5, 20480), ("bf16", 2, 40960),
+])
+def test_quantize_per_token_asym_long_rows(dtype, m, k):
+    """The per-token asymmetric quantizer on rows beyond 2048 values (a
+    workgroup per row, min and max reduced across its waves): codes, scales
+    and zero points exactly the oracle's; one row all positive, one all zero."""
+    x = synth.activations(9700 + m, m, k, synth.choose_channels(9800 + m, k, 6), 100.0, offset=0.1, dtype=dtype)
+    x[0] = np.abs(x[0])
+    x[m - 1] = 0.0
+    xq, xs, xz = pdq.quantize_per_token_asym(dev(x, dtype))
+    q_ref, s_ref, z_ref = O.quantize_rows_asym(x)
+    assert codes_equal(xq, q_ref)
+    assert np.array_equal(host(xs).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(xz), z_ref)

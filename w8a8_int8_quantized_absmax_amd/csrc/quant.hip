@@ -437,14 +437,18 @@ __global__ __launch_bounds__(256, 2) void k_silu_mul_quant(const void* __restric
 // Fewer registers per thread than a wavefront per row, so that several rows
 // are in flight per CU while others compute.  The absmax, the scale and the
 // codes are the same as with a wavefront per row (max is exact in any order).
-// SILU: the row is h = SiLU(gate) * up (gate = x); otherwise the row of x
-// itself, the plain per-token quantizer of k_quant_rows (DT may be binary32).
-template <int DT, int CPT, bool SILU>
+// MODE kRowSilu: the row is h = SiLU(gate) * up (gate = x); kRowPlain: the
+// row of x itself, the plain per-token quantizer of k_quant_rows (DT may be
+// binary32); kRowAsym: the row of x on its own asymmetric grid, as
+// k_quant_rows<..., ASYM> (min and max reduced instead of the absmax, the
+// zero point into rowint).
+constexpr int kRowPlain = 0, kRowSilu = 1, kRowAsym = 2;
+template <int DT, int CPT, int MODE>
 __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restrict__ gate, int64_t ldg_bytes,
                                                            const void* __restrict__ up, int64_t ldu_bytes,
                                                            int64_t rows, int nch, int8_t* __restrict__ q,
-                                                           float* __restrict__ scale, void* __restrict__ h_out,
-                                                           int64_t ldh_bytes) {
+                                                           float* __restrict__ scale, int32_t* __restrict__ rowint,
+                                                           void* __restrict__ h_out, int64_t ldh_bytes) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row = blockIdx.x;
     const int ktiles = (nch + 7) / 8;
@@ -462,46 +466,80 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
     const char* ur = static_cast<const char*>(up) + row * ldu_bytes;
     uint4* hr = h_out ? reinterpret_cast<uint4*>(static_cast<char*>(h_out) + row * ldh_bytes) : nullptr;
     Raw8<DT> hv[CPT];
-    float amax = 0.0f;
+    float amax = 0.0f, lo = 0.0f, hi = 0.0f;  // the asymmetric range starts widened to contain 0
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = tid + 256 * i;
         const int cc = min(c, nch - 1);
-        if constexpr (SILU)
+        if constexpr (MODE == kRowSilu)
             hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
         else
             hv[i] = load_raw8<DT>(gr, cc);
         if (c >= nch) hv[i] = zero_raw8<DT>();
-        amax = chunk_absmax<DT>(hv[i], 0u, amax);
+        if constexpr (MODE == kRowAsym) {
+            float v[8];
+            widen8<DT>(hv[i], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lo = fminf(lo, v[j]);
+                hi = fmaxf(hi, v[j]);
+            }
+        } else {
+            amax = chunk_absmax<DT>(hv[i], 0u, amax);
+        }
     }
-    __shared__ float s_max[4];
-    amax = wave_max_full(amax);
-    if (lane == 0) s_max[wave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    const float s = absmax_step(amax);
+    __shared__ float s_red[2][4];
+    float s;
+    int zq = 0;
+    if constexpr (MODE == kRowAsym) {
+        hi = wave_max_full(hi);
+        lo = -wave_max_full(-lo);
+        if (lane == 0) {
+            s_red[0][wave] = hi;
+            s_red[1][wave] = lo;
+        }
+        __syncthreads();
+        hi = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+        lo = fminf(fminf(s_red[1][0], s_red[1][1]), fminf(s_red[1][2], s_red[1][3]));
+        // S = fl(fl(hi - lo) / 255), 1 for an empty range; Z = clamp(-128 - rne(fl(lo / S)), -128, 127)
+        s = hi == lo ? 1.0f : (hi - lo) / 255.0f;
+        zq = hi == lo ? 0 : min(max(-128 - (int)__builtin_rintf(lo / s), -128), 127);
+    } else {
+        amax = wave_max_full(amax);
+        if (lane == 0) s_red[0][wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+        s = absmax_step(amax);
+    }
     const float inv = 1.0f / s;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = tid + 256 * i;
-        const uint2 code = chunk_codes_absmax<DT, false>(hv[i], 0u, s, inv);
+        uint2 code;
+        if constexpr (MODE == kRowAsym)
+            code = chunk_codes_asym<DT>(hv[i], s, inv, zq);
+        else
+            code = chunk_codes_absmax<DT, false>(hv[i], 0u, s, inv);
         if (c < nch) {
             store_code(c, code);
-            if constexpr (SILU)
+            if constexpr (MODE == kRowSilu)
                 if (hr) hr[c] = hv[i].w[0];
         }
     }
     for (int c = nch + tid; c < ktiles * 8; c += 256) store_code(c, make_uint2(0u, 0u));  // K padding
-    if (tid == 0) scale[row] = s;
+    if (tid == 0) {
+        scale[row] = s;
+        if constexpr (MODE == kRowAsym) rowint[row] = zq;
+    }
 }
 
-template <int DT, int CPT, bool SILU = true>
+template <int DT, int CPT, int MODE = kRowSilu>
 void silu_mul_quant_wg(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int nch,
-                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st) {
+                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st, int32_t* rowint = nullptr) {
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
     constexpr int eb = Elem<DT>::bytes;
-    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, SILU>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate,
-                       ldg * eb, up, ldu * eb, rows, nch, q, scale, h, ldh * eb);
+    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, MODE>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate,
+                       ldg * eb, up, ldu * eb, rows, nch, q, scale, rowint, h, ldh * eb);
 }
 
 template <int DT, int CPL>
@@ -575,18 +613,30 @@ template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                    int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
-    if (!skip && !colsum && !asym && per_lane > 4 && per_lane <= 64) {
-        // the plain per-token quantizer of rows longer than 2048 values: a
-        // workgroup per row (more rows in flight per CU than a wavefront per row)
+    if (!skip && (asym || !colsum) && per_lane > 4 && per_lane <= 64) {
+        // the per-token quantizers (symmetric, or asymmetric with the zero
+        // points in `colsum`) of rows longer than 2048 values: a workgroup per
+        // row (more rows in flight per CU than a wavefront per row)
         const int nch = (int)(K / 8);
-        if (per_lane <= 8)
-            silu_mul_quant_wg<DT, 2, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
-        else if (per_lane <= 16)
-            silu_mul_quant_wg<DT, 4, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
-        else if (per_lane <= 32)
-            silu_mul_quant_wg<DT, 8, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
-        else
-            silu_mul_quant_wg<DT, 16, false>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        if (asym) {
+            if (per_lane <= 8)
+                silu_mul_quant_wg<DT, 2, kRowAsym>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st, colsum);
+            else if (per_lane <= 16)
+                silu_mul_quant_wg<DT, 4, kRowAsym>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st, colsum);
+            else if (per_lane <= 32)
+                silu_mul_quant_wg<DT, 8, kRowAsym>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st, colsum);
+            else
+                silu_mul_quant_wg<DT, 16, kRowAsym>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st, colsum);
+        } else {
+            if (per_lane <= 8)
+                silu_mul_quant_wg<DT, 2, kRowPlain>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+            else if (per_lane <= 16)
+                silu_mul_quant_wg<DT, 4, kRowPlain>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+            else if (per_lane <= 32)
+                silu_mul_quant_wg<DT, 8, kRowPlain>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+            else
+                silu_mul_quant_wg<DT, 16, kRowPlain>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st);
+        }
         return;
     }
     constexpr int kMaxCpl = DT == kF32 ? 16 : 32;
