@@ -949,3 +949,27 @@ def test_quantize_per_token_asym_long_rows(dtype, m, k):
     assert codes_equal(xq, q_ref)
     assert np.array_equal(host(xs).view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(host(xz), z_ref)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("m,n,k", [(2048, 10240, 64), (2000, 10000, 128)])
+def test_gemm_half_tile_last_round(m, n, k):
+    """Shapes whose last round of 256x256 tiles holds at most 128 tiles in whole
+    tile columns (320 tiles: 64 left over, 8 columns): those columns run as
+    half tiles in a second launch.  Every epilogue, exact against the oracle."""
+    assert pdq.gemm_kernel(m, n) == "tiled"
+    x = synth.activations(9900 + m, m, k, synth.choose_channels(9901, k, 3), 20.0, dtype="bf16")
+    w = synth.weights(9902 + m, n, k, "bf16")
+    b = synth.bias(9903, n)
+    prefill_case(x, w, "bf16", bias=b)
+    prefill_asym_case(x, w, "bf16", bias=b)
+    s, z = 0.0625, -5
+    decode_case(x, w, "bf16", s, z, bias=b)
+
+
+@pytest.mark.gpu
+def test_outlier_half_tile_last_round():
+    # 4 x 80 = 320 tiles: the last 16 tile columns as half tiles
+    x = synth.activations(9910, 1000, 256, synth.choose_channels(9911, 256, 4), 50.0, dtype="f16")
+    w = synth.weights(9912, 20400, 256, "f16")
+    outlier_case(x, w, "f16", 6.0, bias=synth.bias(9913, 20400))

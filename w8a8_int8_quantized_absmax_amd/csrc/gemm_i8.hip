@@ -101,7 +101,14 @@ __device__ __forceinline__ void wait_loads_and_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SIDE, int ZP>
+// MI: 32-row MFMA blocks per wave.  4: the 256x256 tile.  2: half of it,
+// rows [128 h, 128 h + 128) of the 256-row tile at m0 (h from the tile
+// index), computed by the 4 waves as 2x2 blocks of 64x128; the K tiles move
+// exactly as for the whole tile (same loads, same waits), the MFMAs and the A
+// fragment reads halve.  Used for a last round of at most 128 tiles, so that
+// it fills the 256 CUs with half the work each instead of leaving half of
+// them idle.
+template <int OUT, bool SIDE, int ZP, int MI>
 __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // The four K-tile buffers (each A[256][64] followed by B[256][64]) are
     // four separate LDS objects, and every access below names its buffer
@@ -130,14 +137,21 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
     const int M = a.M, N = a.N, K = a.K;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    int tm, tn, mh = 0;
+    if constexpr (MI == 4) {
+        tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    } else {
+        int th;
+        tile_of(blockIdx.x, 2 * tiles_m, tiles_n, th, tn);
+        tm = th >> 1;
+        mh = (th & 1) * 128;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int nkt = (K + BK - 1) / BK;
 
-    v16i acc[4][4];
+    v16i acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
@@ -183,8 +197,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     auto read_frags = [&](const uint8_t* sbase, int s, v4i (&fa)[4], v4i (&fb)[4]) {
         const int kc = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[i] = *reinterpret_cast<const v4i*>(sbase + swz(wm * 128 + i * 32 + (lane & 31), kc));
+        for (int i = 0; i < MI; ++i)
+            fa[i] = *reinterpret_cast<const v4i*>(
+                sbase + swz((MI == 4 ? wm * 128 : mh + wm * 64) + i * 32 + (lane & 31), kc));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             fb[j] = *reinterpret_cast<const v4i*>(sbase + BM * BK +
@@ -226,11 +241,15 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             read_frags(sb, 1, f1a, f1b);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     mfma(f0a, f0b, i, j);
-                    if (j & 1) issue_tile(sd, next, 2 * i + (j >> 1));
+                    if constexpr (MI == 4) {
+                        if (j & 1) issue_tile(sd, next, 2 * i + (j >> 1));
+                    } else {
+                        issue_tile(sd, next, 4 * i + j);  // 8 MFMAs, the same 8 loads
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             mfma(f1a, f1b, 0, 0);
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             read_frags(sn, 0, f0a, f0b);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (i | j) mfma(f1a, f1b, i, j);
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // tile with one 8-byte write; the tile then leaves in 16-byte row chunks.
     int side_steps = 0;
     bool poison = false;
-    const int ml0 = wm * 128 + (lane & 31);
+    const int ml0 = (MI == 4 ? wm * 128 : mh + wm * 64) + (lane & 31);
     const int nl0 = wn * 128 + 4 * (lane >> 5);
     [[maybe_unused]] uint4 xs0[4], ws0[4];
     if constexpr (SIDE) {
@@ -284,7 +303,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         if (side_steps > 0) {
             const int koff = 8 * (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < MI; ++i) {
                 const int m = min(m0 + ml0 + 32 * i, M - 1);
                 xs0[i] = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
             }
@@ -303,7 +322,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     float sam[4];
     [[maybe_unused]] int zam[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
         sam[i] = s_sa[ml0 + 32 * i];
         if constexpr (ZP == 2) zam[i] = -s_za[ml0 + 32 * i];  // negated: one multiply-add below
     }
@@ -319,12 +338,12 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int m = m0 + ml0 + 32 * i, n = n0 + nl0 + 32 * j + 8 * g;
                     if (m < M) {
-                        int32_t* ap = a.acc_out + (size_t)m * N + n;
+                        int32_t* ap = a.acc_out + (size_t)m * a.ldacc + n;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (n + e < N) ap[e] = acc[i][j][4 * g + e];
@@ -347,7 +366,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     if constexpr (ZP) zcv[g][e] = s_zc[nl0 + 32 * j + 8 * g + e];
                 }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < MI; ++i) {
                 const int ml = ml0 + 32 * i;
                 v16f side = v16f{};
                 if constexpr (SIDE) {
@@ -403,8 +422,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     uint16_t* y = static_cast<uint16_t*>(a.y);
     const bool vec = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (a.ldy % 8 == 0);
 #pragma unroll 4
-    for (int c = tid; c < BM * (BN / 8); c += 256) {
-        const int ml = c >> 5, nl = (c & 31) * 8;
+    for (int c = tid; c < MI * 64 * (BN / 8); c += 256) {
+        const int ml = (MI == 4 ? 0 : mh) + (c >> 5), nl = (c & 31) * 8;
         const int m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
         const uint2* src = reinterpret_cast<const uint2*>(yrow(ml) + nl * 2);
@@ -425,20 +444,53 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 
 }  // namespace
 
-void launch_gemm_i8(const GemmArgs& a, int out_dt, bool side, hipStream_t st, int zp_mode) {
-    if (a.M <= 0 || a.N <= 0) return;
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+template <int MI>
+void launch_tiles(const GemmArgs& a, int out_dt, bool side, hipStream_t st, int zp_mode) {
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (4 / MI);
     const dim3 grid(tiles), block(256);
     if (!side && zp_mode == 1)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 1>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 1, MI>), grid, block, 0, st, a);
     else if (!side && zp_mode == 2)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 2>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 2, MI>), grid, block, 0, st, a);
     else if (!side)
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 0>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, false, 0, MI>), grid, block, 0, st, a);
     else if (out_dt == kF16)
-        hipLaunchKernelGGL((k_gemm_i8<kF16, true, 0>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kF16, true, 0, MI>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8<kBF16, true, 0>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemm_i8<kBF16, true, 0, MI>), grid, block, 0, st, a);
+}
+
+// One tile per CU and round (one 160 KB workgroup fills a CU).  When the last
+// round would hold at most 128 tiles and they make up whole tile columns, those
+// columns run as a second launch of half tiles: twice the workgroups, half
+// the work each, so that the last round occupies all 256 CUs.
+void launch_gemm_i8(const GemmArgs& args, int out_dt, bool side, hipStream_t st, int zp_mode) {
+    if (args.M <= 0 || args.N <= 0) return;
+    GemmArgs a = args;
+    if (a.ldacc == 0) a.ldacc = a.N;  // the launches below may cover column ranges of it
+    constexpr int kCUs = 256;
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int tiles = tiles_m * tiles_n, last = tiles % kCUs;
+    const int cols = (tiles > kCUs && last > 0 && last <= kCUs / 2 && last % tiles_m == 0) ? last / tiles_m : 0;
+    if (cols == 0 || cols >= tiles_n) {
+        launch_tiles<4>(a, out_dt, side, st, zp_mode);
+        return;
+    }
+    const int n1 = (tiles_n - cols) * BN;  // whole tiles: columns [0, n1)
+    GemmArgs a1 = a;
+    a1.N = n1;
+    launch_tiles<4>(a1, out_dt, side, st, zp_mode);
+    // half tiles: columns [n1, N), every pointer indexed by n moved to column n1
+    GemmArgs a2 = a;
+    a2.N = a.N - n1;
+    a2.B = a.B + (size_t)(n1 / kWGroup) * ((a.K + BK - 1) / BK) * kWBlock;  // packed 16-row groups
+    a2.sb = a.sb + n1;
+    if (a.bias) a2.bias = a.bias + n1;
+    if (a.colsum) a2.colsum = a.colsum + n1;
+    a2.y = static_cast<uint16_t*>(a.y) + n1;
+    if (a.acc_out) a2.acc_out = a.acc_out + n1;
+    if (a.wo) a2.wo = a.wo + (size_t)n1 * a.P;
+    launch_tiles<2>(a2, out_dt, side, st, zp_mode);
 }
 
 }  // namespace pdq

@@ -69,7 +69,8 @@ struct GemmArgs {
     const float* bias;  // [N] or null
     void* y;
     int64_t ldy;
-    int32_t* acc_out;  // [M, N] dense or null
+    int32_t* acc_out;  // [M, N] or null, row pitch ldacc
+    int64_t ldacc;     // 0: N (set by launch_gemm_i8)
     // 16-bit side product (outlier decomposition), used when xo != null
     const uint16_t* xo;  // [M, P]
     const uint16_t* wo;  // [N, P]
