@@ -41,9 +41,11 @@
  *   - Floating-point matrices are row-major; leading dimensions (ld*) are in
  *     elements.  INT8 matrices (weights wq, activation codes xq) are in the
  *     packed tile layout described at pdq_quantize_weight.  Inner dimension K
- *     must be a multiple of 16 (at most 65536); every base pointer and every
- *     row pitch (ld * element size) of a K-wide operand must be a multiple of
- *     16 bytes.  Sizes may be 0 (nothing is written then).
+ *     must be a positive multiple of 16 (at most 65536; K == 0 is
+ *     PDQ_ERR_SHAPE, since every kernel reads at least one 16-value chunk of
+ *     each row it touches); every base pointer and every row pitch (ld *
+ *     element size) of a K-wide operand must be a multiple of 16 bytes.  M and
+ *     N may be 0 (nothing is written then).
  *   - Every argument check runs on the host before anything is enqueued; on
  *     error nothing is launched and no output is touched.  After the
  *     launches, a HIP launch error is reported as PDQ_ERR_HIP.
@@ -63,7 +65,7 @@ extern "C" {
 typedef enum {
     PDQ_OK = 0,
     PDQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
-    PDQ_ERR_SHAPE = 2,       /* negative size, K % 16 != 0, ld too small        */
+    PDQ_ERR_SHAPE = 2,       /* negative size, K not in 16, 32, .., 65536, ld too small */
     PDQ_ERR_DTYPE = 3,       /* dtype not accepted by this entry point          */
     PDQ_ERR_ALIGN = 4,       /* pointer or row pitch not 16-byte aligned        */
     PDQ_ERR_UNSUPPORTED = 5, /* value out of range (scale, zero point, ...)     */

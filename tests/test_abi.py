@@ -136,6 +136,23 @@ def test_outlier_validation(L):
     assert out8(L, w16=P + 1) == ALIGN
 
 
+def test_k_zero_is_refused_before_any_launch(L):
+    """K == 0 with rows present is a shape error on every entry point (the
+    pointers here are fake and never dereferenced: a launch would fault)."""
+    assert qw(L, K=0, ldw=0) == SHAPE
+    assert qw(L, N=0, K=0, ldw=0) == SHAPE
+    assert pre(L, K=0, ldx=0) == SHAPE
+    assert dec(L, K=0, ldx=0) == SHAPE
+    assert out8(L, K=0, ldx=0, ldw=0, maxo=0) == SHAPE
+    assert L.pdq_calibrate_static(P, 1, 4, 0, 0, P, None, None, None) == SHAPE
+    assert L.pdq_quantize_per_token(P, 1, 4, 0, 0, P, P, None) == SHAPE
+    assert L.pdq_quantize_per_token_asym(P, 1, 4, 0, 0, P, P, P, None) == SHAPE
+    assert L.pdq_gemm_per_token(P, P, 4, 0, P, P, None, 16, P, 16, None, None) == SHAPE
+    assert L.pdq_gemm_static(P, 4, 0, 0.5, 0, P, P, P, None, 16, P, 16, None, None) == SHAPE
+    assert L.pdq_quantize_static(P, 1, 4, 0, 0, 0.5, 0, P, None, None) == SHAPE
+    assert L.pdq_silu_mul_quantize_per_token(P, P, 1, 4, 0, 0, 0, P, P, None, 0, None) == SHAPE
+
+
 def test_weight_bytes(L):
     # ceil(N / 16) x ceil(K / 64) blocks of 1024 bytes
     assert L.pdq_weight_bytes(11008, 4096) == 688 * 64 * 1024 == 11008 * 4096

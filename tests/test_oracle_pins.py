@@ -328,6 +328,29 @@ def test_tensor_absmax_worked_example_and_saturation():
     check_tensor_absmax()
 
 
+def test_finalize_of_a_state_that_saw_nothing():
+    """Reading R8 (an empty range gets S = 1, Z = 0) on all three grids, for a
+    fresh observer state {+inf, -inf} (no batch seen) and for a state that saw
+    only zeros; the codes on that grid are then all 0.  A planted mistake --
+    finalising the fresh state without its empty-state branch -- gives an
+    infinite scale."""
+    fresh = (F32(np.inf), F32(-np.inf))
+    assert O.absmax_finalize(fresh) == F32(1)
+    assert O.minmax_finalize(fresh) == (F32(1), 0)
+    assert O.zeropoint_finalize(fresh) == (F32(1), 0)
+    zeros = O.minmax_update(None, np.zeros((3, 16), F32))
+    assert O.absmax_finalize(zeros) == F32(1)
+    assert O.minmax_finalize(zeros) == (F32(1), 0) and O.zeropoint_finalize(zeros) == (F32(1), 0)
+    q, sat = O.quantize_static_sym(np.zeros((2, 16), F32), O.absmax_finalize(fresh))
+    assert not q.any() and sat == 0
+
+    def no_empty_branch(state):
+        c = max(abs(F32(state[0])), abs(F32(state[1])))
+        return F32(O.absmax_scale(np.array([c], F32))[0])
+
+    assert not np.isfinite(no_empty_branch(fresh))
+
+
 def test_tensor_absmax_calibration_is_the_largest_magnitude():
     batches = [synth.activations(60 + b, 16, 128, [4], 30.0, offset=0.2, dtype="f32") for b in range(5)]
     batches[3][7, 9] = -500.0  # the largest magnitude, negative, in one batch

@@ -18,7 +18,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # IEEE binary32: correctly rounded division, no contraction into FMA,
     # denormals kept; the quantization codes depend on it.
     "-ffp-contract=off",
@@ -32,6 +31,11 @@ HIPCC_FLAGS = [
 ]
 
 
+def _quiet(text: str) -> str:
+    return "\n".join(line for line in text.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in line)
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,20 +44,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel), then link libpdq.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+        cmd = [cc, *HIPCC_FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, res.returncode, _quiet(res.stdout + res.stderr)
+
+    with ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 1, 8)) as ex:
+        results = list(ex.map(compile_one, sources))
+    for obj, rc, out in results:
+        if rc != 0:
+            raise RuntimeError(f"libpdq build failed ({obj}):\n{out}")
+        if verbose and out.strip():
+            print(out)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *sources, "-o", tmp]
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _, _ in results], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(
-        line for line in (res.stdout + res.stderr).splitlines()
-        if "packed-fp32-ops' is not a recognized feature" not in line
-    )
     if res.returncode != 0:
-        raise RuntimeError(f"libpdq build failed:\n{out}")
-    if verbose and out.strip():
-        print(out)
+        raise RuntimeError(f"libpdq link failed:\n{_quiet(res.stdout + res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -35,9 +35,10 @@ int elem_bytes(int dt) { return dt == PDQ_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == PDQ_F32 || dt == PDQ_BF16 || dt == PDQ_F16; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Shape rules shared by every K-wide operand.
+// Shape rules shared by every K-wide operand.  K == 0 is refused: the kernels
+// read at least one 16-value chunk of every row they touch.
 pdq_status check_mk(int64_t M, int64_t K, int64_t ld) {
-    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxK || K % 16 != 0) return PDQ_ERR_SHAPE;
+    if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxK || K % 16 != 0) return PDQ_ERR_SHAPE;
     if (ld < K || ld < 0) return PDQ_ERR_SHAPE;
     return PDQ_OK;
 }
@@ -71,7 +72,7 @@ const char* pdq_status_string(pdq_status s) {
     switch (s) {
         case PDQ_OK: return "ok";
         case PDQ_ERR_NULL: return "required pointer is NULL";
-        case PDQ_ERR_SHAPE: return "invalid shape (negative size, K % 16 != 0, K > 65536, or ld too small)";
+        case PDQ_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 16 up to 65536, or ld too small)";
         case PDQ_ERR_DTYPE: return "dtype not accepted by this entry point";
         case PDQ_ERR_ALIGN: return "pointer or row pitch not 16-byte aligned";
         case PDQ_ERR_UNSUPPORTED: return "argument value out of range";

@@ -330,35 +330,111 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         if (lane == 0) rowint[row] = zq;
 }
 
-// h = SiLU(g) * u for one chunk in binary32, rounded to DT (nearest even).
-// e = 2^(-|g| log2(e)) on the hardware exponential (v_exp_f32), r = 1 / (1 + e)
-// on the hardware reciprocal (v_rcp_f32, 1 ulp); sigmoid(g) = r for g >= 0 and
-// e r for g < 0.  e <= 1, so nothing overflows, and SiLU(g) -> -0 as g ->
-// -inf.  Relative error of the binary32 h: the rounded exponent argument
-// contributes |g| 2^-24 (for g >= 0 damped by e / (1 + e)), exp2 and the
-// reciprocal 1 ulp each, the three products half an ulp each -- within
-// (1.5 |g| + 8) 2^-24 while e is a normal number (|g| < 87).  Two
-// transcendental instructions per element instead of the library exponential
-// and a correctly rounded division keep the kernel on the memory roofline.
+// h = SiLU(g) * u, evaluated in binary64 and rounded once to DT's grid
+// (bf16: 8 significant bits, binary32's exponent range, spacing 2^-133 below
+// 2^-126; f16: 11 significant bits, spacing 2^-24 below 2^-14, values from
+// 65520 up round to infinity), returned as DT's bit pattern.  The rare path of
+// silu_mul8: the library's binary64 exponential and a correctly rounded
+// binary64 division, then one rounding by scaling the value's last kept place
+// to 1, rounding to the nearest integer (ties to even) and scaling back --
+// every step exact but the rounding.
+template <int DT>
+__device__ uint32_t silu_mul_exact16(float g, float u) {
+    constexpr int kSig = DT == kF16 ? 11 : 8;
+    constexpr int kEmin = DT == kF16 ? -13 : -125;  // frexp exponent of the smallest normal
+    const double gd = g;
+    const double v = gd / (1.0 + exp(-gd)) * (double)u;
+    int e;
+    (void)__builtin_frexp(v, &e);
+    e = max(e, kEmin);
+    const double r = __builtin_ldexp(__builtin_rint(__builtin_ldexp(v, kSig - e)), e - kSig);
+    if constexpr (DT == kF16) {
+        const float rf = fabs(r) > 65504.0 ? __builtin_copysignf(__builtin_inff(), (float)r) : (float)r;
+        return f32_to_f16(rf);  // exact: rf is on the binary16 grid (or infinite)
+    } else {
+        const float rf = fabs(r) >= 0x1p128 ? __builtin_copysignf(__builtin_inff(), (float)v) : (float)r;
+        return __float_as_uint(rf) >> 16;  // exact: rf has at most 8 significant bits
+    }
+}
+
+// Bound of the fast path (below): for |g| <= kSiluGMax its binary32 h is
+// within kSiluTol units in the last place of binary32 of SiLU(g) * u.  The
+// exponent argument x log2(e) is rounded twice (the binary32 log2(e) is within
+// 0.23 2^-24 of it, the product within 2^-24), which moves e by a relative
+// 1.224 |x| 2^-24; v_exp_f32 and v_rcp_f32 add one unit each, the sum 1 + e
+// and the two products half a unit each: within (1.224 |g| + 7) units,
+// 19.3 at |g| = 10, taken as 24.
+constexpr float kSiluGMax = 10.0f;
+constexpr uint32_t kSiluTol = 24;
+
+// Tie test on a binary32 bit pattern b: the low `drop` bits are what rounding
+// to DT discards (16 for bf16 at every magnitude; 13 for f16 in its normal
+// range), and a tie sits at half of that.  t = (b << (32 - drop)) + bias is
+// (discarded + kSiluTol - half) mod 2^drop in the top bits, at most `lim`
+// exactly when the discarded bits are within kSiluTol of the tie.
+template <int DT>
+struct SiluTie {
+    static constexpr int kDrop = DT == kF16 ? 13 : 16;
+    static constexpr uint32_t kBias = (kSiluTol - (1u << (kDrop - 1))) << (32 - kDrop);
+    static constexpr uint32_t kLim = (2u * kSiluTol) << (32 - kDrop);
+    static __device__ __forceinline__ uint32_t t(float p) {
+        return (__float_as_uint(p) << (32 - kDrop)) + kBias;
+    }
+};
+
+// h = SiLU(g) * u for one chunk, rounded to DT (nearest even), bit-identical to
+// silu_mul_exact16 of every element.  Fast path in binary32: e = 2^(-g
+// log2(e)) on the hardware exponential (v_exp_f32; e overflows to +inf for
+// very negative g and the product to -0, the limit), SiLU(g) = g * (1 / (1 +
+// e)) on the hardware reciprocal (v_rcp_f32), rounded to DT by the conversion
+// instruction: two transcendental instructions per element.  That rounding
+// is the correct one unless the binary32 value lies within the bound above of
+// a tie of DT's grid, or |g| exceeds the bound's range, or (f16) the value is
+// a nonzero binary16 subnormal, whose grid is coarser: such elements -- a few
+// in ten thousand -- are recomputed by silu_mul_exact16 in a branch that the
+// wavefront takes only when one of its lanes has one in this chunk.
 template <int DT>
 __device__ __forceinline__ Raw8<DT> silu_mul8(const Raw8<DT>& g, const Raw8<DT>& u) {
     constexpr float kLog2e = 1.44269504088896340736f;
-    float gv[8], uv[8];
+    float gv[8], uv[8], p[8];
     widen8<DT>(g, gv);
     widen8<DT>(u, uv);
     uint32_t w[4];
+    uint32_t tmin = 0xffffffffu, sub = 0xffffffffu;
+    float gmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-        float p[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float x = gv[j + t];
-            const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-            const float r = __builtin_amdgcn_rcpf(1.0f + e);
-            const float sg = x >= 0.0f ? r : e * r;
-            p[t] = (x * sg) * uv[j + t];
+        for (int k = 0; k < 2; ++k) {
+            const float x = gv[j + k];
+            const float e = __builtin_amdgcn_exp2f(-x * kLog2e);
+            p[j + k] = (x * __builtin_amdgcn_rcpf(1.0f + e)) * uv[j + k];
         }
-        w[j / 2] = f32x2_to_16<DT>(p[0], p[1]);
+        w[j / 2] = f32x2_to_16<DT>(p[j], p[j + 1]);
+        tmin = min(tmin, min(SiluTie<DT>::t(p[j]), SiluTie<DT>::t(p[j + 1])));
+        gmax = fmaxf(gmax, fmaxf(fabsf(gv[j]), fabsf(gv[j + 1])));
+        if constexpr (DT == kF16)  // |p| - 1 ulp as an integer: below 2^-14 - 1 ulp for nonzero subnormals
+            sub = min(sub, min((__float_as_uint(p[j]) & 0x7fffffffu) - 1u,
+                               (__float_as_uint(p[j + 1]) & 0x7fffffffu) - 1u));
+    }
+    const bool unsure = tmin <= SiluTie<DT>::kLim || !(gmax <= kSiluGMax) ||
+                        (DT == kF16 && sub < 0x387fffffu);
+    if (__builtin_expect(__any(unsure), 0)) {
+        // element by element, each branch taken only when a lane of the
+        // wavefront needs that element recomputed
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t pb = __float_as_uint(p[j]) & 0x7fffffffu;
+            const bool near = unsure && (SiluTie<DT>::t(p[j]) <= SiluTie<DT>::kLim || !(fabsf(gv[j]) <= kSiluGMax) ||
+                                         (DT == kF16 && pb - 1u < 0x387fffffu));
+            if (__builtin_expect(__any(near), 0)) {
+                if (near) {
+                    const uint32_t h16 = silu_mul_exact16<DT>(gv[j], uv[j]);
+                    const int sh = (j & 1) * 16;
+                    w[j >> 1] = (w[j >> 1] & ~(0xffffu << sh)) | (h16 << sh);
+                }
+            }
+        }
     }
     Raw8<DT> h;
     h.w[0] = make_uint4(w[0], w[1], w[2], w[3]);
