@@ -403,6 +403,36 @@ pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64
                                    void* workspace, size_t workspace_bytes, int32_t* acc_out,
                                    void* stream);
 
+/*
+ * pdq_linear_int8_outlier without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments, checks, results and
+ * kernels are those of pdq_linear_int8_outlier; the workspace is instead a
+ * scratch array compiled into the library, one copy per GPU (allocated when
+ * the library's code is loaded on that GPU, held until the process ends) of
+ * pdq_noalloc_scratch_bytes() = 8 MiB.  Calls whose
+ * pdq_linear_int8_outlier_workspace(M, N, K, max_outliers) exceeds that are
+ * refused with PDQ_ERR_WORKSPACE before anything is enqueued (the 2048 x 8192
+ * -> 28672 layer with 64 outlier columns needs 3.9 MB).  The stream must belong
+ * to the current device (else PDQ_ERR_UNSUPPORTED).  The first call on a
+ * device looks up that device's scratch address (a HIP symbol query, no
+ * allocation); no call allocates or frees memory.
+ *
+ * Every call on a GPU shares that GPU's scratch, and nothing in it carries
+ * over between calls (every byte a call reads, it first writes): calls that
+ * overlap in time on one GPU -- on different streams, or from different host
+ * threads without ordering -- race and give undefined results.  Calls on one
+ * stream are ordered and safe.
+ */
+size_t pdq_noalloc_scratch_bytes(void);
+
+pdq_status pdq_linear_int8_outlier_noalloc(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx,
+                                           float threshold, const int8_t* wq, const float* w_scale,
+                                           const void* w16, int64_t ldw, const float* bias, int64_t N,
+                                           void* y, int64_t ldy, int8_t* xq, float* x_scale,
+                                           int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers,
+                                           int32_t* acc_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,6 +153,30 @@ def test_k_zero_is_refused_before_any_launch(L):
     assert L.pdq_silu_mul_quantize_per_token(P, P, 1, 4, 0, 0, 0, P, P, None, 0, None) == SHAPE
 
 
+def out8na(L, x=P, dt=2, M=8, K=64, ldx=64, thr=6.0, wq=P, ws=P, w16=P, ldw=64, bias=None, N=16, y=P,
+           ldy=16, xq=P, xs=P, idx=P, cnt=P, maxo=8, acc=None):
+    return L.pdq_linear_int8_outlier_noalloc(x, dt, M, K, ldx, thr, wq, ws, w16, ldw, bias, N, y, ldy, xq, xs,
+                                             idx, cnt, maxo, acc, None)
+
+
+def test_outlier_noalloc_validation(L):
+    """The no-allocation variant runs the same host checks as the workspace
+    call, and refuses a problem whose workspace exceeds its fixed scratch
+    before any HIP call (these pointers are fake)."""
+    assert L.pdq_noalloc_scratch_bytes() == 8 << 20
+    assert out8na(L, dt=0) == DTYPE
+    assert out8na(L, thr=float("nan")) == UNSUP
+    assert out8na(L, maxo=65) == SHAPE
+    assert out8na(L, K=0, ldx=0, ldw=0, maxo=0) == SHAPE
+    assert out8na(L, cnt=None) == NULL
+    assert out8na(L, w16=P + 1) == ALIGN
+    ws = L.pdq_linear_int8_outlier_workspace
+    assert ws(2048, 28672, 8192, 64) <= 8 << 20            # the LLM.int8 layer fits
+    big_n = 70000
+    assert ws(2048, big_n, 8192, 64) > 8 << 20
+    assert out8na(L, M=2048, K=8192, ldx=8192, N=big_n, ldw=8192, ldy=big_n, maxo=64) == WS
+
+
 def test_weight_bytes(L):
     # ceil(N / 16) x ceil(K / 64) blocks of 1024 bytes
     assert L.pdq_weight_bytes(11008, 4096) == 688 * 64 * 1024 == 11008 * 4096

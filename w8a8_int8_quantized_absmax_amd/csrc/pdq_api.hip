@@ -4,11 +4,20 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "pdq.h"
 #include "pdq_device.h"
 #include "pdq_kernels.h"
 
 using namespace pdq;
+
+#define PDQ_TRY(expr)                         \
+    do {                                      \
+        const pdq_status s_ = (expr);         \
+        if (s_ != PDQ_OK) return s_;          \
+    } while (0)
+
 
 namespace {
 
@@ -60,11 +69,111 @@ int64_t side_pitch(int64_t max_out) { return (max_out + 15) / 16 * 16; }
 
 }  // namespace
 
-#define PDQ_TRY(expr)                         \
-    do {                                      \
-        const pdq_status s_ = (expr);         \
-        if (s_ != PDQ_OK) return s_;          \
-    } while (0)
+// Scratch of pdq_linear_int8_outlier_noalloc: one copy per device, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host it names a stand-in, not device memory): the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device current
+// and kept in scratch_ptr[device].
+namespace {
+
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char* scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device of `st` (the current device: a stream of
+// another device is refused).
+pdq_status scratch_for_stream(hipStream_t st, char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PDQ_ERR_HIP;
+    if (st) {
+        int sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) != hipSuccess) return PDQ_ERR_HIP;
+        if (sdev != dev) return PDQ_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PDQ_ERR_HIP;
+        scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = scratch_ptr[dev];
+    return PDQ_OK;
+}
+
+// Host-side checks of the LLM.int8 call, shared by both of its entry points
+// (no HIP call).
+pdq_status check_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx, float threshold,
+                              const int8_t* wq, const float* w_scale, const void* w16, int64_t ldw,
+                              const float* bias, int64_t N, void* y, int64_t ldy, int8_t* xq, float* x_scale,
+                              int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers, int32_t* acc_out) {
+    if (dt != PDQ_F16 && dt != PDQ_BF16) return PDQ_ERR_DTYPE;
+    PDQ_TRY(check_operand(x, elem_bytes(dt), M, K, ldx));
+    PDQ_TRY(check_operand(wq, 1, N, K, K));
+    if (N < 0 || N > kMaxDim || ldy < N || ldw < K) return PDQ_ERR_SHAPE;
+    if (max_outliers < 0 || max_outliers > K) return PDQ_ERR_SHAPE;
+    if (isnan(threshold)) return PDQ_ERR_UNSUPPORTED;
+    if (!n_outlier || (max_outliers > 0 && !outlier_idx)) return PDQ_ERR_NULL;
+    if (N > 0 && (!w_scale || (K > 0 && !w16))) return PDQ_ERR_NULL;
+    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
+    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
+        !aligned(y, 2) || !aligned(w16, 2) || !aligned(acc_out, 4) || !aligned(outlier_idx, 4) ||
+        !aligned(n_outlier, 4))
+        return PDQ_ERR_ALIGN;
+    return PDQ_OK;
+}
+
+// The launches of the LLM.int8 call on a workspace of at least
+// pdq_linear_int8_outlier_workspace(M, N, K, max_outliers) bytes, 256-byte
+// aligned: predicates per row block -> mask, index list, count and the W
+// gather -> INT8 codes of the regular columns with the X gather -> INT8 GEMM
+// with the 16-bit side product in its epilogue.  Every byte of the workspace
+// that is read is first written by the same call.
+void run_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx, float threshold,
+                      const int8_t* wq, const float* w_scale, const void* w16, int64_t ldw, const float* bias,
+                      int64_t N, void* y, int64_t ldy, int8_t* xq, float* x_scale, int32_t* outlier_idx,
+                      int32_t* n_outlier, int64_t max_outliers, char* ws, int32_t* acc_out, hipStream_t st) {
+    const int64_t P = side_pitch(max_outliers);
+    const size_t pitch = (size_t)outlier_partial_pitch(K);
+    uint8_t* partial = reinterpret_cast<uint8_t*>(ws);
+    ws += align256((size_t)outlier_row_blocks(M) * pitch);
+    uint8_t* mask = reinterpret_cast<uint8_t*>(ws);
+    ws += align256(pitch);
+    uint16_t* xo = reinterpret_cast<uint16_t*>(ws);
+    ws += align256((size_t)(M * P * 2));
+    uint16_t* wo = reinterpret_cast<uint16_t*>(ws);
+
+    launch_outlier_partial(x, dt, M, K, ldx, threshold, partial, st);
+    launch_outlier_index(partial, M, K, mask, outlier_idx, n_outlier, max_outliers, w16, N, ldw, wo,
+                         (int)P, st);
+    if (M > 0) {
+        const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
+        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
+    }
+    GemmArgs g{};
+    g.A = xq;
+    g.B = wq;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.sa = x_scale;
+    g.sb = w_scale;
+    g.bias = bias;
+    g.y = y;
+    g.ldy = ldy;
+    g.acc_out = acc_out;
+    g.xo = xo;
+    g.wo = wo;
+    g.P = (int)P;
+    g.count = n_outlier;
+    g.max_count = (int)max_outliers;
+    launch_gemm_i8(g, dt, true, st);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -567,64 +676,35 @@ pdq_status pdq_linear_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64
                                    int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers,
                                    void* workspace, size_t workspace_bytes, int32_t* acc_out,
                                    void* stream) {
-    if (dt != PDQ_F16 && dt != PDQ_BF16) return PDQ_ERR_DTYPE;
-    PDQ_TRY(check_operand(x, elem_bytes(dt), M, K, ldx));
-    PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N || ldw < K) return PDQ_ERR_SHAPE;
-    if (max_outliers < 0 || max_outliers > K) return PDQ_ERR_SHAPE;
-    if (isnan(threshold)) return PDQ_ERR_UNSUPPORTED;
-    if (!n_outlier || (max_outliers > 0 && !outlier_idx)) return PDQ_ERR_NULL;
-    if (N > 0 && (!w_scale || (K > 0 && !w16))) return PDQ_ERR_NULL;
-    if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
-    if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
-    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(bias, 4) ||
-        !aligned(y, 2) || !aligned(w16, 2) || !aligned(acc_out, 4) || !aligned(outlier_idx, 4) ||
-        !aligned(n_outlier, 4))
-        return PDQ_ERR_ALIGN;
+    PDQ_TRY(check_int8_outlier(x, dt, M, K, ldx, threshold, wq, w_scale, w16, ldw, bias, N, y, ldy, xq,
+                               x_scale, outlier_idx, n_outlier, max_outliers, acc_out));
     const size_t need = pdq_linear_int8_outlier_workspace(M, N, K, max_outliers);
     if (!workspace || workspace_bytes < need) return PDQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return PDQ_ERR_ALIGN;
+    run_int8_outlier(x, dt, M, K, ldx, threshold, wq, w_scale, w16, ldw, bias, N, y, ldy, xq, x_scale,
+                     outlier_idx, n_outlier, max_outliers, static_cast<char*>(workspace), acc_out,
+                     static_cast<hipStream_t>(stream));
+    return launched();
+}
 
+size_t pdq_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pdq_status pdq_linear_int8_outlier_noalloc(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t ldx,
+                                           float threshold, const int8_t* wq, const float* w_scale,
+                                           const void* w16, int64_t ldw, const float* bias, int64_t N,
+                                           void* y, int64_t ldy, int8_t* xq, float* x_scale,
+                                           int32_t* outlier_idx, int32_t* n_outlier, int64_t max_outliers,
+                                           int32_t* acc_out, void* stream) {
+    PDQ_TRY(check_int8_outlier(x, dt, M, K, ldx, threshold, wq, w_scale, w16, ldw, bias, N, y, ldy, xq,
+                               x_scale, outlier_idx, n_outlier, max_outliers, acc_out));
+    if (pdq_linear_int8_outlier_workspace(M, N, K, max_outliers) > kScratchBytes) return PDQ_ERR_WORKSPACE;
+    // the argument checks above make no HIP call; from here on the device's
+    // own copy of the scratch array is looked up (once per device)
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t P = side_pitch(max_outliers);
-    const size_t pitch = (size_t)outlier_partial_pitch(K);
-    char* ws = static_cast<char*>(workspace);
-    uint8_t* partial = reinterpret_cast<uint8_t*>(ws);
-    ws += align256((size_t)outlier_row_blocks(M) * pitch);
-    uint8_t* mask = reinterpret_cast<uint8_t*>(ws);
-    ws += align256(pitch);
-    uint16_t* xo = reinterpret_cast<uint16_t*>(ws);
-    ws += align256((size_t)(M * P * 2));
-    uint16_t* wo = reinterpret_cast<uint16_t*>(ws);
-
-    // predicates per row block -> mask, index list, count and the W gather
-    // -> INT8 codes of the regular columns with the X gather -> INT8 GEMM
-    // with the 16-bit side product in its epilogue
-    launch_outlier_partial(x, dt, M, K, ldx, threshold, partial, st);
-    launch_outlier_index(partial, M, K, mask, outlier_idx, n_outlier, max_outliers, w16, N, ldw, wo,
-                         (int)P, st);
-    if (M > 0) {
-        const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
-        launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
-    }
-    GemmArgs g{};
-    g.A = xq;
-    g.B = wq;
-    g.M = (int)M;
-    g.N = (int)N;
-    g.K = (int)K;
-    g.sa = x_scale;
-    g.sb = w_scale;
-    g.bias = bias;
-    g.y = y;
-    g.ldy = ldy;
-    g.acc_out = acc_out;
-    g.xo = xo;
-    g.wo = wo;
-    g.P = (int)P;
-    g.count = n_outlier;
-    g.max_count = (int)max_outliers;
-    launch_gemm_i8(g, dt, true, st);
+    char* ws = nullptr;
+    PDQ_TRY(scratch_for_stream(st, &ws));
+    run_int8_outlier(x, dt, M, K, ldx, threshold, wq, w_scale, w16, ldw, bias, N, y, ldy, xq, x_scale,
+                     outlier_idx, n_outlier, max_outliers, ws, acc_out, st);
     return launched();
 }
 

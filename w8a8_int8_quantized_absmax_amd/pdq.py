@@ -63,6 +63,10 @@ SIGNATURES = {
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _i64, _vp, _sz, _vp, _vp]),
+    "pdq_noalloc_scratch_bytes": (_sz, []),
+    "pdq_linear_int8_outlier_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
+                                                       _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                                       _i64, _vp, _vp]),
 }
 
 _lib = None
@@ -422,6 +426,33 @@ def linear_int8_outlier(x, threshold: float, wq, w_scale, w16, bias=None, max_ou
           _p(w_scale), _p(w16), _ld(w16), _p(bias), n, _p(y), _ld(y), _p(xq), _p(xs), _p(idx),
           _p(cnt), max_outliers, _p(workspace), workspace.numel(), _p(acc), _stream(dev))
     return dict(y=y, xq=xq, x_scale=xs, idx=idx, count=cnt, acc=acc)
+
+
+def linear_int8_outlier_noalloc(x, threshold: float, wq, w_scale, w16, bias=None, max_outliers: int = 64,
+                                want_acc: bool = False, out=None, xq=None, x_scale=None, idx=None, count=None):
+    """linear_int8_outlier on the library's own scratch instead of a workspace (the
+    call itself allocates nothing; outputs not given are allocated here)."""
+    _check_mat(x, "x")
+    _check_mat(w16, "w16")
+    m, k = x.shape
+    n = w_scale.shape[0]
+    _check_weight(wq, n, k)
+    dev = x.device
+    max_outliers = min(max_outliers, k)
+    xq = _codes_out(xq, m, k, dev)
+    xs = x_scale if x_scale is not None else torch.empty(m, dtype=torch.float32, device=dev)
+    idx = idx if idx is not None else torch.empty(max(max_outliers, 1), dtype=torch.int32, device=dev)
+    cnt = count if count is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    y = out if out is not None else torch.empty((m, n), dtype=x.dtype, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+    _call("pdq_linear_int8_outlier_noalloc", _p(x), _DT[x.dtype], m, k, _ld(x), float(threshold), _p(wq),
+          _p(w_scale), _p(w16), _ld(w16), _p(bias), n, _p(y), _ld(y), _p(xq), _p(xs), _p(idx),
+          _p(cnt), max_outliers, _p(acc), _stream(dev))
+    return dict(y=y, xq=xq, x_scale=xs, idx=idx, count=cnt, acc=acc)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().pdq_noalloc_scratch_bytes())
 
 
 def quantize_per_token(x, xq=None, x_scale=None):
