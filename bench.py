@@ -19,9 +19,17 @@ the block's four linears (QKV, O, gate+up, down at hidden 4096) on one shared
 INT8 weight copy each: a prefill pass over 8192 tokens and 256 decode steps
 at batch 32; under "silu_mul_quant" the down projection's input SiLU(gate) * up
 (8192 x 14336) quantized by the fused kernel, against the unfused pair, and the
-whole down projection.
+whole down projection; under "cs_cg" the quantizer and GEMM costs (C_s, C_g)
+of per-token dynamic against per-tensor static activations at M = 1, 64,
+512, 4096 on the decode linear.
 
-cpu_baseline: the CPU oracle timed on the host on the same prefill workload.
+Every timed region that follows host-side setup is preceded by 200 ms of
+untimed work of its own kind (the clock ramps up over the first ~35 ms after
+the GPU idles); "cold_start" reports the headline step timed without it.
+
+cpu_baseline: the CPU oracle timed on the host: whole prefill linears (its
+`value`), the linear stage by stage, the decode linear at M = 1 .. 64, the
+LLM.int8() layer, and one-thread times of the tiny and M = 1 workloads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -99,6 +107,70 @@ def graph_timed(fn, calls: int, replays: int, stream) -> float:
     return ms
 
 
+SETTLE_MS = 200.0  # untimed work before a timed region that follows host-side setup
+
+
+def settle(fn, stream, ms: float = SETTLE_MS) -> int:
+    """Run fn(i) untimed for about `ms` milliseconds of GPU time.
+
+    After the GPU has been idle (here: while the host generates the next
+    workload's inputs), the first ~35 ms of back-to-back launches run up to
+    30% slower while the power management raises the clock (measured: the
+    prefill GEMM 190-250 us over its first ~200 launches after a pause of 1-3
+    s, 160-163 us after; the same on the same buffers, so no first-touch
+    effect).  Every timed region that follows host-side work is preceded by
+    this, so that it measures the steady state; the cold-start figure is
+    reported separately."""
+    import torch
+
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def sample_sclk(fn, ms: float = 600.0):
+    """Shader clock (MHz) that rocm-smi reports while fn(i) runs back to back
+    for about `ms` milliseconds (untimed; None where rocm-smi is unavailable)."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                                     timeout=5).stdout
+                m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out)
+                if m:
+                    samples.append(int(m.group(1)))
+            except Exception:
+                return
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=6)
+    if not samples:
+        return None
+    samples.sort()
+    return {"median_MHz": samples[len(samples) // 2], "min_MHz": samples[0], "max_MHz": samples[-1],
+            "samples": len(samples)}
+
+
 def kernel_hash() -> str:
     with open(GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -136,6 +208,7 @@ def bench_prefill(args, torch, pdq, synth):
         pdq._call("pdq_linear_prefill", pdq._p(xs[r]), pdq.BF16, M, K, K, pdq._p(wqs[r]), pdq._p(ws),
                   None, N, pdq._p(xqs[r]), pdq._p(xsc), pdq._p(y), N, None, pdq._stream(x.device))
 
+    settle(step, stream)
     ms_step = timed(step, args.steps, args.warmup, stream)
 
     # the INT8 GEMM kernel alone (same launch configuration as inside the step)
@@ -199,12 +272,22 @@ def bench_prefill(args, torch, pdq, synth):
     for r in range(nrot):  # codes, scales and zero points of every activation copy
         quant_asym(r)
     ms_gemm_asym = timed(gemm_asym, asym_steps, args.warmup // 2, stream)
+    for r in range(nrot):  # symmetric codes again for the GEMM-only figures below
+        pdq.quantize_per_token(xs[r], xq=xqs[r], x_scale=xsc)
+    # the shader clock while the GEMM runs back to back (untimed)
+    sclk = sample_sclk(gemm)
+    # cold start: the same step timed as above but right after the GPU has
+    # been idle for 1.5 s, without the settling phase
+    torch.cuda.synchronize()
+    time.sleep(1.5)
+    ms_step_cold = timed(step, args.steps, args.warmup, stream)
     ops = 2.0 * M * N * K
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     gemm_bytes = M * K + N * K + 4 * (M + N) + 2 * M * N  # xq, wq, scales, bf16 y
     quant_bytes = 2 * M * K + M * K + 4 * M
     del wqs, xs, xqs
     return dict(M=M, K=K, N=N, ms_step=ms_step, ms_gemm=ms_gemm, ms_quant=ms_quant, ops=ops,
+                ms_step_cold=ms_step_cold, sclk=sclk,
                 ms_step_asym=ms_step_asym, ms_quant_asym=ms_quant_asym, ms_gemm_asym=ms_gemm_asym,
                 ms_lib=ms_lib,
                 gemm_tops=gemm_tops, gemm_bytes=gemm_bytes, quant_bytes=quant_bytes,
@@ -258,6 +341,7 @@ def bench_decode(args, torch, pdq, synth):
                       pdq._p(cs), None, N, pdq._p(y), N, None, pdq._stream(x.device))
 
         iters = max(args.steps * 10, 200)
+        settle(call, stream)
         ms_call = timed(call, iters, args.warmup * 4, stream)
         ms_gemv = timed(gemv, iters, args.warmup * 4, stream)
         # the same calls replayed from a HIP graph (one call per weight copy)
@@ -295,11 +379,63 @@ def bench_decode(args, torch, pdq, synth):
                            gemv_frac=gemv_bytes / (ms_gemv * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            saturated=nsat, saturated_frac=nsat / (m * K),
                            us_call_static_sym_graph=ms_sym_g * 1e3, us_call_zeropoint_graph=ms_zp_g * 1e3)
-    del wqs
-    return dict(S=s, Z=z, S_sym=s_sym, S_zp=s_zp, Z_zp=z_zp, K=K, N=N, per_batch=res)
+    # the C_s / C_g pair at a few M, over 16 of the weight copies (the --sweep
+    # protocol; the full sweep over M = 1 .. 8192 is `bench.py --sweep`)
+    x_all = torch.from_numpy(c.x(max(SWEEP_M))).to(torch.bfloat16).cuda()
+    cs_cg = {str(m): cs_cg_point(torch, pdq, m, x_all, s, z, wqs, ws, cs, 16, 10 if m <= 256 else 4)
+             for m in CS_CG_M}
+    del wqs, x_all
+    return dict(S=s, Z=z, S_sym=s_sym, S_zp=s_zp, Z_zp=z_zp, K=K, N=N, per_batch=res, cs_cg=cs_cg)
 
 
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
+
+
+CS_CG_M = (1, 64, 512, 4096)  # the compact C_s / C_g figures of the default run
+
+
+def cs_cg_point(torch, pdq, m, x_all, s, z, wqs, ws, cs, nrot, replays):
+    """C_s and C_g of one M on the decode linear: per-token dynamic
+    (quantize_per_token + gemm_per_token) and per-tensor static
+    (quantize_static + gemm_static, and the one-launch decode call where it
+    applies), each from HIP-graph replays of nrot calls over the rotated
+    weight copies."""
+    K, N = x_all.shape[1], ws.shape[0]
+    x = x_all[:m]
+    xq = torch.empty(pdq.act_bytes(m, K), dtype=torch.int8, device="cuda")  # packed codes
+    xsc = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def dq(i):
+        pdq._call("pdq_quantize_per_token", pdq._p(x), pdq.BF16, m, K, K, pdq._p(xq), pdq._p(xsc), pdq._stream(x.device))
+
+    def dg(i):
+        pdq._call("pdq_gemm_per_token", pdq._p(xq), pdq._p(xsc), m, K, pdq._p(wqs[i % nrot]), pdq._p(ws),
+                  None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+    def sq(i):
+        pdq._call("pdq_quantize_static", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(xq), None, pdq._stream(x.device))
+
+    def sg(i):
+        pdq._call("pdq_gemm_static", pdq._p(xq), m, K, s, z, pdq._p(wqs[i % nrot]), pdq._p(ws), pdq._p(cs),
+                  None, N, pdq._p(y), N, None, pdq._stream(x.device))
+
+    def call(i):
+        pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(wqs[i % nrot]),
+                  pdq._p(ws), pdq._p(cs), None, N, pdq._p(xq), pdq._p(y), N, None, None, pdq._stream(x.device))
+
+    dq(0)
+    settle(dg, stream, 50.0)
+    t = {name: graph_timed(fn, nrot, replays, stream) * 1e3
+         for name, fn in (("dyn_quant", dq), ("dyn_gemm", dg), ("static_quant", sq),
+                          ("static_gemm", sg), ("static_call", call))}
+    t["dyn_total"] = t["dyn_quant"] + t["dyn_gemm"]
+    t["static_total"] = t["static_quant"] + t["static_gemm"]
+    t["dyn_Cs_over_Cg"] = t["dyn_quant"] / t["dyn_gemm"]
+    t["static_Cs_over_Cg"] = t["static_quant"] / t["static_gemm"]
+    t["gemm_TOPS_dyn"] = 2.0 * m * N * K / (t["dyn_gemm"] * 1e-6) / 1e12
+    return {k: round(v, 3) for k, v in t.items()}
 
 
 def bench_sweep(args, torch, pdq, synth):
@@ -321,44 +457,11 @@ def bench_sweep(args, torch, pdq, synth):
     wq0, ws, cs = pdq.quantize_weight(torch.from_numpy(c.w()).to(torch.bfloat16).cuda())
     nrot = 16
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
-    mmax = max(SWEEP_M)
-    x_all = torch.from_numpy(c.x(mmax)).to(torch.bfloat16).cuda()
-    stream = torch.cuda.current_stream()
+    x_all = torch.from_numpy(c.x(max(SWEEP_M))).to(torch.bfloat16).cuda()
     rows = {}
     for m in SWEEP_M:
-        x = x_all[:m]
-        xq = torch.empty(pdq.act_bytes(m, K), dtype=torch.int8, device="cuda")  # packed codes
-        xsc = torch.empty(m, dtype=torch.float32, device="cuda")
-        y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
-        replays = 20 if m <= 256 else 4
-
-        def dq(i):
-            pdq._call("pdq_quantize_per_token", pdq._p(x), pdq.BF16, m, K, K, pdq._p(xq), pdq._p(xsc), pdq._stream(x.device))
-
-        def dg(i):
-            pdq._call("pdq_gemm_per_token", pdq._p(xq), pdq._p(xsc), m, K, pdq._p(wqs[i % nrot]), pdq._p(ws),
-                      None, N, pdq._p(y), N, None, pdq._stream(x.device))
-
-        def sq(i):
-            pdq._call("pdq_quantize_static", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(xq), None, pdq._stream(x.device))
-
-        def sg(i):
-            pdq._call("pdq_gemm_static", pdq._p(xq), m, K, s, z, pdq._p(wqs[i % nrot]), pdq._p(ws), pdq._p(cs),
-                      None, N, pdq._p(y), N, None, pdq._stream(x.device))
-
-        def call(i):
-            pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(wqs[i % nrot]),
-                      pdq._p(ws), pdq._p(cs), None, N, pdq._p(xq), pdq._p(y), N, None, None, pdq._stream(x.device))
-
-        t = {name: graph_timed(fn, nrot, replays, stream) * 1e3
-             for name, fn in (("dyn_quant", dq), ("dyn_gemm", dg), ("static_quant", sq),
-                              ("static_gemm", sg), ("static_call", call))}
-        t["dyn_total"] = t["dyn_quant"] + t["dyn_gemm"]
-        t["static_total"] = t["static_quant"] + t["static_gemm"]
-        t["dyn_Cs_over_Cg"] = t["dyn_quant"] / t["dyn_gemm"]
-        t["static_Cs_over_Cg"] = t["static_quant"] / t["static_gemm"]
-        t["gemm_TOPS_dyn"] = 2.0 * m * N * K / (t["dyn_gemm"] * 1e-6) / 1e12
-        rows[str(m)] = {k: round(v, 3) for k, v in t.items()}
+        t = cs_cg_point(torch, pdq, m, x_all, s, z, wqs, ws, cs, nrot, 20 if m <= 256 else 4)
+        rows[str(m)] = t
         log(f"[sweep] M={m:5d}: dynamic {t['dyn_quant']:8.2f} + {t['dyn_gemm']:8.2f} us, static "
             f"{t['static_quant']:8.2f} + {t['static_gemm']:8.2f} us (one call {t['static_call']:8.2f} us)")
     del wqs
@@ -398,6 +501,7 @@ def bench_silu_mul(args, torch, pdq, synth):
         pdq._call("pdq_linear_prefill_silu_mul", pdq._p(gate), pdq._p(up), pdq.BF16, M, K, 2 * K, 2 * K,
                   pdq._p(wq), pdq._p(ws), None, n_down, pdq._p(xq), pdq._p(xs), pdq._p(y), n_down, None, dv)
 
+    settle(fused, stream)
     ms_fused = timed(fused, 20, 5, stream)
     ms_unfused = timed(unfused, 10, 3, stream)
     ms_linear = timed(linear, 10, 3, stream)
@@ -485,6 +589,7 @@ def bench_block(args, torch, pdq, synth):
                       pdq._p(d["ws"]), None, d["n"], pdq._p(d["xq"]), pdq._p(d["xs"]), pdq._p(d["y"]), d["n"], None,
                       pdq._stream(d["x"].device))
 
+    settle(prefill, stream)
     ms_prefill = timed(prefill, max(args.steps // 5, 5), max(args.warmup // 10, 3), stream)
     ops = sum(2.0 * M * d["n"] * d["k"] for d in lin)
     for d in lin:
@@ -503,6 +608,7 @@ def bench_block(args, torch, pdq, synth):
                       pdq._p(d["wqs"][t % nrot]), pdq._p(d["ws"]), pdq._p(d["cs"]), None, d["n"], pdq._p(d["xq"]),
                       pdq._p(d["y"]), d["n"], None, None, pdq._stream(x.device))
 
+    settle(lambda i: step(i % T), stream)
     ms_step = graph_timed(step, T, 2, stream)
     wbytes = sum(d["n"] * d["k"] for d in lin)
     step_bytes = sum(d["n"] * d["k"] + 2 * B * d["k"] + 2 * B * d["n"] + 8 * d["n"] for d in lin)
@@ -515,8 +621,9 @@ def bench_llm_int8(args, torch, pdq, synth):
     c = synth.LlmInt8()
     M, K, N = c.M, c.K, c.N
     log(f"[llm.int8] generating X[{M},{K}] and W[{N},{K}] ({c.dtype})")
-    x = torch.from_numpy(c.x()).half().cuda()
-    w16 = torch.from_numpy(c.w()).half().cuda()
+    x_host, w_host = c.x(), c.w()
+    x = torch.from_numpy(x_host).half().cuda()
+    w16 = torch.from_numpy(w_host).half().cuda()
     wq0, ws, _ = pdq.quantize_weight(w16)
     nrot = 2
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
@@ -536,43 +643,145 @@ def bench_llm_int8(args, torch, pdq, synth):
                   pdq._p(xs), pdq._p(idx), pdq._p(cnt), max_out, pdq._p(work), ws_bytes, None,
                   pdq._stream(x.device))
 
+    settle(call, stream)
     ms = timed(call, args.steps, args.warmup, stream)
     n_out = int(cnt.item())
     ops = 2.0 * M * N * K
     return dict(M=M, K=K, N=N, ms=ms, n_outlier=n_out, int8_tops=ops / (ms * 1e-3) / 1e12,
+                host=(x_host, w_host, c.threshold),
                 side_flops=2.0 * M * N * n_out)
 
 
-def cpu_baseline(pre):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pre, synth, llm_host=None, dec=None):
+    """The oracle (plain numpy, binary64 BLAS for the exact integer products)
+    timed on this host's cores: whole prefill linears (the headline workload,
+    `value`), the same linear stage by stage, the offline steps, the decode
+    linear at M = 1, 8, 32, 64 (GB/s over the same algorithmic bytes as the
+    GPU figures), the LLM.int8() layer (TOPS of its INT8 product), and the tiny
+    and M = 1 decode workloads on one thread.  About 20 s of host time."""
     import oracle.pdq_oracle as O
 
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        threadpool_limits, blas_threads = None, os.cpu_count() or 1
+    cores = len(os.sched_getaffinity(0))
+    clock = time.perf_counter
+    out = {"unit": "TOPS", "kind": "oracle", "cores": cores, "blas_threads": int(blas_threads),
+           "cpu_model": _cpu_model()}
     x, w = pre["x_host"], pre["w_host"]
-    wq, sw, _ = O.quantize_weight(w)  # offline, not timed
-    # whole prefill linears, repeated until about 10 s of host time (at most 30)
-    runs, t0 = 0, time.perf_counter()
+    M, K, N = pre["M"], pre["K"], pre["N"]
+    t0 = clock()
+    wq, sw, _ = O.quantize_weight(w)
+    t_wq = clock() - t0
+    # whole prefill linears, repeated until about 6 s (at least 2 runs)
+    runs, t0 = 0, clock()
     while True:
         O.linear_prefill(x, wq, sw)
         runs += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or runs >= 30:
+        dt = clock() - t0
+        if (dt >= 6.0 and runs >= 2) or runs >= 30:
             break
-    return {"value": pre["ops"] * runs / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} full prefill linears {pre['M']}x{pre['K']}->{pre['N']} (per-token quant, "
-                      f"exact integer GEMM via a binary64 BLAS product, binary32 epilogue) in {dt:.1f} s"}
+    out["value"] = pre["ops"] * runs / dt / 1e12
+    out["sample"] = (f"{runs} full prefill linears {M}x{K}->{N} (per-token quant, exact integer GEMM via a "
+                     f"binary64 BLAS product, binary32 epilogue) in {dt:.1f} s")
+    # the same linear stage by stage
+    t0 = clock()
+    xq, sx = O.quantize_rows_absmax(x)
+    t_q = clock() - t0
+    t0 = clock()
+    acc = O.int_matmul(xq, wq)
+    t_g = clock() - t0
+    t0 = clock()
+    O.dequantize(acc, sx, sw)
+    t_e = clock() - t0
+    del acc
+    out["prefill_stages_s"] = {"quantize_per_token": round(t_q, 4), "int_gemm": round(t_g, 4),
+                               "dequant_epilogue": round(t_e, 4), "weight_quant_offline": round(t_wq, 4)}
+    out["prefill_quant_GBps"] = round((2 * M * K + M * K + 4 * M) / t_q / 1e9, 3)
+    out["prefill_gemm_TOPS"] = round(pre["ops"] / t_g / 1e12, 4)
+    # decode linear 4096 -> 4096 with the calibrated static (S, Z)
+    c = synth.Decode()
+    wd = c.w()
+    wqd, swd, csd = O.quantize_weight(wd)
+    cal = [c.calib(b) for b in range(10)]
+    t0 = clock()
+    state = None
+    for xb in cal:
+        state = O.minmax_update(state, xb)
+    O.minmax_finalize(state)
+    out["calibration_s_per_batch"] = round((clock() - t0) / len(cal), 5)
+    s_dec, z_dec = (dec["S"], dec["Z"]) if dec else O.calibrate(cal)[1:]
+    dec_out = {}
+    for m in c.batches:
+        xm = c.x(m)
+        reps, t0 = 0, clock()
+        while True:
+            O.linear_decode(xm, np.float32(s_dec), z_dec, wqd, swd, csd)
+            reps += 1
+            if clock() - t0 >= 0.5 and reps >= 3:
+                break
+        us = (clock() - t0) / reps * 1e6
+        nbytes = c.N * c.K + 2 * m * c.K + 2 * m * c.N + 8 * c.N
+        dec_out[str(m)] = {"us_call": round(us, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 3)}
+    out["decode"] = dec_out
+    # the LLM.int8() layer: outlier detection, then the whole decomposition
+    if llm_host is not None:
+        x8, w8, thr = llm_host
+        wq8, sw8, _ = O.quantize_weight(w8)
+        t0 = clock()
+        O.outlier_columns(x8, thr)
+        t_det = clock() - t0
+        t0 = clock()
+        O.linear_int8_outlier(x8, w8, wq8, sw8, thr)
+        t_l = clock() - t0
+        ops8 = 2.0 * x8.shape[0] * w8.shape[0] * x8.shape[1]
+        out["llm_int8"] = {"s": round(t_l, 3), "int8_TOPS": round(ops8 / t_l / 1e12, 4),
+                           "outlier_detection_s": round(t_det, 4)}
+    # one thread: the tiny workload's prefill and decode, and the M = 1 decode linear
+    if threadpool_limits is not None:
+        tiny = synth.Tiny()
+        xt, wt = tiny.x(), tiny.w()
+        with threadpool_limits(1):
+            rq, rs, rc = O.quantize_weight(wt)
+            t0 = clock()
+            for _ in range(20):
+                O.linear_prefill(xt, rq, rs)
+            t_tp = (clock() - t0) / 20
+            t0 = clock()
+            for _ in range(20):
+                O.linear_decode(xt, np.float32(0.5), 3, rq, rs, rc)
+            t_td = (clock() - t0) / 20
+            x1 = c.x(1)
+            t0 = clock()
+            for _ in range(3):
+                O.linear_decode(x1, np.float32(s_dec), z_dec, wqd, swd, csd)
+            t_d1 = (clock() - t0) / 3
+        out["one_thread"] = {"tiny_prefill_us": round(t_tp * 1e6, 1), "tiny_decode_us": round(t_td * 1e6, 1),
+                             "decode_m1_us": round(t_d1 * 1e6, 1),
+                             "decode_m1_GBps": round((c.N * c.K + 2 * c.K + 2 * c.N + 8 * c.N) / t_d1 / 1e9, 3)}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=60)  # ~13 ms of prefill steps: the clock settles first
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "silu"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "silu", "block"], default="all",
                     help="prefill: the headline line without the other workloads; decode: only the decode "
                          "measurements, in a line of their own (for counter collection); silu: only the "
                          "fused SiLU*up quantizer and its down projection")
@@ -633,6 +842,16 @@ def main():
                           "unfused_us": round(smq["ms_unfused"] * 1e3, 2),
                           "down_projection_us": round(smq["ms_linear"] * 1e3, 1)}), flush=True)
         return
+    if args.only == "block":
+        blk = bench_block(args, torch, pdq, synth)
+        print(json.dumps({"metric": "decoder block decode step GB/s", "unit": "GB/s", "n_gpus": 1,
+                          "data": "synthetic",
+                          "config": {"workload": "QKV 4096->12288, O 4096->4096, gate+up 4096->28672, "
+                                                 "down 14336->4096; prefill 8192 tokens, decode batch 32"},
+                          "prefill_us": round(blk["ms_prefill"] * 1e3, 1),
+                          "decode_us_per_step": round(blk["ms_step"] * 1e3, 2),
+                          "decode_GBps": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9, 1)}), flush=True)
+        return
     if args.only == "decode":
         dec = bench_decode(args, torch, pdq, synth)
         print(json.dumps({"metric": "decode GB/s", "unit": "GB/s", "n_gpus": 1, "data": "synthetic",
@@ -688,7 +907,16 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre["gemm_tops"] / PEAK_INT8_TOPS, 4),
                      "traffic": traffic_for(pre["gemm_bytes"]),
                      "kernel": "k_gemm_i8 (INT8 MFMA GEMM + bf16 epilogue)",
-                     "us_per_launch": round(pre["ms_gemm"] * 1e3, 2)},
+                     "us_per_launch": round(pre["ms_gemm"] * 1e3, 2),
+                     "sclk_during_gemm": pre["sclk"]},
+        "settle": {"ms_before_each_timed_region": SETTLE_MS,
+                   "why": "the first ~35 ms of launches after the GPU has idled (input generation on the host) "
+                          "run up to 30% slower while the clock ramps up; each timed region is preceded by "
+                          "this much untimed work of its own kind, so it measures the steady state"},
+        "cold_start": {"prefill_step_us": round(pre["ms_step_cold"] * 1e3, 2),
+                       "TOPS": round(pre["ops"] / (pre["ms_step_cold"] * 1e-3) / 1e12, 1),
+                       "what": f"the same {args.steps} steps after {args.warmup} warmups, timed right after "
+                               "1.5 s of GPU idle, without the settling phase"},
         "prefill_quant": {"us": round(pre["ms_quant"] * 1e3, 2),
                           "GBps": round(pre["quant_bytes"] / (pre["ms_quant"] * 1e-3) / 1e9, 1)},
         "reference_library_gemm": None if pre["ms_lib"] is None else {
@@ -706,6 +934,10 @@ def main():
                          "S_zeropoint": dec["S_zp"], "Z_zeropoint": dec["Z_zp"],
                          "per_batch": {m: {k: round(v, 5) if isinstance(v, float) else v
                                            for k, v in r.items()} for m, r in dec["per_batch"].items()}}
+        out["cs_cg"] = {"workload": "decode linear 4096 -> 4096, bf16 activations: quantizer cost C_s and "
+                                    "GEMM cost C_g (us, HIP-graph replays over 16 weight copies), per-token "
+                                    "dynamic vs per-tensor static",
+                        "per_m": dec["cs_cg"]}
     if llm:
         out["llm_int8"] = {"us": round(llm["ms"] * 1e3, 1), "int8_TOPS": round(llm["int8_tops"], 1),
                            "frac": round(llm["int8_tops"] / PEAK_INT8_TOPS, 4),
@@ -734,7 +966,7 @@ def main():
             "down_projection_TOPS": round(smq["ops"] / (smq["ms_linear"] * 1e-3) / 1e12, 1)}
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(pre)
+        out["cpu_baseline"] = cpu_baseline(pre, synth, llm_host=llm.get("host") if llm else None, dec=dec)
     print(json.dumps(out), flush=True)
 
 

@@ -433,6 +433,21 @@ def test_static_large_m(m, n, k):
     decode_case(x, synth.weights(4960 + n, n, k, "bf16"), "bf16", s, z, bias=synth.bias(4970, n))
 
 
+# K tile counts that differ between the four wavefronts of a skinny-kernel
+# workgroup (K not a multiple of 4 x 64; at K = 64 three wavefronts get no
+# tile at all): a tile a wavefront does not have must add nothing (MFMA
+# instructions ignore the lane mask, so the kernel must branch around them).
+# 16 and 32 channels per workgroup, one to three row blocks of 16.
+@pytest.mark.parametrize("m,n,k", [(20, 300, 4288), (10, 12300, 4288), (20, 9000, 320), (3, 12300, 576),
+                                   (32, 8200, 64), (17, 5000, 1088)])
+def test_skinny_uneven_tiles_per_wavefront(m, n, k):
+    assert pdq.gemm_kernel(m, n) == "skinny"
+    x = synth.activations(4980 + m, m, k, [1, k - 2], 100.0, offset=0.1, dtype="bf16")
+    w = synth.weights(4990 + n, n, k, "bf16")
+    prefill_case(x, w, "bf16", bias=synth.bias(4991, n))
+    decode_case(x, w, "bf16", F32(0.9), -3, bias=synth.bias(4992, n))
+
+
 def test_decode_fused_strided_rows():
     m, n, k = 6, 300, 1024
     wide = synth.activations(4900, m, k + 48, [5], 100.0, offset=0.1, dtype="bf16")

@@ -148,7 +148,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     constexpr int KB = NG == 1 ? (NMB == 1 ? 8 : (NMB == 2 ? 6 : 4)) : (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3));
     __shared__ v4i red[4][NG * NMB][64];
     __shared__ __attribute__((aligned(16))) int8_t xs[FUSED ? 4 : 1][FUSED ? kFusedWave : 16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wavefront index read through readfirstlane is known to be uniform,
+    // so that branches on it (tiles a wavefront skips) are scalar branches:
+    // MFMA instructions ignore EXEC, and an MFMA under a lane mask that the
+    // compiler does not skip with a branch would still accumulate.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = a.M, K = a.K;
     const int n0 = blockIdx.x * kRows * NG;
     const int mbase = blockIdx.y * kMRows;
