@@ -350,24 +350,33 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     }
                 }
     }
+    // One 32-row block of the wave's outputs at a time: the wave converts its
+    // 32 rows x 128 columns of block i into its own part of the LDS output
+    // tile, reads them back as 16-byte row chunks and stores them, then
+    // converts block i + 1 while those stores drain.  No workgroup barrier:
+    // a wave only reads back what it wrote itself (LDS operations of one wave
+    // complete in order), and the four waves' parts of the tile are disjoint.
     // The bias test is taken once for the whole tile, not per element.
+    uint16_t* y = static_cast<uint16_t*>(a.y);
+    const bool vec = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (a.ldy % 8 == 0);
+    const int rbase = MI == 4 ? wm * 128 : mh + wm * 64;  // the wave's first tile row
     auto convert = [&](auto bias_tag) {
         constexpr bool kBias = decltype(bias_tag)::value;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float sbv[4][4], bv[4][4];
-            int32_t zcv[4][4];
+        for (int i = 0; i < MI; ++i) {
+            const int ml = ml0 + 32 * i;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int j = 0; j < 4; ++j) {
+                float sbv[4][4], bv[4][4];
+                int32_t zcv[4][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
-                    if constexpr (kBias) bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
-                    if constexpr (ZP) zcv[g][e] = s_zc[nl0 + 32 * j + 8 * g + e];
-                }
+                for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int ml = ml0 + 32 * i;
+                    for (int e = 0; e < 4; ++e) {
+                        sbv[g][e] = s_sb[nl0 + 32 * j + 8 * g + e];
+                        if constexpr (kBias) bv[g][e] = s_bias[nl0 + 32 * j + 8 * g + e];
+                        if constexpr (ZP) zcv[g][e] = s_zc[nl0 + 32 * j + 8 * g + e];
+                    }
                 v16f side = v16f{};
                 if constexpr (SIDE) {
                     // 16-bit product of the outlier columns for this 32x32
@@ -407,39 +416,35 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                         make_uint2(f32x2_to_16<OUT>(v[0], v[1]), f32x2_to_16<OUT>(v[2], v[3]));
                 }
             }
+            // Rows rbase + 32 i .. + 32, columns wn * 128 .. + 128 of the tile:
+            // 8 passes of 4 rows x 16 chunks of 8 outputs.  A chunk is read as
+            // two 8-byte halves (rows are 8-byte aligned at the 520-byte
+            // pitch); lanes 0..15 read 256 consecutive bytes of one row and
+            // lanes 16..31 the next row, 130 words further: 64 distinct banks.
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int r = rbase + 32 * i + 4 * q + (lane >> 4);
+                const int nl = wn * 128 + 8 * (lane & 15);
+                const int m = m0 + r, n = n0 + nl;
+                const uint2* src = reinterpret_cast<const uint2*>(yrow(r) + nl * 2);
+                const uint2 lo = src[0], hi = src[1];
+                if (m >= M || n >= N) continue;
+                uint16_t* dst = y + (size_t)m * a.ldy + n;
+                if (vec && n + 8 <= N) {
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    const uint16_t v[8] = {(uint16_t)lo.x, (uint16_t)(lo.x >> 16), (uint16_t)lo.y,
+                                           (uint16_t)(lo.y >> 16), (uint16_t)hi.x, (uint16_t)(hi.x >> 16),
+                                           (uint16_t)hi.y, (uint16_t)(hi.y >> 16)};
+                    for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = v[e];
+                }
+            }
         }
     };
     if (a.bias)
         convert(std::true_type{});
     else
         convert(std::false_type{});
-    __syncthreads();
-    // 256 rows x 32 chunks of 8 outputs; consecutive threads take consecutive
-    // chunks of a row.  A chunk is read as two 8-byte halves; 32 lanes (one
-    // row, 512 bytes) share one pass over the 64 banks, so lanes 16..31 of each
-    // half-wave read their upper half first: lanes j and j + 16 then hit
-    // banks 4j, 4j + 1 and 4j + 2, 4j + 3 instead of the same pair.
-    uint16_t* y = static_cast<uint16_t*>(a.y);
-    const bool vec = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (a.ldy % 8 == 0);
-#pragma unroll 4
-    for (int c = tid; c < MI * 64 * (BN / 8); c += 256) {
-        const int ml = (MI == 4 ? 0 : mh) + (c >> 5), nl = (c & 31) * 8;
-        const int m = m0 + ml, n = n0 + nl;
-        if (m >= M || n >= N) continue;
-        const uint2* src = reinterpret_cast<const uint2*>(yrow(ml) + nl * 2);
-        const int first = (c >> 4) & 1;
-        const uint2 p0 = src[first], p1 = src[first ^ 1];
-        const uint2 lo = first ? p1 : p0, hi = first ? p0 : p1;
-        uint16_t* dst = y + (size_t)m * a.ldy + n;
-        if (vec && n + 8 <= N) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-            const uint16_t v[8] = {(uint16_t)lo.x, (uint16_t)(lo.x >> 16), (uint16_t)lo.y,
-                                   (uint16_t)(lo.y >> 16), (uint16_t)hi.x, (uint16_t)(hi.x >> 16),
-                                   (uint16_t)hi.y, (uint16_t)(hi.y >> 16)};
-            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = v[e];
-        }
-    }
 }
 
 }  // namespace
