@@ -133,7 +133,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         else return st3;
     };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wavefront index through readfirstlane: wave-uniform, so it and what
+    // derives from it (the tile quadrant, the LDS rows this wave fills) live
+    // in scalar registers; the K loop uses every vector register.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int M = a.M, N = a.N, K = a.K;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -288,10 +291,13 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // r%4 and m = l%32, i.e. 4 consecutive outputs of one row of y per
     // register quad.  They are rounded, packed and written to the LDS output
     // tile with one 8-byte write; the tile then leaves in 16-byte row chunks.
+    // The lane index again, from the lane masks (v_mbcnt) rather than kept in
+    // a register across the K loop.
+    const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     int side_steps = 0;
     bool poison = false;
-    const int ml0 = (MI == 4 ? wm * 128 : mh + wm * 64) + (lane & 31);
-    const int nl0 = wn * 128 + 4 * (lane >> 5);
+    const int ml0 = (MI == 4 ? wm * 128 : mh + wm * 64) + (elane & 31);
+    const int nl0 = wn * 128 + 4 * (elane >> 5);
     [[maybe_unused]] uint4 xs0[4], ws0[4];
     if constexpr (SIDE) {
         const int cnt = *a.count;
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         // fetched while the last K tiles land.  Rows past M or N are clamped:
         // they only feed outputs that are never stored.
         if (side_steps > 0) {
-            const int koff = 8 * (lane >> 5);
+            const int koff = 8 * (elane >> 5);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int m = min(m0 + ml0 + 32 * i, M - 1);
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int wr = min(n0 + wn * 128 + 32 * j + (lane & 31), N - 1);
+                const int wr = min(n0 + wn * 128 + 32 * j + (elane & 31), N - 1);
                 ws0[j] = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
             }
         }
@@ -385,9 +391,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     if (side_steps > 0) {
                         side = side_mfma(ws0[j], xs0[i], side);
                         const int m = min(m0 + ml, M - 1);
-                        const int wr = min(n0 + wn * 128 + 32 * j + (lane & 31), N - 1);
+                        const int wr = min(n0 + wn * 128 + 32 * j + (elane & 31), N - 1);
                         for (int ks = 1; ks < side_steps; ++ks) {
-                            const int koff = ks * 16 + 8 * (lane >> 5);
+                            const int koff = ks * 16 + 8 * (elane >> 5);
                             const uint4 xv = *reinterpret_cast<const uint4*>(a.xo + (size_t)m * a.P + koff);
                             const uint4 wv = *reinterpret_cast<const uint4*>(a.wo + (size_t)wr * a.P + koff);
                             side = side_mfma(wv, xv, side);
@@ -419,15 +425,20 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             // Rows rbase + 32 i .. + 32, columns wn * 128 .. + 128 of the tile:
             // 8 passes of 4 rows x 16 chunks of 8 outputs.  A chunk is read as
             // two 8-byte halves (rows are 8-byte aligned at the 520-byte
-            // pitch); lanes 0..15 read 256 consecutive bytes of one row and
-            // lanes 16..31 the next row, 130 words further: 64 distinct banks.
+            // pitch), as two separate ds_read_b64: in each, lanes 0..15 read
+            // every other 8 bytes of 256 consecutive bytes of one row and lanes
+            // 16..31 those of the next row, 130 words further, so the 32 lanes
+            // of a pass hit 64 distinct banks.  (Merged into one ds_read2_b64
+            // the same reads counted 1024 bank-conflict cycles per workgroup.)
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int r = rbase + 32 * i + 4 * q + (lane >> 4);
-                const int nl = wn * 128 + 8 * (lane & 15);
+                const int r = rbase + 32 * i + 4 * q + (elane >> 4);
+                const int nl = wn * 128 + 8 * (elane & 15);
                 const int m = m0 + r, n = n0 + nl;
                 const uint2* src = reinterpret_cast<const uint2*>(yrow(r) + nl * 2);
-                const uint2 lo = src[0], hi = src[1];
+                const uint2 lo = src[0];
+                asm volatile("" ::: "memory");  // keeps the two reads apart
+                const uint2 hi = src[1];
                 if (m >= M || n >= N) continue;
                 uint16_t* dst = y + (size_t)m * a.ldy + n;
                 if (vec && n + 8 <= N) {
