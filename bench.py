@@ -261,12 +261,14 @@ def bench_prefill(args, torch, pdq, synth):
         def lib_gemm(i):
             torch._int_mm(a_rm, bs[i % nrot].t())
 
+        settle(lib_gemm, stream)  # after the host-side unpacking above
         ms_lib = timed(lib_gemm, max(args.steps // 2, 10), args.warmup // 2, stream)
         del bs, a_rm, b_rm
     except (RuntimeError, TypeError) as e:  # no hipBLASLt INT8 path for this shape or build
         log(f"[prefill] torch._int_mm reference unavailable: {e}")
 
     asym_steps = max(args.steps // 2, 10)
+    settle(step_asym, stream)
     ms_step_asym = timed(step_asym, asym_steps, args.warmup // 2, stream)
     ms_quant_asym = timed(quant_asym, asym_steps, args.warmup // 2, stream)
     for r in range(nrot):  # codes, scales and zero points of every activation copy
