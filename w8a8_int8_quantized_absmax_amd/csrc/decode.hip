@@ -144,8 +144,12 @@ constexpr int kFusedWave = kFusedBytes / 4 + 16 * 64;
 template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false, int NG = 1>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     static_assert(!FUSED || NG == 1, "the one-launch path has one channel group");
-    // K tiles per batch: about 5 fragments per tile and batch, two batches in flight
-    constexpr int KB = NG == 1 ? (NMB == 1 ? 8 : (NMB == 2 ? 6 : 4)) : (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3));
+    // K tiles per batch, two batches in flight.  Measured per shape (graph
+    // replays, weights rotated beyond the MALL): 16 channels and 17..32 rows
+    // run 5% faster with 4 tiles (three workgroups per CU) than with 6 (two);
+    // 33..64 rows are best at 4, 32 channels at 4 (17..32 rows) -- 2 or 3
+    // were slower or no faster.
+    constexpr int KB = NG == 1 ? (NMB == 1 ? 8 : 4) : (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3));
     __shared__ v4i red[4][NG * NMB][64];
     __shared__ __attribute__((aligned(16))) int8_t xs[FUSED ? 4 : 1][FUSED ? kFusedWave : 16];
     // The wavefront index read through readfirstlane is known to be uniform,
