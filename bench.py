@@ -172,8 +172,14 @@ def sample_sclk(fn, ms: float = 600.0):
 
 
 def kernel_hash() -> str:
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the GEMM source with its // comments and blank lines removed, so
+    that a change of comments alone does not invalidate the counter summary."""
+    import re
+
+    with open(GEMM_SRC, encoding="utf-8") as f:
+        lines = [re.sub(r"\s*//.*$", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(per_launch_bytes_expected: float):
