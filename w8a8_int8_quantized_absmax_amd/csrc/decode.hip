@@ -392,10 +392,13 @@ void launch_decode_fused(const DecodeArgs& a, hipStream_t st) {
 }
 
 // 32 channels per workgroup halve the activation fragments each channel
-// costs, but also the number of workgroups: worth it from about one and a
-// half workgroups per CU (256 CUs).
+// costs, but also the number of workgroups: worth it from two workgroups per
+// CU (256 CUs).  Measured at K = 4096: 28672 channels x 32 rows (896 such
+// workgroups) 26.9 us against 32.9 with 16 channels; 12288 channels x 32 /
+// 48 / 64 rows and 6144 x 128 (384 of them) 11.2 / 14.3 / 17.2 / 17.0 us
+// with 16 channels against 11.5 / 14.6 / 18.6 / 18.5 with 32.
 bool decode_wide_groups(int64_t M, int64_t N) {
-    return (N + 2 * kRows - 1) / (2 * kRows) * ((M + kMRows - 1) / kMRows) >= 384;
+    return (N + 2 * kRows - 1) / (2 * kRows) * ((M + kMRows - 1) / kMRows) >= 512;
 }
 
 template <int NG>
