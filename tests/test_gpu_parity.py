@@ -182,6 +182,36 @@ def test_prefill_asym_building_blocks(m, n, k):
     assert torch.equal(one["y"], two["y"]) and torch.equal(one["acc"], two["acc"])
 
 
+# Rows with a pitch past K (a view of the first K columns of a wider buffer):
+# both per-token quantizers -- a wavefront per row up to K = 2048, a workgroup
+# per row beyond -- and both GEMM kernels read the right rows.
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(37, 520, 1040), (300, 700, 4096), (2048, 2600, 2112)])
+def test_prefill_strided_rows(dtype, m, n, k):
+    pad = 40
+    wide = synth.activations(5200 + k, m, k + pad, [3, k - 1], 100.0, dtype=dtype)
+    x = np.ascontiguousarray(wide[:, :k])
+    wq, ws, cs, (rq, rs, rc) = weight_case(synth.weights(5201, n, k, dtype), dtype)
+    xt = dev(wide, dtype)[:, :k]
+    assert xt.stride(0) == k + pad
+    res = pdq.linear_prefill(xt, wq, ws, want_acc=True)
+    xq_ref, sx_ref = O.quantize_rows_absmax(x)
+    assert codes_equal(res["xq"], xq_ref)
+    assert np.array_equal(host(res["x_scale"]).view(np.uint32), sx_ref.view(np.uint32))
+    acc_ref = O.int_matmul(xq_ref, rq)
+    assert np.array_equal(host(res["acc"]), acc_ref)
+    check_16bit(host(res["y"]), O.dequantize(acc_ref, sx_ref, rs, None), "bf16", True)
+    res = pdq.linear_prefill_asym(xt, wq, ws, cs, want_acc=True)
+    q_ref, s_ref, z_ref = O.quantize_rows_asym(x)
+    assert codes_equal(res["xq"], q_ref)
+    assert np.array_equal(host(res["x_scale"]).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(res["x_zp"]), z_ref)
+    acc_ref = O.int_matmul(q_ref, rq)
+    assert np.array_equal(host(res["acc"]), acc_ref)
+    check_16bit(host(res["y"]), O.dequantize(O.zero_point_correct(acc_ref, rc, z_ref), s_ref, rs, None), "bf16",
+                True)
+
+
 def test_prefill_empty_batch():
     w = synth.weights(7, 64, 64, "bf16")
     wq, ws, _ = pdq.quantize_weight(dev(w, "bf16"))
