@@ -541,6 +541,116 @@ def test_decode_brute_force_error_bound():
             assert abs(float(res["y32"][m, n]) - exact) <= bound * (1 + 1e-5) + 1e-6 * abs(exact)
 
 
+def _layer_bound(x, w, sa, sw, ha=None):
+    """|x w^T - y| bound of a quantized layer: each activation within sa[m]/2 of
+    its grid point (plus ha[m, k] of its own rounding), each weight within
+    sw[n]/2, and the cross term."""
+    m_, k_ = x.shape
+    n_ = w.shape[0]
+    b = np.zeros((m_, n_))
+    for m in range(m_):
+        for n in range(n_):
+            b[m, n] = sum((abs(float(w[n, k])) * (float(sa[m]) / 2 + (0.0 if ha is None else ha[m, k]))
+                           + abs(float(x[m, k])) * float(sw[n]) / 2 + float(sa[m]) * float(sw[n]) / 4)
+                          for k in range(k_))
+    return b
+
+
+def check_static_sym_layer(oracle=O):
+    """[LLM.int8] part 1 section 1 absmax, tensor-wise with a calibrated static
+    scale: the layer approximates X W^T within the quantization bound when no
+    value saturates."""
+    cal = [synth.activations(110 + b, 8, 32, [3], 20.0, dtype="f32") for b in range(3)]
+    _, s = oracle.calibrate_absmax(cal)
+    x = np.clip(synth.activations(114, 3, 32, [3], 20.0, dtype="f32"), -127 * s, 127 * s).astype(F32)
+    w = synth.weights(115, 5, 32, "f32")
+    wq, sw, _ = oracle.quantize_weight(w)
+    res = oracle.linear_static_sym(x, s, wq, sw)
+    assert res["sat"] == 0
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = _layer_bound(x, w, np.full(3, s), sw)
+    assert np.all(np.abs(res["y32"] - exact) <= bound * (1 + 1e-5) + 1e-6 * np.abs(exact))
+
+
+def test_static_sym_brute_force_error_bound():
+    check_static_sym_layer()
+
+
+def test_static_sym_of_one_row_is_per_token_prefill():
+    """With one activation row and S its own absmax / 127, the tensor-wise
+    static code is the per-token code: the whole layer equals the prefill
+    linear, bit for bit."""
+    x = synth.activations(116, 1, 64, [5], 30.0, dtype="f32")
+    w = synth.weights(117, 6, 64, "f32")
+    wq, sw, _ = O.quantize_weight(w)
+    s = O.absmax_scale(np.max(np.abs(x)))
+    a = O.linear_static_sym(x, s, wq, sw)
+    b = O.linear_prefill(x, wq, sw)
+    assert np.array_equal(a["xq"], b["xq"]) and np.array_equal(a["acc"], b["acc"])
+    assert np.array_equal(np.asarray(a["y32"], F32).view(np.uint32), np.asarray(b["y32"], F32).view(np.uint32))
+
+
+def check_zeropoint_layer(oracle=O):
+    """The 254-level zero-point grid ([LLM.int8] part 1 section 2) over a range
+    not centred on 0: the layer, with the zero point removed through the code
+    sums, approximates X W^T within the quantization bound."""
+    cal = [synth.activations(120 + b, 8, 32, [1], 10.0, offset=2.0, dtype="f32") for b in range(3)]
+    _, s, z = oracle.calibrate_zeropoint(cal)
+    assert z != 0
+    lo, hi = (-127 - z) * float(s), (127 - z) * float(s)
+    x = np.clip(synth.activations(124, 3, 32, [1], 10.0, offset=2.0, dtype="f32"), lo, hi).astype(F32)
+    w = synth.weights(125, 5, 32, "f32")
+    wq, sw, colsum = oracle.quantize_weight(w)
+    res = oracle.linear_zeropoint(x, s, z, wq, sw, colsum)
+    assert res["sat"] == 0
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = _layer_bound(x, w, np.full(3, s), sw)
+    assert np.all(np.abs(res["y32"] - exact) <= bound * (1 + 1e-5) + 1e-6 * np.abs(exact))
+
+
+def test_zeropoint_brute_force_error_bound():
+    check_zeropoint_layer()
+
+
+def test_zeropoint_over_a_symmetric_range_is_static_sym():
+    """A calibrated range symmetric about 0 puts the 254-level grid's zero point
+    at 0 and its step at C / 127: the zero-point layer equals the static
+    symmetric one, bit for bit."""
+    x = synth.activations(126, 4, 48, [2], 25.0, dtype="f32")
+    c = float(np.max(np.abs(x)))
+    state = (F32(-c), F32(c))
+    s, z = O.zeropoint_finalize(state)
+    assert z == 0 and s == O.absmax_finalize(state)
+    w = synth.weights(127, 7, 48, "f32")
+    wq, sw, colsum = O.quantize_weight(w)
+    a = O.linear_zeropoint(x, s, z, wq, sw, colsum)
+    b = O.linear_static_sym(x, s, wq, sw)
+    assert np.array_equal(a["xq"], b["xq"]) and np.array_equal(a["acc"], b["acc"])
+    assert np.array_equal(np.asarray(a["y32"], F32).view(np.uint32), np.asarray(b["y32"], F32).view(np.uint32))
+
+
+def check_silu_mul_layer(oracle=O):
+    """The down projection fed by SiLU(gate) * up: against the exact product of
+    the unrounded SiLU(g) u (math.exp, binary64) with W, within the bound of
+    the bf16 rounding of h (2^-9 relative), its per-token quantization and
+    the weight's."""
+    rng = np.random.default_rng(128)
+    g = _bf16_values(rng, 3 * 32, -3, 2).reshape(3, 32)
+    u = _bf16_values(rng, 3 * 32, -3, 2).reshape(3, 32)
+    w = synth.weights(129, 5, 32, "f32")
+    wq, sw, _ = oracle.quantize_weight(w)
+    res = oracle.linear_prefill_silu_mul(g, u, wq, sw)
+    hx = np.array([[float(g[m, k]) / (1.0 + math.exp(-float(g[m, k]))) * float(u[m, k]) for k in range(32)]
+                   for m in range(3)])
+    exact = hx @ w.astype(np.float64).T
+    bound = _layer_bound(hx, w, res["x_scale"], sw, ha=np.abs(hx) * 2.0 ** -9 * (1 + 1e-9))
+    assert np.all(np.abs(res["y32"] - exact) <= bound * (1 + 1e-5) + 1e-6 * np.abs(exact))
+
+
+def test_prefill_silu_mul_brute_force_error_bound():
+    check_silu_mul_layer()
+
+
 def test_epilogue_matches_binary64_evaluation():
     x = synth.activations(98, 32, 256, [9], 100.0, dtype="f32")
     w = synth.weights(99, 48, 256, "f32")
@@ -845,6 +955,25 @@ def _silu_mul_via_binary32(g, u, dtype="bf16"):
     return O.bf16_bits_to_f32(O.to_bf16_bits(v))
 
 
+def _static_sym_layer_without_activation_scale(x, s, wq, sw, bias=None):
+    xq, sat = O.quantize_static_sym(x, s)
+    acc = O.int_matmul(xq, wq)
+    return dict(xq=xq, sat=sat, acc=acc, y32=O.dequantize(acc, F32(1), sw, bias))
+
+
+def _zeropoint_layer_adding_zero_point(x, s, z, wq, sw, colsum, bias=None):
+    xq, sat = O.quantize_zeropoint(x, s, z)
+    acc = O.int_matmul(xq, wq)
+    return dict(xq=xq, sat=sat, acc=acc, y32=O.dequantize(acc + z * colsum.astype(np.int64)[None, :], F32(s), sw,
+                                                           bias))
+
+
+def _silu_mul_layer_quantizing_gate(gate, up, wq, sw, bias=None, dtype="bf16"):
+    xq, sx = O.quantize_rows_absmax(np.asarray(gate, F32))
+    acc = O.int_matmul(xq, wq)
+    return dict(h=None, xq=xq, x_scale=sx, acc=acc, y32=O.dequantize(acc, sx, sw, bias))
+
+
 @pytest.mark.parametrize("mutant,check", [
     (_Mutant(silu_mul=_silu_mul_flipped_sigmoid), check_silu_mul),
     (_Mutant(silu_mul=_silu_mul_without_up), check_silu_mul),
@@ -861,6 +990,9 @@ def _silu_mul_via_binary32(g, u, dtype="bf16"):
     (_Mutant(quantize_zeropoint=_zeropoint_wide_clamp), check_zeropoint),
     (_Mutant(quantize_rows_asym=_asym_rows_unwidened), check_asym_rows),
     (_Mutant(quantize_rows_asym=_asym_rows_zero_point_sign), check_asym_rows),
+    (_Mutant(linear_static_sym=_static_sym_layer_without_activation_scale), check_static_sym_layer),
+    (_Mutant(linear_zeropoint=_zeropoint_layer_adding_zero_point), check_zeropoint_layer),
+    (_Mutant(linear_prefill_silu_mul=_silu_mul_layer_quantizing_gate), check_silu_mul_layer),
 ])
 def test_planted_mistake_is_caught(mutant, check):
     with pytest.raises(AssertionError):
