@@ -517,14 +517,19 @@ __global__ __launch_bounds__(256, 2) void k_silu_mul_quant(const void* __restric
 // row of x itself, the plain per-token quantizer of k_quant_rows (DT may be
 // binary32); kRowAsym: the row of x on its own asymmetric grid, as
 // k_quant_rows<..., ASYM> (min and max reduced instead of the absmax, the
-// zero point into rowint).
+// zero point into rowint).  SKIP (kRowPlain, 16-bit types): the outlier
+// columns of the LLM.int8() decomposition take no part in the absmax and are
+// coded 0, and their values are gathered into X_out, as k_quant_rows<...,
+// SKIP> does with a wavefront per row.
 constexpr int kRowPlain = 0, kRowSilu = 1, kRowAsym = 2;
-template <int DT, int CPT, int MODE>
+template <int DT, int CPT, int MODE, bool SKIP = false>
 __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restrict__ gate, int64_t ldg_bytes,
                                                            const void* __restrict__ up, int64_t ldu_bytes,
                                                            int64_t rows, int nch, int8_t* __restrict__ q,
                                                            float* __restrict__ scale, int32_t* __restrict__ rowint,
-                                                           void* __restrict__ h_out, int64_t ldh_bytes) {
+                                                           void* __restrict__ h_out, int64_t ldh_bytes,
+                                                           OutlierSkip skip) {
+    static_assert(!SKIP || (MODE == kRowPlain && DT != kF32), "outlier columns: plain 16-bit rows only");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row = blockIdx.x;
     const int ktiles = (nch + 7) / 8;
@@ -541,7 +546,20 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
     const char* gr = static_cast<const char*>(gate) + row * ldg_bytes;
     const char* ur = static_cast<const char*>(up) + row * ldu_bytes;
     uint4* hr = h_out ? reinterpret_cast<uint4*>(static_cast<char*>(h_out) + row * ldh_bytes) : nullptr;
+    // Outlier gather into X_out (SKIP): thread j fetches x[row, idx[j]] (j <
+    // 256; the index is clamped into the row, entries past the count are
+    // unset) while the row is being quantized, and stores it, or the zero
+    // padding, once the count is known to fit.
+    const bool gather = SKIP && skip.xo != nullptr && skip.max_out > 0;
+    const uint16_t* gr16 = reinterpret_cast<const uint16_t*>(gr);
+    int gidx = 0, gcnt = 0;
+    uint16_t gval = 0;
+    if (gather) {
+        gidx = skip.idx[min(tid, skip.max_out - 1)];
+        gcnt = *skip.count;
+    }
     Raw8<DT> hv[CPT];
+    uint32_t sk[CPT];
     float amax = 0.0f, lo = 0.0f, hi = 0.0f;  // the asymmetric range starts widened to contain 0
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -551,7 +569,13 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
             hv[i] = silu_mul8<DT>(load_raw8<DT>(gr, cc), load_raw8<DT>(ur, cc));
         else
             hv[i] = load_raw8<DT>(gr, cc);
+        sk[i] = SKIP ? skip.mask[cc] : 0u;
         if (c >= nch) hv[i] = zero_raw8<DT>();
+    }
+    if (gather) gval = gr16[min(max(gidx, 0), nch * 8 - 1)];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        if constexpr (SKIP) hv[i] = zero_skipped<DT>(hv[i], sk[i]);  // +0: no part in the absmax, code 0
         if constexpr (MODE == kRowAsym) {
             float v[8];
             widen8<DT>(hv[i], v);
@@ -603,19 +627,30 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
         }
     }
     for (int c = nch + tid; c < ktiles * 8; c += 256) store_code(c, make_uint2(0u, 0u));  // K padding
+    if (gather && gcnt <= skip.max_out) {
+        uint16_t* xo_row = skip.xo + row * skip.P;
+        const int used = (gcnt + 15) / 16 * 16;
+        if (tid < used) xo_row[tid] = tid < gcnt ? gval : (uint16_t)0;
+        for (int j = tid + 256; j < used; j += 256) {
+            const uint16_t v = gr16[skip.idx[min(j, gcnt - 1)]];
+            xo_row[j] = j < gcnt ? v : (uint16_t)0;
+        }
+    }
     if (tid == 0) {
         scale[row] = s;
         if constexpr (MODE == kRowAsym) rowint[row] = zq;
     }
 }
 
-template <int DT, int CPT, int MODE = kRowSilu>
+template <int DT, int CPT, int MODE = kRowSilu, bool SKIP = false>
 void silu_mul_quant_wg(const void* gate, int64_t ldg, const void* up, int64_t ldu, int64_t rows, int nch,
-                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st, int32_t* rowint = nullptr) {
+                       int8_t* q, float* scale, void* h, int64_t ldh, hipStream_t st, int32_t* rowint = nullptr,
+                       const OutlierSkip* skip = nullptr) {
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
     constexpr int eb = Elem<DT>::bytes;
-    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, MODE>), dim3((unsigned)rows_pad), dim3(256), 0, st, gate,
-                       ldg * eb, up, ldu * eb, rows, nch, q, scale, rowint, h, ldh * eb);
+    const OutlierSkip none{};
+    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, MODE, SKIP>), dim3((unsigned)rows_pad), dim3(256), 0, st,
+                       gate, ldg * eb, up, ldu * eb, rows, nch, q, scale, rowint, h, ldh * eb, skip ? *skip : none);
 }
 
 template <int DT, int CPL>
@@ -689,6 +724,27 @@ template <int DT>
 void quant_rows_dt(const void* x, int64_t rows, int64_t K, int64_t ldx, int8_t* q, float* scale,
                    int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const int64_t per_lane = (K / 8 + 63) / 64;  // chunks of 8 per lane
+    if constexpr (DT != kF32) {
+        // the regular columns of the LLM.int8() decomposition, rows longer than
+        // 2048 values: a workgroup per row as well (outlier columns skipped,
+        // their values gathered into X_out)
+        if (skip && !asym && !colsum && per_lane > 4 && per_lane <= 64) {
+            const int nch = (int)(K / 8);
+            if (per_lane <= 8)
+                silu_mul_quant_wg<DT, 2, kRowPlain, true>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st,
+                                                          nullptr, skip);
+            else if (per_lane <= 16)
+                silu_mul_quant_wg<DT, 4, kRowPlain, true>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st,
+                                                          nullptr, skip);
+            else if (per_lane <= 32)
+                silu_mul_quant_wg<DT, 8, kRowPlain, true>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st,
+                                                          nullptr, skip);
+            else
+                silu_mul_quant_wg<DT, 16, kRowPlain, true>(x, ldx, nullptr, 0, rows, nch, q, scale, nullptr, 0, st,
+                                                           nullptr, skip);
+            return;
+        }
+    }
     if (!skip && (asym || !colsum) && per_lane > 4 && per_lane <= 64) {
         // the per-token quantizers (symmetric, or asymmetric with the zero
         // points in `colsum`) of rows longer than 2048 values: a workgroup per
