@@ -582,7 +582,8 @@ def test_outlier_capacity_exceeded_poisons_output():
 
 
 def test_outlier_capacity_beyond_fused_gather():
-    """More capacity than the index kernel keeps in LDS: the separate W gather runs."""
+    """A capacity of 5000 columns with 3 outliers spread over K = 8192, one of
+    them the last column: the capacity sets only the pitch of X_out and W_out."""
     k = 8192
     x = synth.normal(5900, (33, k))
     cols = [3, 4100, k - 1]
@@ -590,6 +591,23 @@ def test_outlier_capacity_beyond_fused_gather():
     x = synth.round_to(x, "f16")
     res, cnt = outlier_case(x, synth.weights(5902, 40, k, "f16"), "f16", 6.0, max_out=5000)
     assert cnt == 3
+
+
+@pytest.mark.parametrize("k", [1024, 4096])
+def test_outlier_more_columns_than_a_workgroup_has_threads(k):
+    """300 outlier columns (304 with the zero padding), more than the 256
+    threads of a gather workgroup: X_out and W_out are gathered by loops over
+    the columns, on the wavefront-per-row quantizer (K = 1024) and on the
+    workgroup-per-row one (K = 4096); 203 weight rows end in a short gather
+    slab."""
+    m, n = 40, 203
+    x = synth.normal(6100 + k, (m, k))
+    cols = synth.choose_channels(6200 + k, k, 300)
+    x[:, cols] = synth.normal(6300 + k, (m, len(cols)), 60.0)
+    x = synth.round_to(x, "f16")
+    res, cnt = outlier_case(x, synth.weights(6400 + k, n, k, "f16"), "f16", 6.0,
+                            bias=synth.bias(6500, n), max_out=512)
+    assert cnt == 300
 
 
 def test_outlier_single_hits_in_far_row_blocks():

@@ -10,17 +10,15 @@
 //                     block.  Every byte is written, so nothing needs clearing
 //                     first and no atomics are involved.
 //  * k_outlier_index  ORs the row blocks into the final per-chunk mask, counts
-//                     and lists the outlier columns in ascending order, and
-//                     gathers the outlier columns of W.  Every workgroup
-//                     derives the list itself (a few KB from L2) and gathers
-//                     its own slab of W rows; workgroup 0 publishes the mask,
-//                     the index list and the count.
-//  * k_gather_cols    X_out / W_out from a published index list: the W gather
-//                     for capacities beyond what k_outlier_index holds in LDS.
+//                     and lists the outlier columns in ascending order: one
+//                     workgroup writes the mask, the index list and the count.
 //
-// The X gather is fused into the activation quantizer (quant.hip), which
-// reads every row anyway.  X_out and W_out are packed and zero-padded to a
-// multiple of 16 columns for the 16-bit MFMA in the GEMM epilogue.
+// Both gathers are fused into the regular-column quantizer (quant.hip): its
+// row workgroups gather X_out from the rows they read anyway, and extra
+// workgroups of the same launch gather W_out, so that the scattered reads of
+// the W gather overlap the quantization.  X_out and W_out are packed and
+// zero-padded to a multiple of 16 columns for the 16-bit MFMA in the GEMM
+// epilogue.
 
 #include "pdq_device.h"
 #include "pdq_kernels.h"
@@ -97,19 +95,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int& total, int* s_wa
 }
 
 // Thread t owns the mask words (4 chunks each) [t * wpt, t * wpt + wpt).
-// gather: W rows [blockIdx.x * rows_per_wg, ...) of the outlier columns
-// into wo (pitch P), zero-padded to a multiple of 16, when the count fits
-// max_out; wo == null skips it.
-__global__ __launch_bounds__(kIndexThreads) void k_outlier_index(
-    const uint8_t* __restrict__ partial, int nrb, int pitch, int nch, uint8_t* __restrict__ mask,
-    int32_t* __restrict__ idx, int32_t* __restrict__ count,
-    int max_out, const uint16_t* __restrict__ w16, int64_t N, int64_t ldw,
-    uint16_t* __restrict__ wo, int P, int rows_per_wg) {
-    __shared__ int32_t s_idx[kOutlierIdxCap];
+__global__ __launch_bounds__(kIndexThreads) void k_outlier_index(const uint8_t* __restrict__ partial, int nrb,
+                                                                 int pitch, int nch, uint8_t* __restrict__ mask,
+                                                                 int32_t* __restrict__ idx,
+                                                                 int32_t* __restrict__ count, int max_out) {
     __shared__ uint32_t s_words[kMaxMaskWords];
     __shared__ int s_wave[kIndexThreads / 64];
     const int tid = threadIdx.x;
-    const bool publish = blockIdx.x == 0;
     const int nwords = (nch + 3) / 4;
     const int wpt = (nwords + kIndexThreads - 1) / kIndexThreads;
     const int w0 = tid * wpt;
@@ -129,13 +121,12 @@ __global__ __launch_bounds__(kIndexThreads) void k_outlier_index(
         if (valid < 4) m &= (1u << (8 * valid)) - 1u;
         mine += __popc(m);
         s_words[w] = m;
-        if (publish) reinterpret_cast<uint32_t*>(mask)[w] = m;
+        reinterpret_cast<uint32_t*>(mask)[w] = m;
     }
     int total;
     int run = block_exclusive_scan(mine, total, s_wave);
 
-    // pass 2: ascending index list
-    const int cap = min(max_out, kOutlierIdxCap);
+    // pass 2: ascending index list (the first max_out columns)
     for (int k = 0; k < nw; ++k) {
         const int w = w0 + k;
         const uint32_t m = s_words[w];
@@ -146,58 +137,12 @@ __global__ __launch_bounds__(kIndexThreads) void k_outlier_index(
             while (byte) {
                 const int j = __ffs(byte) - 1;
                 byte &= byte - 1;
-                if (run < cap) s_idx[run] = 8 * c + j;
-                if (publish && run < max_out) idx[run] = 8 * c + j;
+                if (run < max_out) idx[run] = 8 * c + j;
                 ++run;
             }
         }
     }
-    if (publish && tid == 0) *count = total;
-    __syncthreads();
-    if (!wo || total > max_out) return;
-
-    const int used = (total + 15) / 16 * 16;
-    if (used == 0) return;
-    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
-    const int nrows = (int)min((int64_t)rows_per_wg, N - row0);
-    if (used <= kIndexThreads) {
-        // kIndexThreads / used rows at a time, one column per thread; eight
-        // rows' loads are issued (clamped) before any of them is stored
-        constexpr int kG = 8;
-        const int rpi = kIndexThreads / used, rl = tid / used, j = tid - rl * used;
-        const int col = s_idx[min(j, total - 1)];
-        if (rl < rpi) {
-            for (int rb = rl; rb < nrows; rb += rpi * kG) {
-                uint16_t v[kG];
-#pragma unroll
-                for (int u = 0; u < kG; ++u)
-                    v[u] = w16[(row0 + min(rb + u * rpi, nrows - 1)) * ldw + col];
-#pragma unroll
-                for (int u = 0; u < kG; ++u) {
-                    const int r = rb + u * rpi;
-                    if (r < nrows) wo[(row0 + r) * P + j] = j < total ? v[u] : (uint16_t)0;
-                }
-            }
-        }
-    } else {
-        for (int r = 0; r < nrows; ++r)
-            for (int j = tid; j < used; j += kIndexThreads)
-                wo[(row0 + r) * P + j] = j < total ? w16[(row0 + r) * ldw + s_idx[j]] : (uint16_t)0;
-    }
-}
-
-__global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ src, int64_t rows,
-                                                     int64_t ld, const int32_t* __restrict__ idx,
-                                                     const int32_t* __restrict__ count, int max_out,
-                                                     uint16_t* __restrict__ dst, int P) {
-    const int cnt = *count;
-    if (cnt > max_out) return;
-    const int used = (cnt + 15) / 16 * 16;
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t r = t / P;
-    const int j = (int)(t - r * P);
-    if (r >= rows || j >= used) return;
-    dst[r * P + j] = j < cnt ? src[r * ld + idx[j]] : (uint16_t)0;
+    if (tid == 0) *count = total;
 }
 
 }  // namespace
@@ -231,32 +176,10 @@ void launch_outlier_partial(const void* x, int dt, int64_t M, int64_t K, int64_t
                            thr, partial, pitch);
 }
 
-void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask,
-                          int32_t* idx, int32_t* count, int64_t max_out,
-                          const void* w16, int64_t N, int64_t ldw, uint16_t* wo, int P,
-                          hipStream_t st) {
-    const int nch = (int)(K / 8);
-    const bool gather = wo && N > 0 && max_out <= kOutlierIdxCap;
-    int groups = 1, rows_per_wg = 0;
-    if (gather) {
-        groups = (int)std::min<int64_t>(256, std::max<int64_t>(1, (N + 127) / 128));
-        rows_per_wg = (int)((N + groups - 1) / groups);
-        groups = (int)((N + rows_per_wg - 1) / rows_per_wg);
-    }
-    hipLaunchKernelGGL(k_outlier_index, dim3(groups), dim3(kIndexThreads), 0, st, partial,
-                       outlier_row_blocks(M), outlier_partial_pitch(K), nch, mask, idx, count,
-                       (int)max_out, static_cast<const uint16_t*>(w16), N, ldw,
-                       gather ? wo : nullptr, P, rows_per_wg);
-    if (wo && N > 0 && !gather)
-        launch_gather_cols(w16, N, ldw, idx, count, (int)max_out, wo, P, st);
-}
-
-void launch_gather_cols(const void* src, int64_t rows, int64_t ld, const int32_t* idx,
-                        const int32_t* count, int max_out, uint16_t* dst, int P, hipStream_t st) {
-    if (rows <= 0 || P <= 0) return;
-    const int64_t total = rows * P;
-    hipLaunchKernelGGL(k_gather_cols, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(src), rows, ld, idx, count, max_out, dst, P);
+void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask, int32_t* idx,
+                          int32_t* count, int64_t max_out, hipStream_t st) {
+    hipLaunchKernelGGL(k_outlier_index, dim3(1), dim3(kIndexThreads), 0, st, partial, outlier_row_blocks(M),
+                       outlier_partial_pitch(K), (int)(K / 8), mask, idx, count, (int)max_out);
 }
 
 }  // namespace pdq

@@ -4,6 +4,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "pdq.h"
@@ -147,10 +148,22 @@ void run_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K, int64_t
     uint16_t* wo = reinterpret_cast<uint16_t*>(ws);
 
     launch_outlier_partial(x, dt, M, K, ldx, threshold, partial, st);
-    launch_outlier_index(partial, M, K, mask, outlier_idx, n_outlier, max_outliers, w16, N, ldw, wo,
-                         (int)P, st);
+    launch_outlier_index(partial, M, K, mask, outlier_idx, n_outlier, max_outliers, st);
     if (M > 0) {
-        const OutlierSkip skip{mask, outlier_idx, n_outlier, (int)max_outliers, xo, (int)P};
+        // the regular-column quantizer; extra workgroups of its launch gather
+        // W_out (at most 256 of them)
+        OutlierSkip skip{};
+        skip.mask = mask;
+        skip.idx = outlier_idx;
+        skip.count = n_outlier;
+        skip.max_out = (int)max_outliers;
+        skip.xo = xo;
+        skip.P = (int)P;
+        skip.w16 = static_cast<const uint16_t*>(w16);
+        skip.ldw = ldw;
+        skip.N = N;
+        skip.wo = wo;
+        skip.wrows = (int)std::max<int64_t>(64, (N + 255) / 256);
         launch_quant_rows(x, dt, M, K, ldx, xq, x_scale, nullptr, &skip, st);
     }
     GemmArgs g{};

@@ -12,7 +12,9 @@ namespace pdq {
 // Outlier columns of the LLM.int8() decomposition, for the row quantizer:
 // they take no part in the absmax and are coded 0, and with xo set their
 // 16-bit values are also packed into xo[r, :] (pitch P, zero-padded to a
-// multiple of 16) when *count <= max_out.
+// multiple of 16) when *count <= max_out.  With w16 set, the same launch also
+// gathers wo[n, :] = w16[n, idx[:]] (pitch P, zero-padded likewise) in extra
+// workgroups of wrows weight rows each, placed first in the grid.
 struct OutlierSkip {
     const uint8_t* mask;   // [K/8] bit j of byte c: column 8c + j is an outlier
     const int32_t* idx;    // [max_out] ascending outlier columns (the first max_out)
@@ -20,6 +22,12 @@ struct OutlierSkip {
     int max_out;
     uint16_t* xo;          // [rows, P] or null
     int P;
+    const uint16_t* w16;   // [N, ldw] 16-bit weight, or null: no W gather
+    int64_t ldw;
+    int64_t N;
+    uint16_t* wo;          // [N, P]
+    int wrows;             // weight rows per gather workgroup
+    int gblocks;           // the launch's first gblocks workgroups gather W (set by the launcher)
 };
 // Per-row absmax symmetric INT8: q (packed tiles of pdq_device.h, padding
 // zeroed), scale[r]; optional code sums; optional outlier columns to skip
@@ -116,9 +124,6 @@ bool decode_fusable(int64_t M, int64_t K);
 void launch_decode_fused(const DecodeArgs& a, hipStream_t st);
 
 // outlier.hip -------------------------------------------------------------
-// Capacity (outlier columns) up to which the W gather is fused into
-// launch_outlier_index; beyond it a separate gather runs.
-constexpr int kOutlierIdxCap = 4096;
 // Row blocks of the partial predicate pass (at most 32), rows per block, and
 // the byte pitch of one block's predicate row (K/8 chunks, padded to 16).
 int outlier_row_blocks(int64_t M);
@@ -128,16 +133,8 @@ int outlier_partial_pitch(int64_t K);
 void launch_outlier_partial(const void* x, int dt, int64_t M, int64_t K, int64_t ldx,
                             float threshold, uint8_t* partial, hipStream_t st);
 // From the partial predicates: mask[c] (K/8 bytes, padded to a multiple of
-// 4), idx (first max_out ascending outlier columns), *count; and wo[n, :] =
-// w16[n, idx[:]] zero-padded to round_up(count, 16) when wo is set and
-// count <= max_out.
-void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask,
-                          int32_t* idx, int32_t* count, int64_t max_out,
-                          const void* w16, int64_t N, int64_t ldw, uint16_t* wo, int P,
-                          hipStream_t st);
-// dst[r, j] = src[r, idx[j]] for j < count, 0 for count <= j < round_up(count, 16);
-// nothing when count > max_out.  16-bit elements.
-void launch_gather_cols(const void* src, int64_t rows, int64_t ld, const int32_t* idx,
-                        const int32_t* count, int max_out, uint16_t* dst, int P, hipStream_t st);
+// 4), idx (first max_out ascending outlier columns), *count.
+void launch_outlier_index(const uint8_t* partial, int64_t M, int64_t K, uint8_t* mask, int32_t* idx,
+                          int32_t* count, int64_t max_out, hipStream_t st);
 
 }  // namespace pdq

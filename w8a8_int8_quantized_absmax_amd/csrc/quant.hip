@@ -55,6 +55,44 @@ __device__ __forceinline__ uint32_t skip_mask(const OutlierSkip& sk, int chunk) 
         return sk.mask[chunk];
 }
 
+// W_out rows [b * wrows, ...) of the LLM.int8() decomposition: wo[n, j] =
+// w16[n, idx[j]] for j < count, zeros up to the next multiple of 16, nothing
+// when the count exceeds max_out.  Up to 256 columns one per thread, 256 /
+// used rows at a time, eight rows' loads issued (clamped) before any of them
+// is stored (the reads are scattered: a 64-byte sector per 2-byte value);
+// beyond, a loop over the columns.  The index list and the count are
+// published by the index kernel earlier on the stream.
+__device__ __forceinline__ void gather_w_block(const OutlierSkip& sk, int64_t b) {
+    const int tid = threadIdx.x;
+    const int total = *sk.count;
+    if (total > sk.max_out) return;
+    const int used = (total + 15) / 16 * 16;
+    const int64_t row0 = b * sk.wrows;
+    const int nrows = (int)min((int64_t)sk.wrows, sk.N - row0);
+    if (used == 0 || nrows <= 0) return;
+    if (used <= 256) {
+        constexpr int kG = 8;
+        const int rpi = 256 / used, rl = tid / used, j = tid - rl * used;
+        const int col = sk.idx[min(j, total - 1)];
+        if (rl < rpi) {
+            for (int rb = rl; rb < nrows; rb += rpi * kG) {
+                uint16_t v[kG];
+#pragma unroll
+                for (int u = 0; u < kG; ++u) v[u] = sk.w16[(row0 + min(rb + u * rpi, nrows - 1)) * sk.ldw + col];
+#pragma unroll
+                for (int u = 0; u < kG; ++u) {
+                    const int r = rb + u * rpi;
+                    if (r < nrows) sk.wo[(row0 + r) * sk.P + j] = j < total ? v[u] : (uint16_t)0;
+                }
+            }
+        }
+    } else {
+        for (int r = 0; r < nrows; ++r)
+            for (int j = tid; j < used; j += 256)
+                sk.wo[(row0 + r) * sk.P + j] = j < total ? sk.w16[(row0 + r) * sk.ldw + sk.idx[j]] : (uint16_t)0;
+    }
+}
+
 // The chunk with its skipped elements (bit j of m) replaced by +0: they then
 // neither raise the absmax nor get a nonzero code.  Plain bit operations, so
 // no per-element lane masks stay live between the absmax and the codes.
@@ -181,8 +219,16 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
                                                     float* __restrict__ scale,
                                                     int32_t* __restrict__ rowint,
                                                     OutlierSkip skip) {
+    int64_t blk = blockIdx.x;
+    if constexpr (SKIP) {
+        if (blk < skip.gblocks) {  // a W_out gather workgroup
+            gather_w_block(skip, blk);
+            return;
+        }
+        blk -= skip.gblocks;
+    }
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t row = blk * kRowsPerBlock + (threadIdx.x >> 6);
     // whole wavefronts leave together; the rows of the last 16-row group past
     // `rows` are padding, written as zeros
     if (row >= (rows + kWGroup - 1) / kWGroup * kWGroup) return;
@@ -530,8 +576,15 @@ __global__ __launch_bounds__(256) void k_silu_mul_quant_wg(const void* __restric
                                                            void* __restrict__ h_out, int64_t ldh_bytes,
                                                            OutlierSkip skip) {
     static_assert(!SKIP || (MODE == kRowPlain && DT != kF32), "outlier columns: plain 16-bit rows only");
+    int64_t row = blockIdx.x;
+    if constexpr (SKIP) {
+        if (row < skip.gblocks) {  // a W_out gather workgroup
+            gather_w_block(skip, row);
+            return;
+        }
+        row -= skip.gblocks;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t row = blockIdx.x;
     const int ktiles = (nch + 7) / 8;
     int8_t* const qg = q + wpack_block(row / kWGroup, 0, ktiles);
     const int rg = (int)(row % kWGroup);
@@ -648,9 +701,10 @@ void silu_mul_quant_wg(const void* gate, int64_t ldg, const void* up, int64_t ld
                        const OutlierSkip* skip = nullptr) {
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
     constexpr int eb = Elem<DT>::bytes;
-    const OutlierSkip none{};
-    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, MODE, SKIP>), dim3((unsigned)rows_pad), dim3(256), 0, st,
-                       gate, ldg * eb, up, ldu * eb, rows, nch, q, scale, rowint, h, ldh * eb, skip ? *skip : none);
+    OutlierSkip sk = skip ? *skip : OutlierSkip{};
+    sk.gblocks = sk.w16 && sk.N > 0 ? (int)((sk.N + sk.wrows - 1) / sk.wrows) : 0;
+    hipLaunchKernelGGL((k_silu_mul_quant_wg<DT, CPT, MODE, SKIP>), dim3((unsigned)(rows_pad + sk.gblocks)), dim3(256),
+                       0, st, gate, ldg * eb, up, ldu * eb, rows, nch, q, scale, rowint, h, ldh * eb, sk);
 }
 
 template <int DT, int CPL>
@@ -694,19 +748,23 @@ void launch_rows(int64_t rows, const void* x, int64_t ldb, int nch, int8_t* q, f
                  int32_t* colsum, const OutlierSkip* skip, bool asym, hipStream_t st) {
     const OutlierSkip none{};
     const int64_t rows_pad = (rows + kWGroup - 1) / kWGroup * kWGroup;
-    const dim3 grid((unsigned)((rows_pad + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (asym)
+    const int64_t qblocks = (rows_pad + kRowsPerBlock - 1) / kRowsPerBlock;
+    const dim3 grid((unsigned)qblocks);
+    if (asym) {
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false, true>), grid, dim3(256), 0, st, x,
                            ldb, rows, nch, q, scale, colsum, none);
-    else if (skip)
-        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), grid, dim3(256), 0, st, x, ldb,
-                           rows, nch, q, scale, colsum, *skip);
-    else if (colsum)
+    } else if (skip) {
+        OutlierSkip sk = *skip;
+        sk.gblocks = sk.w16 && sk.N > 0 ? (int)((sk.N + sk.wrows - 1) / sk.wrows) : 0;
+        hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, true, false>), dim3((unsigned)(qblocks + sk.gblocks)),
+                           dim3(256), 0, st, x, ldb, rows, nch, q, scale, colsum, sk);
+    } else if (colsum) {
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, true>), grid, dim3(256), 0, st, x, ldb,
                            rows, nch, q, scale, colsum, none);
-    else
+    } else {
         hipLaunchKernelGGL((k_quant_rows<DT, CPL, FULL, false, false>), grid, dim3(256), 0, st, x, ldb,
                            rows, nch, q, scale, colsum, none);
+    }
 }
 
 template <int DT, int CPL>
