@@ -119,12 +119,21 @@ size_t pdq_act_bytes(int64_t M, int64_t K);
  * quantizer into the skinny kernel; pdq_linear_int8_outlier always runs the
  * tiled one).  Both give the same bits.  -1 when M < 1 or N < 1.
  *   PDQ_GEMM_SKINNY  one pass over the weight per 64 activation rows,
- *                    16 or 32 channels per workgroup (all M <= 64, and
+ *                    16 to 64 channels per workgroup (all M <= 64, and
  *                    larger M while that is estimated to be faster)
  *   PDQ_GEMM_TILED   256 x 256 output tiles staged through LDS
  */
 enum { PDQ_GEMM_SKINNY = 0, PDQ_GEMM_TILED = 1 };
 int pdq_gemm_kernel(int64_t M, int64_t N);
+
+/*
+ * Weight channels per workgroup of the skinny kernel for M activation rows
+ * and N weight channels: 16, 32, 48 or 64 (16 up to 16 rows; beyond, the
+ * width that moves the fewest bytes through the busiest compute unit).  A
+ * performance choice only: every width gives the same bits.  -1 when M < 1
+ * or N < 1.
+ */
+int pdq_skinny_channels(int64_t M, int64_t N);
 
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream);

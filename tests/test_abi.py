@@ -277,6 +277,22 @@ def test_gemm_kernel_choice(L):
     assert k(256, 4096) == 0                    # a few hundred rows of a 4096-wide weight
 
 
+def test_skinny_channels_choice(L):
+    """Channels per workgroup of the skinny kernel: 16 up to 16 rows; beyond,
+    the width that moves the fewest bytes through the busiest of 256 CUs."""
+    c = L.pdq_skinny_channels
+    assert c(0, 16) == -1 and c(16, 0) == -1
+    for n in (4096, 12288, 28672):              # up to 16 rows: the most workgroups
+        assert c(1, n) == c(8, n) == c(16, n) == 16
+    assert c(32, 4096) == 16 and c(64, 4096) == 16     # O projection: 256 workgroups of 16
+    # QKV: 16 channels give 3 workgroups per CU x (16 + 32) bytes per K value,
+    # 48 channels exactly 256 workgroups x (48 + 32)
+    assert c(32, 12288) == 48 and c(64, 12288) == 48
+    assert c(32, 28672) == 64 and c(64, 28672) == 64   # gate+up: 448 workgroups of 64
+    assert c(17, 5000) == 32
+    assert c(96, 4096) == 32 and c(256, 4096) == 64    # beyond 64 rows: one workgroup row per 64
+
+
 def test_zeropoint_validation(L):
     lin = L.pdq_linear_zeropoint
 

@@ -451,12 +451,14 @@ def test_decode_fused_shapes(dtype, m, n, k):
 
 
 # Static codes past 64 rows: the zero-point correction in the epilogue of
-# the skinny kernel (the first four; 300 x 4100 with 32 channels per
+# the skinny kernel (the first four; 300 x 4100 with 48 channels per
 # workgroup) and of the tiled GEMM (the others).
 @pytest.mark.parametrize("m,n,k", [(65, 700, 1040), (300, 256, 2048), (513, 1000, 4096), (300, 4100, 1040),
                                    (2048, 2600, 1040), (1600, 4096, 2048), (3000, 1500, 2048)])
 def test_static_large_m(m, n, k):
     assert pdq.gemm_kernel(m, n) == ("tiled" if m in (2048, 1600, 3000) else "skinny")
+    if (m, n) == (300, 4100):
+        assert pdq.skinny_channels(m, n) == 48
     cal = [synth.activations(4900 + b, 64, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16") for b in range(3)]
     _, s, z = O.calibrate(cal)
     x = synth.activations(4950 + m, m, k, [2, k - 3], 100.0, offset=0.1, dtype="bf16")
@@ -467,15 +469,31 @@ def test_static_large_m(m, n, k):
 # workgroup (K not a multiple of 4 x 64; at K = 64 three wavefronts get no
 # tile at all): a tile a wavefront does not have must add nothing (MFMA
 # instructions ignore the lane mask, so the kernel must branch around them).
-# 16 and 32 channels per workgroup, one to three row blocks of 16.
-@pytest.mark.parametrize("m,n,k", [(20, 300, 4288), (10, 12300, 4288), (20, 9000, 320), (3, 12300, 576),
-                                   (32, 8200, 64), (17, 5000, 1088)])
-def test_skinny_uneven_tiles_per_wavefront(m, n, k):
-    assert pdq.gemm_kernel(m, n) == "skinny"
+# 16, 32, 48 and 64 channels per workgroup, one to three row blocks of 16.
+@pytest.mark.parametrize("m,n,k,ch", [(20, 300, 4288, 16), (10, 12300, 4288, 16), (20, 9000, 320, 48),
+                                      (3, 12300, 576, 16), (32, 8200, 64, 48), (17, 5000, 1088, 32),
+                                      (40, 12328, 64, 64)])
+def test_skinny_uneven_tiles_per_wavefront(m, n, k, ch):
+    assert pdq.gemm_kernel(m, n) == "skinny" and pdq.skinny_channels(m, n) == ch
     x = synth.activations(4980 + m, m, k, [1, k - 2], 100.0, offset=0.1, dtype="bf16")
     w = synth.weights(4990 + n, n, k, "bf16")
     prefill_case(x, w, "bf16", bias=synth.bias(4991, n))
     decode_case(x, w, "bf16", F32(0.9), -3, bias=synth.bias(4992, n))
+
+
+# Each width of the skinny kernel (32, 48, 64 weight channels per workgroup)
+# with a ragged last workgroup (N not a multiple of the width: its last
+# channel group partly past N, or wholly, then clamped onto the last one and
+# not stored), ragged rows and K, and, past 64 rows, two to four row blocks
+# with a short last one; static (zero-point) and per-token epilogues.
+@pytest.mark.parametrize("m,n,k,ch", [(24, 8200, 4096, 48), (40, 12328, 1040, 64), (33, 6000, 2048, 32),
+                                      (100, 6144, 2048, 48), (200, 4096, 1040, 64), (64, 12280, 1088, 48)])
+def test_skinny_channel_widths(m, n, k, ch):
+    assert pdq.gemm_kernel(m, n) == "skinny" and pdq.skinny_channels(m, n) == ch
+    x = synth.activations(5050 + m, m, k, [1, k - 2], 100.0, offset=0.1, dtype="bf16")
+    w = synth.weights(5060 + n, n, k, "bf16")
+    prefill_case(x, w, "bf16", bias=synth.bias(5070, n))
+    decode_case(x, w, "bf16", F32(0.9), -3, bias=synth.bias(5071, n))
 
 
 def test_decode_fused_strided_rows():

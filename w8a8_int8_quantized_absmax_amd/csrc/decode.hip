@@ -13,8 +13,8 @@
 //
 // The weight matrix is read exactly once and is the whole cost (the
 // hardware-acceleration page's "data movement and memory bandwidth": decode is
-// bandwidth-bound).  Each 256-thread workgroup owns 16 weight channels (32
-// when there are workgroups enough to spare); its four wavefronts interleave
+// bandwidth-bound).  Each 256-thread workgroup owns 16, 32, 48 or 64 weight
+// channels (decode_groups); its four wavefronts interleave
 // over the K tiles of the packed weight (wavefront w takes tiles w, w + 4,
 // ...) and multiply with v_mfma_i32_16x16x64_i8,
 // weight channels as the row operand, activation rows as the column operand.
@@ -51,8 +51,9 @@ namespace pdq {
 
 namespace {
 
-constexpr int kRows = 16;   // weight rows per workgroup
+constexpr int kRows = 16;   // weight rows per channel group
 constexpr int kMRows = 64;  // activation rows per workgroup (four register blocks of 16)
+constexpr int kCUs = 256;   // compute units of an MI355X
 
 // Epilogue operands of this lane's four outputs n = n0 + 4 (lane / 16) + r
 // (16x16 accumulator layout: register r is row 4 (lane / 16) + r, the weight
@@ -139,8 +140,8 @@ constexpr int kFusedWave = kFusedBytes / 4 + 16 * 64;
 // 16 r -- the only ones whose MFMA column is the activation row -- take
 // quarter r from lane 16 r + j of their DPP row: no LDS round trip.
 //
-// NG: 16-channel groups per workgroup (2 when there are workgroups enough to
-// spare: the activation fragments then serve 32 channels per load).
+// NG: 16-channel groups per workgroup (1 to 4, chosen by decode_groups):
+// each activation fragment then serves 16 NG channels per load.
 template <int NMB, bool FUSED, int DT, int kQ = 1, bool ONEROW = false, int NG = 1>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     static_assert(!FUSED || NG == 1, "the one-launch path has one channel group");
@@ -148,8 +149,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     // replays, weights rotated beyond the MALL): 16 channels and 17..32 rows
     // run 5% faster with 4 tiles (three workgroups per CU) than with 6 (two);
     // 33..64 rows are best at 4, 32 channels at 4 (17..32 rows) -- 2 or 3
-    // were slower or no faster.
-    constexpr int KB = NG == 1 ? (NMB == 1 ? 8 : 4) : (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3));
+    // were slower or no faster.  48 and 64 channels take 2 or 3, which keeps
+    // two workgroups per CU up to 32 rows.
+    constexpr int KB = NG == 1   ? (NMB == 1 ? 8 : 4)
+                       : NG == 2 ? (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3))
+                       : NG == 3 ? (NMB == 1 ? 4 : (NMB == 2 ? 3 : 2))
+                                 : (NMB == 1 ? 4 : 2);
     __shared__ v4i red[4][NG * NMB][64];
     __shared__ __attribute__((aligned(16))) int8_t xs[FUSED ? 4 : 1][FUSED ? kFusedWave : 16];
     // The wavefront index read through readfirstlane is known to be uniform,
@@ -391,14 +396,36 @@ void launch_decode_fused(const DecodeArgs& a, hipStream_t st) {
     }
 }
 
-// 32 channels per workgroup halve the activation fragments each channel
-// costs, but also the number of workgroups: worth it from two workgroups per
-// CU (256 CUs).  Measured at K = 4096: 28672 channels x 32 rows (896 such
-// workgroups) 26.9 us against 32.9 with 16 channels; 12288 channels x 32 /
-// 48 / 64 rows and 6144 x 128 (384 of them) 11.2 / 14.3 / 17.2 / 17.0 us
-// with 16 channels against 11.5 / 14.6 / 18.6 / 18.5 with 32.
-bool decode_wide_groups(int64_t M, int64_t N) {
-    return (N + 2 * kRows - 1) / (2 * kRows) * ((M + kMRows - 1) / kMRows) >= 512;
+// Channel groups per workgroup.  Each workgroup reads the activation
+// fragments of all its rows once, whatever its channel count, so wider
+// workgroups cut those bytes per weight byte but leave fewer workgroups.  Up
+// to 16 rows the fragments cost no more than the weight and 16 channels (the
+// most workgroups, the most weight bytes in flight) run.  Beyond, the time
+// follows the bytes that the busiest CU pulls from the L2: ceil(workgroups /
+// 256) x (16 g + rows) x K for g groups; the g in 1..4 with the fewest runs
+// (ties to the smaller).  Measured with the weights streamed from HBM: at
+// 8, 32 and 64 rows (12288, 4096 and 28672 channels at K = 4096, 4096 at K =
+// 14336) the choice is the fastest of the four widths; from 8 to 512 rows
+// (also 11008 channels) it is never more than 2% slower than the earlier
+// rule (32 channels once that gave 512 workgroups, else 16), except at 16
+// rows x 28672 channels (4%), and up to 35% faster: 12288 channels at 32 /
+// 64 rows 15.5 / 21.7 -> 13.0 / 15.3 us (48 channels), 28672 at 64 rows
+// 42.2 -> 32.2 us (64), 4096 x 4096 at 256 rows 19.9 -> 14.7 us (64).
+int decode_groups(int64_t M, int64_t N) {
+    const int64_t rows = M < kMRows ? M : kMRows;
+    if (rows <= 16) return 1;
+    const int64_t rowblocks = (M + kMRows - 1) / kMRows;
+    int best = 1;
+    int64_t best_bytes = 0;
+    for (int g = 1; g <= 4; ++g) {
+        const int64_t wgs = (N + kRows * g - 1) / (kRows * g) * rowblocks;
+        const int64_t bytes = (wgs + kCUs - 1) / kCUs * (kRows * g + rows);
+        if (g == 1 || bytes < best_bytes) {
+            best = g;
+            best_bytes = bytes;
+        }
+    }
+    return best;
 }
 
 template <int NG>
@@ -414,10 +441,12 @@ void launch_gemv_ng(const DecodeArgs& a, hipStream_t st) {
 
 void launch_decode_gemv(const DecodeArgs& a, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return;
-    if (decode_wide_groups(a.M, a.N))
-        launch_gemv_ng<2>(a, st);
-    else
-        launch_gemv_ng<1>(a, st);
+    switch (decode_groups(a.M, a.N)) {
+        case 1: launch_gemv_ng<1>(a, st); break;
+        case 2: launch_gemv_ng<2>(a, st); break;
+        case 3: launch_gemv_ng<3>(a, st); break;
+        default: launch_gemv_ng<4>(a, st); break;
+    }
 }
 
 }  // namespace pdq

@@ -29,7 +29,7 @@ constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
 // the 256 x 256-tile GEMM.  The skinny kernel's work is ceil(N / 16) x
 // ceil(M / 64) units, each one pass over the K tiles of 16 weight channels
 // for up to 64 activation rows, and costs about 4 us plus 4.7 us per 256 of
-// them with 16 channels per workgroup, 3.6 us with 32; the tiled GEMM costs
+// them with 16 channels per workgroup, 3.6 us with more; the tiled GEMM costs
 // about 52 us per round of 256 tiles, however few tiles the round holds (all
 // measured on MI355X at K = 4096; K scales both alike).  Up to 64 rows the
 // skinny kernel always runs.
@@ -37,7 +37,7 @@ bool skinny_gemm(int64_t M, int64_t N) {
     if (M <= 64) return true;
     const double units = (double)((N + 15) / 16) * (double)((M + 63) / 64);
     const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
-    const double per256 = decode_wide_groups(M, N) ? 3.6 : 4.7;
+    const double per256 = decode_groups(M, N) > 1 ? 3.6 : 4.7;
     return 4.0 + per256 * units / 256.0 < 52.0 * ceil(tiles / 256.0);
 }
 
@@ -214,6 +214,11 @@ size_t pdq_act_bytes(int64_t M, int64_t K) { return pdq_weight_bytes(M, K); }
 int pdq_gemm_kernel(int64_t M, int64_t N) {
     if (M < 1 || N < 1) return -1;
     return skinny_gemm(M, N) ? PDQ_GEMM_SKINNY : PDQ_GEMM_TILED;
+}
+
+int pdq_skinny_channels(int64_t M, int64_t N) {
+    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return -1;
+    return 16 * decode_groups(M, N);
 }
 
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,

@@ -115,10 +115,10 @@ struct DecodeArgs {
     uint32_t* sat;   // nullable saturation counter
     int narrow;      // codes clamped to [-127, 127] (symmetric or zero-point grid)
 };
-// Activations already quantized (xq); 16 or 32 channels per workgroup
-// (decode_wide_groups).
+// Activations already quantized (xq); 16 x decode_groups(M, N) weight
+// channels per workgroup (1 to 4 groups of 16).
 void launch_decode_gemv(const DecodeArgs& a, hipStream_t st);
-bool decode_wide_groups(int64_t M, int64_t N);
+int decode_groups(int64_t M, int64_t N);
 // Static quantization fused into the GEMM; only when decode_fusable(M, K).
 bool decode_fusable(int64_t M, int64_t K);
 void launch_decode_fused(const DecodeArgs& a, hipStream_t st);

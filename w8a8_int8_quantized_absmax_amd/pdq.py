@@ -60,6 +60,7 @@ SIGNATURES = {
     "pdq_weight_bytes": (_sz, [_i64, _i64]),
     "pdq_act_bytes": (_sz, [_i64, _i64]),
     "pdq_gemm_kernel": (ctypes.c_int, [_i64, _i64]),
+    "pdq_skinny_channels": (ctypes.c_int, [_i64, _i64]),
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _i64, _vp, _sz, _vp, _vp]),
@@ -170,6 +171,11 @@ unpack_weight = unpack
 def gemm_kernel(m: int, n: int) -> str:
     """The GEMM kernel the library runs for M activation rows x N channels: "skinny" or "tiled"."""
     return {0: "skinny", 1: "tiled"}.get(int(lib().pdq_gemm_kernel(m, n)), "none")
+
+
+def skinny_channels(m: int, n: int) -> int:
+    """Weight channels per workgroup of the skinny kernel for M rows x N channels (16 .. 64)."""
+    return int(lib().pdq_skinny_channels(m, n))
 
 
 class Codes:
