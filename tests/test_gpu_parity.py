@@ -79,13 +79,14 @@ def test_prefill_tiny_f32():
 
 
 # (2048, 2600, 1040) runs on the tiled GEMM, the others on the skinny kernel
-# ((200, 4100) with 32 channels per workgroup, the last one's second group
-# past N).
+# ((200, 4100) with 48 channels per workgroup, the last one's second group
+# partly and its third wholly past N).
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(300, 700, 1040), (1, 257, 128), (257, 1, 16), (513, 256, 2048),
                                    (200, 4100, 1040), (2048, 2600, 1040)])
 def test_prefill_ragged(dtype, m, n, k):
     assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
+    assert (m, n) != (200, 4100) or pdq.skinny_channels(m, n) == 48
     x = synth.activations(2000 + m, m, k, [0, k - 1, k // 3], 100.0, dtype=dtype)
     if m > 2:
         x[2, :] = 0.0  # all-zero token: scale 1, codes 0
@@ -148,7 +149,7 @@ def prefill_asym_case(x, w, dtype, bias=None, rows=None):
 
 
 # Both GEMM kernels: (2048, 2600) runs on the tiled one, the others on the
-# skinny one ((200, 4100) with 32 channels per workgroup).
+# skinny one ((200, 4100) with 48 channels per workgroup).
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1040), (37, 520, 2048), (300, 700, 1040), (257, 1, 16),
                                    (200, 4100, 1040), (2048, 2600, 1040)])
@@ -367,7 +368,7 @@ def test_zeropoint_calibration():
     assert host(out[0]).view(np.uint32)[0] == np.array([s], F32).view(np.uint32)[0] and int(host(out[1])[0]) == z
 
 
-# One launch (M * K <= 8192), the skinny kernel (16 and 32 channels per
+# One launch (M * K <= 8192), the skinny kernel (16 and 48 channels per
 # workgroup) and the tiled GEMM; decode values beyond the calibrated range
 # saturate at both ends.
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])

@@ -148,9 +148,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     // K tiles per batch, two batches in flight.  Measured per shape (graph
     // replays, weights rotated beyond the MALL): 16 channels and 17..32 rows
     // run 5% faster with 4 tiles (three workgroups per CU) than with 6 (two);
-    // 33..64 rows are best at 4, 32 channels at 4 (17..32 rows) -- 2 or 3
-    // were slower or no faster.  48 and 64 channels take 2 or 3, which keeps
-    // two workgroups per CU up to 32 rows.
+    // 33..64 rows are best at 4, and 32 channels with 17..32 rows at 4 (2 or
+    // 3 were slower or no faster).  48 and 64 channels take 2 or 3, which
+    // keeps two workgroups per CU up to 32 rows.
     constexpr int KB = NG == 1   ? (NMB == 1 ? 8 : 4)
                        : NG == 2 ? (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3))
                        : NG == 3 ? (NMB == 1 ? 4 : (NMB == 2 ? 3 : 2))
