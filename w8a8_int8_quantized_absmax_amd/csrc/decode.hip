@@ -149,11 +149,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     // replays, weights rotated beyond the MALL): 16 channels and 17..32 rows
     // run 5% faster with 4 tiles (three workgroups per CU) than with 6 (two);
     // 33..64 rows are best at 4, and 32 channels with 17..32 rows at 4 (2 or
-    // 3 were slower or no faster).  48 and 64 channels take 2 or 3, which
-    // keeps two workgroups per CU up to 32 rows.
+    // 3 were slower or no faster).  48 channels with 17..32 rows take 4 (one
+    // workgroup per CU, as where that width is chosen: 12288 channels x 32
+    // rows 12.6 us against 13.0 with 3), otherwise 2; 64 channels take 2
+    // (3 was 4-12% slower at 24..512 rows).
     constexpr int KB = NG == 1   ? (NMB == 1 ? 8 : 4)
                        : NG == 2 ? (NMB == 1 ? 6 : (NMB == 2 ? 4 : 3))
-                       : NG == 3 ? (NMB == 1 ? 4 : (NMB == 2 ? 3 : 2))
+                       : NG == 3 ? (NMB == 1 ? 4 : (NMB == 2 ? 4 : 2))
                                  : (NMB == 1 ? 4 : 2);
     __shared__ v4i red[4][NG * NMB][64];
     __shared__ __attribute__((aligned(16))) int8_t xs[FUSED ? 4 : 1][FUSED ? kFusedWave : 16];
