@@ -789,10 +789,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "silu", "block"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "silu", "block", "block-gemv"], default="all",
                     help="prefill: the headline line without the other workloads; decode: only the decode "
                          "measurements, in a line of their own (for counter collection); silu: only the "
-                         "fused SiLU*up quantizer and its down projection")
+                         "fused SiLU*up quantizer and its down projection; block-gemv: the decoder block's "
+                         "four decode GEMMs at batch 32, six calls each (for counter collection)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline run: the per-token vs static C_s / C_g sweep over "
                          "M on the decode linear (one JSON line of its own)")
@@ -859,6 +860,24 @@ def main():
                           "prefill_us": round(blk["ms_prefill"] * 1e3, 1),
                           "decode_us_per_step": round(blk["ms_step"] * 1e3, 2),
                           "decode_GBps": round(blk["step_bytes"] / (blk["ms_step"] * 1e-3) / 1e9, 1)}), flush=True)
+        return
+    if args.only == "block-gemv":
+        # random weights and activations of the decoder block's shapes, six
+        # eager GEMM calls per linear in the block's order; the line reports
+        # the kernel plan (the timings of this workload are the block's)
+        c = synth.DecoderBlock()
+        out = {}
+        for name, n, k in c.linears:
+            wq, ws, cs = pdq.quantize_weight((torch.randn(n, k, device="cuda") * 0.02).to(torch.bfloat16))
+            xq = pdq.quantize_static((torch.randn(c.decode_batch, k, device="cuda") + 0.1).to(torch.bfloat16),
+                                     0.05, 3)
+            for _ in range(6):
+                pdq.gemm_static(xq, 0.05, 3, wq, ws, cs)
+            torch.cuda.synchronize()
+            out[name] = {"N": n, "K": k, "channels_per_workgroup": pdq.skinny_channels(c.decode_batch, n)}
+            del wq, ws, cs, xq
+        print(json.dumps({"metric": "decoder block decode GEMMs", "unit": "us", "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": "static INT8 codes, batch 32"}, "per_linear": out}), flush=True)
         return
     if args.only == "decode":
         dec = bench_decode(args, torch, pdq, synth)
