@@ -23,8 +23,6 @@
 #include "pdq_device.h"
 #include "pdq_kernels.h"
 
-#include <algorithm>
-
 namespace pdq {
 
 namespace {
