@@ -104,6 +104,25 @@ const char* pdq_status_string(pdq_status s);
 size_t pdq_weight_bytes(int64_t N, int64_t K);
 
 /*
+ * Layout conversion for callers that hold INT8 matrices in plain row-major
+ * form (weights quantized by another tool, codes to be read back on the
+ * device): no quantization, only the byte order.
+ *
+ * pdq_pack_int8: src [rows, K] int8, row pitch ld bytes (ld >= K, src and ld
+ *   16-byte aligned, K a multiple of 16) -> packed, pdq_weight_bytes(rows, K)
+ *   bytes in the layout described above (rows >= rows and K values >= K
+ *   written as 0).  A weight packed this way, with its own per-channel scales
+ *   and code sums, is a valid wq for every GEMM entry point.
+ * pdq_unpack_int8: the inverse, packed -> dst [rows, K] int8 with row pitch
+ *   ld bytes (the padding is not copied; the bytes of dst between K and ld are
+ *   left untouched).
+ * Errors as elsewhere: PDQ_ERR_SHAPE, PDQ_ERR_NULL, PDQ_ERR_ALIGN, checked
+ * before anything is enqueued.
+ */
+pdq_status pdq_pack_int8(const int8_t* src, int64_t rows, int64_t K, int64_t ld, int8_t* packed, void* stream);
+pdq_status pdq_unpack_int8(const int8_t* packed, int64_t rows, int64_t K, int8_t* dst, int64_t ld, void* stream);
+
+/*
  * Activation codes (the xq of every entry point below) use the same packed
  * layout with M rows in place of the N channels: pdq_act_bytes(M, K) bytes
  * (= pdq_weight_bytes(M, K)), rows >= M and K values >= K written as 0.  The

@@ -79,6 +79,24 @@ def dec(L, x=P, dt=1, M=4, K=64, ldx=64, s=0.5, z=-3, wq=P, ws=P, cs=P, bias=Non
     return L.pdq_linear_decode(x, dt, M, K, ldx, s, z, wq, ws, cs, bias, N, xq, y, ldy, acc, sat, None)
 
 
+def test_pack_validation(L):
+    pk, up = L.pdq_pack_int8, L.pdq_unpack_int8
+    assert pk(P, 4, 40, 48, P, None) == SHAPE          # K not a multiple of 16
+    assert pk(P, 4, 64, 32, P, None) == SHAPE          # pitch below K
+    assert pk(None, 4, 64, 64, P, None) == NULL
+    assert pk(P, 4, 64, 64, None, None) == NULL
+    assert pk(P + 8, 4, 64, 64, P, None) == ALIGN
+    assert pk(P, 4, 64, 72, P, None) == ALIGN          # row pitch not 16-byte aligned
+    assert pk(P, 4, 64, 64, P + 4, None) == ALIGN
+    assert pk(P, 0, 64, 64, None, None) == OK
+    assert up(P, 4, 40, P, 48, None) == SHAPE
+    assert up(None, 4, 64, P, 64, None) == NULL
+    assert up(P, 4, 64, None, 64, None) == NULL
+    assert up(P + 4, 4, 64, P, 64, None) == ALIGN
+    assert up(P, 4, 64, P, 80 + 8, None) == ALIGN
+    assert up(P, 0, 64, None, 64, None) == OK
+
+
 def test_decode_validation(L):
     assert dec(L, dt=-1) == DTYPE
     assert dec(L, K=8, ldx=8) == SHAPE

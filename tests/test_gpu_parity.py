@@ -497,6 +497,44 @@ def test_skinny_channel_widths(m, n, k, ch):
     decode_case(x, w, "bf16", F32(0.9), -3, bias=synth.bias(5071, n))
 
 
+# Layout conversion: plain int8 [rows, K] <-> the packed tile image.  The
+# packed image equals the numpy packer's (written from the header's
+# definition) byte for byte, padding included, at ragged row counts, K and row
+# pitches; unpacking gives the matrix back and leaves a wider destination's
+# gap bytes alone; a weight packed this way (codes and scales from the
+# oracle) runs the GEMMs to the oracle's results.
+@pytest.mark.parametrize("rows,k,ld", [(1, 16, 16), (5, 48, 64), (16, 64, 64), (37, 1040, 1072),
+                                       (300, 4096, 4096), (4100, 208, 224)])
+def test_pack_unpack_int8(rows, k, ld):
+    codes = synth.random_int8(9300 + rows, (rows, k))
+    src = torch.full((rows, ld), 77, dtype=torch.int8)
+    src[:, :k] = torch.from_numpy(codes)
+    src = src.cuda()[:, :k]
+    packed = pdq.pack_int8(src)
+    assert packed.numel() == pdq.weight_bytes(rows, k)
+    assert np.array_equal(host(packed), pack(codes))
+    dst = torch.full((rows, ld + 16), -5, dtype=torch.int8, device="cuda")
+    pdq.unpack_int8(packed, rows, k, out=dst[:, :k])
+    back = host(dst)
+    assert np.array_equal(back[:, :k], codes)
+    assert (back[:, k:] == -5).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(40, 300, 1040), (300, 520, 2048)])
+def test_gemm_on_a_weight_packed_from_plain_codes(m, n, k):
+    w = synth.weights(9400 + n, n, k, "bf16")
+    rq, rs, rc = O.quantize_weight(w)
+    wq = pdq.pack_int8(torch.from_numpy(rq).cuda())
+    x = synth.activations(9410 + m, m, k, [2, k - 3], 100.0, dtype="bf16")
+    res = pdq.linear_prefill(dev(x, "bf16"), wq, torch.from_numpy(rs).cuda(), want_acc=True)
+    xq_ref, sx_ref = O.quantize_rows_absmax(x)
+    acc = O.int_matmul(xq_ref, rq)
+    assert np.array_equal(host(res["acc"]), acc)
+    check_16bit(host(res["y"]), O.dequantize(acc, sx_ref, rs), "bf16", exact=True)
+    # the codes read back as a plain matrix on the device
+    assert np.array_equal(host(pdq.unpack_int8(res["xq"].data, m, k)), xq_ref)
+
+
 def test_decode_fused_strided_rows():
     m, n, k = 6, 300, 1024
     wide = synth.activations(4900, m, k + 48, [5], 100.0, offset=0.1, dtype="bf16")

@@ -221,6 +221,24 @@ int pdq_skinny_channels(int64_t M, int64_t N) {
     return 16 * decode_groups(M, N);
 }
 
+pdq_status pdq_pack_int8(const int8_t* src, int64_t rows, int64_t K, int64_t ld, int8_t* packed, void* stream) {
+    PDQ_TRY(check_operand(src, 1, rows, K, ld));
+    if (rows > 0 && !packed) return PDQ_ERR_NULL;
+    if (!aligned(packed, 16)) return PDQ_ERR_ALIGN;
+    if (rows == 0) return PDQ_OK;
+    launch_pack_int8(src, rows, K, ld, packed, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+pdq_status pdq_unpack_int8(const int8_t* packed, int64_t rows, int64_t K, int8_t* dst, int64_t ld, void* stream) {
+    PDQ_TRY(check_operand(dst, 1, rows, K, ld));
+    if (rows > 0 && !packed) return PDQ_ERR_NULL;
+    if (!aligned(packed, 16)) return PDQ_ERR_ALIGN;
+    if (rows == 0) return PDQ_OK;
+    launch_unpack_int8(packed, rows, K, dst, ld, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
 pdq_status pdq_quantize_weight(const void* w, pdq_dtype w_dt, int64_t N, int64_t K, int64_t ldw,
                                int8_t* wq, float* w_scale, int32_t* w_colsum, void* stream) {
     if (!dtype_ok(w_dt)) return PDQ_ERR_DTYPE;

@@ -123,6 +123,13 @@ int decode_groups(int64_t M, int64_t N);
 bool decode_fusable(int64_t M, int64_t K);
 void launch_decode_fused(const DecodeArgs& a, hipStream_t st);
 
+// layout.hip --------------------------------------------------------------
+// Plain row-major INT8 [rows, K] (row pitch ld bytes, 16-byte aligned rows)
+// to the packed tile layout of pdq_device.h and back; the packed image has
+// pdq_weight_bytes(rows, K) bytes, its padding written as zeros.
+void launch_pack_int8(const int8_t* src, int64_t rows, int64_t K, int64_t ld, int8_t* packed, hipStream_t st);
+void launch_unpack_int8(const int8_t* packed, int64_t rows, int64_t K, int8_t* dst, int64_t ld, hipStream_t st);
+
 // outlier.hip -------------------------------------------------------------
 // Row blocks of the partial predicate pass (at most 32), rows per block, and
 // the byte pitch of one block's predicate row (K/8 chunks, padded to 16).

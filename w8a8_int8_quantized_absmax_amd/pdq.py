@@ -61,6 +61,8 @@ SIGNATURES = {
     "pdq_act_bytes": (_sz, [_i64, _i64]),
     "pdq_gemm_kernel": (ctypes.c_int, [_i64, _i64]),
     "pdq_skinny_channels": (ctypes.c_int, [_i64, _i64]),
+    "pdq_pack_int8": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "pdq_unpack_int8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp]),
     "pdq_linear_int8_outlier": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _vp, _vp,
                                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _i64, _vp, _sz, _vp, _vp]),
@@ -171,6 +173,23 @@ unpack_weight = unpack
 def gemm_kernel(m: int, n: int) -> str:
     """The GEMM kernel the library runs for M activation rows x N channels: "skinny" or "tiled"."""
     return {0: "skinny", 1: "tiled"}.get(int(lib().pdq_gemm_kernel(m, n)), "none")
+
+
+def pack_int8(x: torch.Tensor) -> torch.Tensor:
+    """A plain int8 [rows, K] device matrix -> its packed image (pdq_weight_bytes(rows, K) bytes), the
+    layout every GEMM takes its weight and activation codes in."""
+    _check_mat(x, "x", (torch.int8,))
+    rows, k = x.shape
+    out = torch.empty(weight_bytes(rows, k), dtype=torch.int8, device=x.device)
+    _call("pdq_pack_int8", _p(x), rows, k, _ld(x), _p(out), _stream(x.device))
+    return out
+
+
+def unpack_int8(packed: torch.Tensor, rows: int, k: int, out=None) -> torch.Tensor:
+    """The packed image of an int8 [rows, K] matrix -> the plain [rows, K] int8 matrix on the device."""
+    dst = out if out is not None else torch.empty((rows, k), dtype=torch.int8, device=packed.device)
+    _call("pdq_unpack_int8", _p(packed), rows, k, _p(dst), _ld(dst), _stream(packed.device))
+    return dst
 
 
 def skinny_channels(m: int, n: int) -> int:
