@@ -368,6 +368,22 @@ def test_zeropoint_calibration():
     assert host(out[0]).view(np.uint32)[0] == np.array([s], F32).view(np.uint32)[0] and int(host(out[1])[0]) == z
 
 
+def zeropoint_case(x, w, dtype, s, z, bias=None):
+    wq, ws, cs, (rq, rs, rc) = weight_case(w, dtype)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    y, y_check = gapped(x.shape[0], w.shape[0])
+    with guarded():
+        res = pdq.linear_zeropoint(dev(x, dtype), s, z, wq, ws, cs, b, sat_count=sat, want_acc=True, out=y)
+    y_check()
+    ref = O.linear_zeropoint(x, F32(s), z, rq, rs, rc, bias)
+    assert codes_equal(res["xq"], ref["xq"])
+    assert int(host(sat)[0]) == ref["sat"]
+    assert np.array_equal(host(res["acc"]), ref["acc"])
+    check_16bit(host(res["y"]), ref["y32"], "bf16", exact=True)
+    return ref
+
+
 # One launch (M * K <= 8192), the skinny kernel (16 and 48 channels per
 # workgroup) and the tiled GEMM; decode values beyond the calibrated range
 # saturate at both ends.
@@ -381,20 +397,8 @@ def test_zeropoint_linear(dtype, m, n, k):
     big = 3.0 * max(float(np.abs(c).max()) for c in cal)
     x[0, 7], x[m - 1, 9] = big, -big
     x = synth.round_to(x, dtype)
-    w = synth.weights(8400 + n, n, k, dtype)
-    wq, ws, cs, (rq, rs, rc) = weight_case(w, dtype)
-    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
-    b = synth.bias(8500, n)
-    y, y_check = gapped(m, n)
-    with guarded():
-        res = pdq.linear_zeropoint(dev(x, dtype), s, z, wq, ws, cs, torch.from_numpy(b).cuda(), sat_count=sat,
-                                   want_acc=True, out=y)
-    y_check()
-    ref = O.linear_zeropoint(x, F32(s), z, rq, rs, rc, b)
-    assert codes_equal(res["xq"], ref["xq"])
-    assert int(host(sat)[0]) == ref["sat"] > 0
-    assert np.array_equal(host(res["acc"]), ref["acc"])
-    check_16bit(host(res["y"]), ref["y32"], "bf16", exact=True)
+    ref = zeropoint_case(x, synth.weights(8400 + n, n, k, dtype), dtype, s, z, bias=synth.bias(8500, n))
+    assert ref["sat"] > 0
     if m * k > 8192:
         assert pdq.gemm_kernel(m, n) == ("tiled" if m == 2048 else "skinny")
 
