@@ -45,7 +45,10 @@
  *     PDQ_ERR_SHAPE, since every kernel reads at least one 16-value chunk of
  *     each row it touches); every base pointer and every row pitch (ld *
  *     element size) of a K-wide operand must be a multiple of 16 bytes.  M and
- *     N may be 0 (nothing is written then).
+ *     N may be 0 (nothing is written then); each is at most 2^21 (2097152),
+ *     one operand holds at most 2^34 values (M * K, N * K) and one product at
+ *     most 2^39 outputs (M * N), so that every launch grid stays inside the
+ *     dispatch limits; larger shapes are PDQ_ERR_SHAPE.
  *   - Every argument check runs on the host before anything is enqueued; on
  *     error nothing is launched and no output is touched.  After the
  *     launches, a HIP launch error is reported as PDQ_ERR_HIP.
@@ -65,7 +68,7 @@ extern "C" {
 typedef enum {
     PDQ_OK = 0,
     PDQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
-    PDQ_ERR_SHAPE = 2,       /* negative size, K not in 16, 32, .., 65536, ld too small */
+    PDQ_ERR_SHAPE = 2,       /* negative or too large size, K not in 16, 32, .., 65536, ld too small */
     PDQ_ERR_DTYPE = 3,       /* dtype not accepted by this entry point          */
     PDQ_ERR_ALIGN = 4,       /* pointer or row pitch not 16-byte aligned        */
     PDQ_ERR_UNSUPPORTED = 5, /* value out of range (scale, zero point, ...)     */

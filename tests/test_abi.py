@@ -362,3 +362,18 @@ def test_silu_mul_validation(L):
     assert lcall(y=None) == NULL
     assert lcall(xq=None) == NULL
     assert lcall(M=0) == OK
+
+
+def test_shapes_beyond_the_launch_limits_are_refused(L):
+    """Rows beyond 2^21, more than 2^34 values in one operand or 2^39 outputs
+    in one product are shape errors (fake pointers: a launch would fault)."""
+    big = 1 << 21
+    assert qw(L, N=big + 1, K=16, ldw=16) == SHAPE
+    assert pre(L, M=big + 1, K=16, ldx=16) == SHAPE
+    assert pre(L, M=big, K=16384, ldx=16384) == SHAPE            # 2^35 values
+    assert pre(L, M=big, N=big, K=16, ldx=16, ldy=big) == SHAPE  # 2^42 outputs
+    assert dec(L, M=big + 1) == SHAPE
+    assert dec(L, N=big + 1, ldy=big + 1) == SHAPE
+    assert L.pdq_quantize_static(P, 1, big, 16384, 16384, 0.5, 0, P, None, None) == SHAPE
+    assert L.pdq_gemm_per_token(P, P, 4, 64, P, P, None, big + 1, P, big + 1, None, None) == SHAPE
+    assert L.pdq_skinny_channels(big + 1, 16) == -1

@@ -23,7 +23,15 @@ using namespace pdq;
 namespace {
 
 constexpr int64_t kMaxK = 65536;        // |sum_k (q_x - Z) q_w| < 255 * 127 * K stays in int32
-constexpr int64_t kMaxDim = 0x7fffffff;  // M, N are ints on the device
+// Rows of any operand (M activation rows, N weight rows = output channels).
+// Together with the two products below this keeps every launch grid inside
+// the dispatch limits with room to spare: the skinny GEMM's second grid
+// dimension is rows / 64, the per-token quantizers run 256 threads per row,
+// the static quantizer one thread per 8 values, the tiled GEMM 256 threads
+// per 256 x 256 output tile.
+constexpr int64_t kMaxRows = int64_t(1) << 21;
+constexpr int64_t kMaxValues = int64_t(1) << 34;   // M x K of one operand
+constexpr int64_t kMaxOutputs = int64_t(1) << 39;  // M x N of one product
 // Which kernel runs an M x N INT8 GEMM, whichever quantization scheme
 // produced the codes: the skinny (weight-streaming) kernel of decode.hip or
 // the 256 x 256-tile GEMM.  The skinny kernel's work is ceil(N / 16) x
@@ -48,7 +56,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Shape rules shared by every K-wide operand.  K == 0 is refused: the kernels
 // read at least one 16-value chunk of every row they touch.
 pdq_status check_mk(int64_t M, int64_t K, int64_t ld) {
-    if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxK || K % 16 != 0) return PDQ_ERR_SHAPE;
+    if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK || K % 16 != 0) return PDQ_ERR_SHAPE;
+    if (M * K > kMaxValues) return PDQ_ERR_SHAPE;
     if (ld < K || ld < 0) return PDQ_ERR_SHAPE;
     return PDQ_OK;
 }
@@ -113,7 +122,7 @@ pdq_status check_int8_outlier(const void* x, pdq_dtype dt, int64_t M, int64_t K,
     if (dt != PDQ_F16 && dt != PDQ_BF16) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N || ldw < K) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N || ldw < K) return PDQ_ERR_SHAPE;
     if (max_outliers < 0 || max_outliers > K) return PDQ_ERR_SHAPE;
     if (isnan(threshold)) return PDQ_ERR_UNSUPPORTED;
     if (!n_outlier || (max_outliers > 0 && !outlier_idx)) return PDQ_ERR_NULL;
@@ -217,7 +226,7 @@ int pdq_gemm_kernel(int64_t M, int64_t N) {
 }
 
 int pdq_skinny_channels(int64_t M, int64_t N) {
-    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return -1;
+    if (M < 1 || N < 1 || M > kMaxRows || N > kMaxRows) return -1;
     return 16 * decode_groups(M, N);
 }
 
@@ -279,7 +288,7 @@ pdq_status pdq_gemm_per_token(const int8_t* xq, const float* x_scale, int64_t M,
                               uint16_t* y, int64_t ldy, int32_t* acc_out, void* stream) {
     PDQ_TRY(check_operand(xq, 1, M, K, K));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (N > 0 && !w_scale) return PDQ_ERR_NULL;
     if (M > 0 && !x_scale) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
@@ -326,7 +335,7 @@ pdq_status pdq_linear_prefill(const void* x, pdq_dtype x_dt, int64_t M, int64_t 
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (N > 0 && !w_scale) return PDQ_ERR_NULL;
     if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
@@ -359,7 +368,7 @@ pdq_status pdq_linear_prefill_silu_mul(const void* gate, const void* up, pdq_dty
     PDQ_TRY(check_operand(gate, 2, M, K, ldg));
     PDQ_TRY(check_operand(up, 2, M, K, ldu));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (N > 0 && !w_scale) return PDQ_ERR_NULL;
     if (M > 0 && ((K > 0 && !xq) || !x_scale)) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
@@ -387,7 +396,7 @@ pdq_status pdq_gemm_per_token_asym(const int8_t* xq, const float* x_scale, const
                                    int64_t ldy, int32_t* acc_out, void* stream) {
     PDQ_TRY(check_operand(xq, 1, M, K, K));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
     if (M > 0 && (!x_scale || !x_zp)) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
@@ -438,7 +447,7 @@ pdq_status pdq_linear_prefill_asym(const void* x, pdq_dtype x_dt, int64_t M, int
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
     if (M > 0 && ((K > 0 && !xq) || !x_scale || !x_zp)) return PDQ_ERR_NULL;
     if (M > 0 && N > 0 && !y) return PDQ_ERR_NULL;
@@ -471,7 +480,7 @@ pdq_status pdq_gemm_static(const int8_t* xq, int64_t M, int64_t K, float a_scale
                            void* stream) {
     PDQ_TRY(check_operand(xq, 1, M, K, K));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
         return PDQ_ERR_UNSUPPORTED;
     if (N > 0 && (!w_scale || (a_zp != 0 && !w_colsum))) return PDQ_ERR_NULL;
@@ -548,7 +557,7 @@ pdq_status pdq_linear_static_sym(const void* x, pdq_dtype x_dt, int64_t M, int64
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (!(a_scale > 0.0f) || !isfinite(a_scale)) return PDQ_ERR_UNSUPPORTED;
     if (N > 0 && !w_scale) return PDQ_ERR_NULL;
     if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
@@ -616,7 +625,7 @@ pdq_status pdq_linear_zeropoint(const void* x, pdq_dtype x_dt, int64_t M, int64_
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -127 || a_zp > 127) return PDQ_ERR_UNSUPPORTED;
     if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
     if (M > 0 && K > 0 && !xq) return PDQ_ERR_NULL;
@@ -659,7 +668,7 @@ pdq_status pdq_linear_decode(const void* x, pdq_dtype x_dt, int64_t M, int64_t K
     if (!dtype_ok(x_dt)) return PDQ_ERR_DTYPE;
     PDQ_TRY(check_operand(x, elem_bytes(x_dt), M, K, ldx));
     PDQ_TRY(check_operand(wq, 1, N, K, K));
-    if (N < 0 || N > kMaxDim || ldy < N) return PDQ_ERR_SHAPE;
+    if (N < 0 || N > kMaxRows || M * N > kMaxOutputs || ldy < N) return PDQ_ERR_SHAPE;
     if (!(a_scale > 0.0f) || !isfinite(a_scale) || a_zp < -128 || a_zp > 127)
         return PDQ_ERR_UNSUPPORTED;
     if (N > 0 && (!w_scale || !w_colsum)) return PDQ_ERR_NULL;
