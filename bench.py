@@ -289,6 +289,13 @@ def bench_prefill(args, torch, pdq, synth):
     torch.cuda.synchronize()
     time.sleep(1.5)
     ms_step_cold = timed(step, args.steps, args.warmup, stream)
+    # one untimed call with the INT32 accumulators: its outputs, on the host,
+    # for the CPU-baseline leg to compare with the oracle's same linear
+    chk = pdq.linear_prefill(x, wq0, ws, want_acc=True)
+    torch.cuda.synchronize()
+    gpu_out = dict(xq=chk["xq"].unpack(), x_scale=chk["x_scale"].cpu().numpy(), acc=chk["acc"].cpu().numpy(),
+                   y=chk["y"].cpu().view(torch.int16).numpy().view(np.uint16))
+    del chk
     ops = 2.0 * M * N * K
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     gemm_bytes = M * K + N * K + 4 * (M + N) + 2 * M * N  # xq, wq, scales, bf16 y
@@ -299,7 +306,7 @@ def bench_prefill(args, torch, pdq, synth):
                 ms_step_asym=ms_step_asym, ms_quant_asym=ms_quant_asym, ms_gemm_asym=ms_gemm_asym,
                 ms_lib=ms_lib,
                 gemm_tops=gemm_tops, gemm_bytes=gemm_bytes, quant_bytes=quant_bytes,
-                x_host=x_host, w_host=w_host)
+                x_host=x_host, w_host=w_host, gpu_out=gpu_out)
 
 
 def bench_decode(args, torch, pdq, synth):
@@ -329,15 +336,19 @@ def bench_decode(args, torch, pdq, synth):
     wqs = [wq0] + [wq0.clone() for _ in range(nrot - 1)]
     stream = torch.cuda.current_stream()
     res = {}
+    gpu_out = {}  # host copies of each batch's first call, for the CPU-baseline leg's parity check
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     for m in c.batches:
         x = torch.from_numpy(c.x(m)).to(torch.bfloat16).cuda()
         xq = torch.empty(pdq.act_bytes(m, K), dtype=torch.int8, device="cuda")  # packed codes
         y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
         sat.zero_()
-        pdq.linear_decode(x, s, z, wq0, ws, cs, sat_count=sat, out=y, xq=xq)
+        first = pdq.linear_decode(x, s, z, wq0, ws, cs, sat_count=sat, out=y, xq=xq, want_acc=True)
         torch.cuda.synchronize()
         nsat = int(sat.item())
+        gpu_out[str(m)] = dict(xq=pdq.Codes(xq, m, K).unpack(), acc=first["acc"].cpu().numpy(),
+                               y=y.cpu().view(torch.int16).numpy().view(np.uint16), sat=nsat)
+        del first
 
         def call(i):
             pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, m, K, K, s, z, pdq._p(wqs[i % nrot]),
@@ -393,7 +404,8 @@ def bench_decode(args, torch, pdq, synth):
     cs_cg = {str(m): cs_cg_point(torch, pdq, m, x_all, s, z, wqs, ws, cs, 16, 10 if m <= 256 else 4)
              for m in CS_CG_M}
     del wqs, x_all
-    return dict(S=s, Z=z, S_sym=s_sym, S_zp=s_zp, Z_zp=z_zp, K=K, N=N, per_batch=res, cs_cg=cs_cg)
+    return dict(S=s, Z=z, S_sym=s_sym, S_zp=s_zp, Z_zp=z_zp, K=K, N=N, per_batch=res, cs_cg=cs_cg,
+                gpu_out=gpu_out)
 
 
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
@@ -671,6 +683,31 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _parity(O, g, ref):
+    """The GPU's outputs of one call (host copies) against the oracle's result
+    for the same inputs: mismatch counts of the codes, scales, accumulators,
+    saturation count and bf16 bits, and the bf16 output's error against the
+    oracle's binary32 dequant (max relative error with the denominator floored
+    at 1e-3 max|y|; mean absolute error against that value rounded to bf16)."""
+    y32 = ref["y32"].astype(np.float64)
+    ref_bits = O.to_bf16_bits(ref["y32"])
+    got = O.bf16_bits_to_f32(g["y"]).astype(np.float64)
+    floor = 1e-3 * max(float(np.abs(y32).max()), 1e-30)
+    rel = float((np.abs(got - y32) / np.maximum(np.abs(y32), floor)).max())
+    mae = float(np.mean(np.abs(got - O.bf16_bits_to_f32(ref_bits).astype(np.float64))))
+    out = {"outputs": int(y32.size),
+           "code_mismatches": int(np.count_nonzero(g["xq"] != ref["xq"])),
+           "acc_mismatches": int(np.count_nonzero(g["acc"] != ref["acc"])),
+           "y_bits_mismatches": int(np.count_nonzero(g["y"] != ref_bits)),
+           "y_max_rel_err": rel, "y_mae": mae}
+    if "x_scale" in g:
+        out["scale_mismatches"] = int(np.count_nonzero(g["x_scale"].view(np.uint32) !=
+                                                       ref["x_scale"].view(np.uint32)))
+    if "sat" in g:
+        out["saturation_count_equal"] = bool(g["sat"] == ref["sat"])
+    return out
+
+
 def cpu_baseline(pre, synth, llm_host=None, dec=None):
     """The oracle (plain numpy, binary64 BLAS for the exact integer products)
     timed on this host's cores: whole prefill linears (the headline workload,
@@ -697,12 +734,16 @@ def cpu_baseline(pre, synth, llm_host=None, dec=None):
     # whole prefill linears, repeated until about 6 s (at least 2 runs)
     runs, t0 = 0, clock()
     while True:
-        O.linear_prefill(x, wq, sw)
+        ref = O.linear_prefill(x, wq, sw)
         runs += 1
         dt = clock() - t0
         if (dt >= 6.0 and runs >= 2) or runs >= 30:
             break
     out["value"] = pre["ops"] * runs / dt / 1e12
+    parity = {}
+    if pre.get("gpu_out") is not None:
+        parity["prefill"] = _parity(O, pre["gpu_out"], ref)
+    del ref
     out["sample"] = (f"{runs} full prefill linears {M}x{K}->{N} (per-token quant, exact integer GEMM via a "
                      f"binary64 BLAS product, binary32 epilogue) in {dt:.1f} s")
     # the same linear stage by stage
@@ -737,14 +778,19 @@ def cpu_baseline(pre, synth, llm_host=None, dec=None):
         xm = c.x(m)
         reps, t0 = 0, clock()
         while True:
-            O.linear_decode(xm, np.float32(s_dec), z_dec, wqd, swd, csd)
+            dref = O.linear_decode(xm, np.float32(s_dec), z_dec, wqd, swd, csd)
             reps += 1
             if clock() - t0 >= 0.5 and reps >= 3:
                 break
         us = (clock() - t0) / reps * 1e6
         nbytes = c.N * c.K + 2 * m * c.K + 2 * m * c.N + 8 * c.N
         dec_out[str(m)] = {"us_call": round(us, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 3)}
+        g = (dec or {}).get("gpu_out", {}).get(str(m))
+        if g is not None:
+            parity.setdefault("decode", {})[str(m)] = _parity(O, g, dref)
     out["decode"] = dec_out
+    if parity:
+        out["parity"] = parity
     # the LLM.int8() layer: outlier detection, then the whole decomposition
     if llm_host is not None:
         x8, w8, thr = llm_host
