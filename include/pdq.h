@@ -73,13 +73,22 @@ typedef enum {
     PDQ_ERR_ALIGN = 4,       /* pointer or row pitch not 16-byte aligned        */
     PDQ_ERR_UNSUPPORTED = 5, /* value out of range (scale, zero point, ...)     */
     PDQ_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required         */
-    PDQ_ERR_HIP = 8          /* the HIP runtime reported a launch error         */
+    PDQ_ERR_HIP = 8,         /* the HIP runtime reported a launch error         */
+    /* range sentinels, never returned: every 32-bit value is a valid value of
+       the type, so an unknown code passed to pdq_status_string is defined */
+    PDQ_STATUS_MIN_ENUM_ = -0x7fffffff - 1,
+    PDQ_STATUS_MAX_ENUM_ = 0x7fffffff
 } pdq_status;
 
 typedef enum {
     PDQ_F32 = 0,  /* IEEE binary32                */
     PDQ_BF16 = 1, /* bfloat16 (upper half of f32) */
-    PDQ_F16 = 2   /* IEEE binary16                */
+    PDQ_F16 = 2,  /* IEEE binary16                */
+    /* range sentinels, not dtypes: any 32-bit value a caller passes is a
+       valid value of the type, and anything but the three above is refused
+       with PDQ_ERR_DTYPE */
+    PDQ_DTYPE_MIN_ENUM_ = -0x7fffffff - 1,
+    PDQ_DTYPE_MAX_ENUM_ = 0x7fffffff
 } pdq_dtype;
 
 /* Human-readable name of a status code (static string; never NULL). */

@@ -203,14 +203,16 @@ const char* pdq_status_string(pdq_status s) {
     switch (s) {
         case PDQ_OK: return "ok";
         case PDQ_ERR_NULL: return "required pointer is NULL";
-        case PDQ_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 16 up to 65536, or ld too small)";
+        case PDQ_ERR_SHAPE:
+            return "invalid shape (negative or too large size, K not a positive multiple of 16 up to 65536, or ld "
+                   "too small)";
         case PDQ_ERR_DTYPE: return "dtype not accepted by this entry point";
         case PDQ_ERR_ALIGN: return "pointer or row pitch not 16-byte aligned";
         case PDQ_ERR_UNSUPPORTED: return "argument value out of range";
         case PDQ_ERR_WORKSPACE: return "workspace missing or too small";
         case PDQ_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";  // any other value, the range sentinels included
     }
-    return "unknown status";
 }
 
 size_t pdq_weight_bytes(int64_t N, int64_t K) {
