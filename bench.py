@@ -667,8 +667,18 @@ def bench_llm_int8(args, torch, pdq, synth):
     ms = timed(call, args.steps, args.warmup, stream)
     n_out = int(cnt.item())
     ops = 2.0 * M * N * K
+    # one untimed call with the INT32 accumulators: its outputs, on the host,
+    # for the CPU-baseline leg to compare with the oracle's same layer
+    chk = pdq.linear_int8_outlier(x, c.threshold, wq0, ws, w16, max_outliers=max_out, want_acc=True,
+                                  workspace=work)
+    torch.cuda.synchronize()
+    n_chk = int(chk["count"].item())
+    gpu_out = dict(idx=chk["idx"][:min(n_chk, max_out)].cpu().numpy(), count=n_chk, xq=chk["xq"].unpack(),
+                   x_scale=chk["x_scale"].cpu().numpy(), acc=chk["acc"].cpu().numpy(),
+                   y=chk["y"].cpu().view(torch.int16).numpy().view(np.uint16))
+    del chk
     return dict(M=M, K=K, N=N, ms=ms, n_outlier=n_out, int8_tops=ops / (ms * 1e-3) / 1e12,
-                host=(x_host, w_host, c.threshold),
+                host=(x_host, w_host, c.threshold, gpu_out),
                 side_flops=2.0 * M * N * n_out)
 
 
@@ -706,6 +716,25 @@ def _parity(O, g, ref):
     if "sat" in g:
         out["saturation_count_equal"] = bool(g["sat"] == ref["sat"])
     return out
+
+
+def _parity_llm_int8(O, g, ref):
+    """The GPU's LLM.int8() outputs against the oracle's: the outlier columns,
+    codes, scales and INT32 accumulators exactly; the f16 output (whose
+    16-bit side product the oracle sums in binary64) by its max relative error
+    (denominator floored at 1e-3 max|y|) and its MAE against the oracle's
+    binary64 value rounded to f16."""
+    y64 = ref["y64"]
+    got = g["y"].view(np.float16).astype(np.float64)
+    floor = 1e-3 * max(float(np.abs(y64).max()), 1e-30)
+    rel = float((np.abs(got - y64) / np.maximum(np.abs(y64), floor)).max())
+    mae = float(np.mean(np.abs(got - O.to_f16(y64).astype(np.float64))))
+    return {"outputs": int(y64.size), "outlier_columns_equal": bool(g["count"] == len(ref["cols"]) and
+                                                                    np.array_equal(g["idx"], ref["cols"])),
+            "code_mismatches": int(np.count_nonzero(g["xq"] != ref["xq"])),
+            "scale_mismatches": int(np.count_nonzero(g["x_scale"].view(np.uint32) != ref["x_scale"].view(np.uint32))),
+            "acc_mismatches": int(np.count_nonzero(g["acc"] != ref["acc"])),
+            "y_max_rel_err": rel, "y_mae": mae}
 
 
 def cpu_baseline(pre, synth, llm_host=None, dec=None):
@@ -789,18 +818,19 @@ def cpu_baseline(pre, synth, llm_host=None, dec=None):
         if g is not None:
             parity.setdefault("decode", {})[str(m)] = _parity(O, g, dref)
     out["decode"] = dec_out
-    if parity:
-        out["parity"] = parity
     # the LLM.int8() layer: outlier detection, then the whole decomposition
     if llm_host is not None:
-        x8, w8, thr = llm_host
+        x8, w8, thr, g8 = llm_host
         wq8, sw8, _ = O.quantize_weight(w8)
         t0 = clock()
         O.outlier_columns(x8, thr)
         t_det = clock() - t0
         t0 = clock()
-        O.linear_int8_outlier(x8, w8, wq8, sw8, thr)
+        ref8 = O.linear_int8_outlier(x8, w8, wq8, sw8, thr)
         t_l = clock() - t0
+        if g8 is not None:
+            parity["llm_int8"] = _parity_llm_int8(O, g8, ref8)
+        del ref8
         ops8 = 2.0 * x8.shape[0] * w8.shape[0] * x8.shape[1]
         out["llm_int8"] = {"s": round(t_l, 3), "int8_TOPS": round(ops8 / t_l / 1e12, 4),
                            "outlier_detection_s": round(t_det, 4)}
@@ -826,6 +856,8 @@ def cpu_baseline(pre, synth, llm_host=None, dec=None):
         out["one_thread"] = {"tiny_prefill_us": round(t_tp * 1e6, 1), "tiny_decode_us": round(t_td * 1e6, 1),
                              "decode_m1_us": round(t_d1 * 1e6, 1),
                              "decode_m1_GBps": round((c.N * c.K + 2 * c.K + 2 * c.N + 8 * c.N) / t_d1 / 1e9, 3)}
+    if parity:
+        out["parity"] = parity
     return out
 
 
