@@ -167,7 +167,7 @@ def quantize_static(x, s, z, qmin=QMIN_ASYM):
     on out-of-distribution inputs, so the count of values whose unclamped
     code r' = rne(x/S) + Z falls outside [-128, 127] is returned.  The float
     quotient is limited to +-512 before conversion to an integer; this
-    changes neither the clamped code nor the saturation verdict.  qmin =
+    changes neither the clamped code nor the saturation flag.  qmin =
     -127 gives the narrow range [-127, 127] of the zero-point grid below.
     """
     x = _f32(x)

@@ -6,7 +6,7 @@ point) with both sanitizers on the host pass only (device code unchanged and
 never run here), links it with the library's other objects into a temporary
 library, and runs the ABI validation tests (tests/test_abi.py) against it in
 a child process with the sanitizer runtime preloaded.  Any report stops that
-process, so the child's exit status is the verdict.
+process, so the child's exit status is the outcome.
 """
 import glob
 import os
