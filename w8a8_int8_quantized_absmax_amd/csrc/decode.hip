@@ -57,9 +57,10 @@ constexpr int kCUs = 256;   // compute units of an MI355X
 
 // Epilogue operands of this lane's four outputs n = n0 + 4 (lane / 16) + r
 // (16x16 accumulator layout: register r is row 4 (lane / 16) + r, the weight
-// row n).  Loaded unconditionally: columns past N are clamped, a missing bias
-// or code sum (per-token scales, no zero point) reads the scales and is
-// ignored.
+// row n).  Loaded unconditionally: one 16-byte load per array where the four
+// channels are inside N and the arrays 16-byte aligned, else element by
+// element with columns past N clamped; a missing bias or code sum (per-token
+// scales, no zero point) reads the scales and is ignored.
 struct EpiOps {
     float sw[4], bias[4];
     int32_t cs[4];
@@ -69,12 +70,27 @@ __device__ __forceinline__ EpiOps load_epi(const DecodeArgs& a, int n0, int lane
     EpiOps e;
     const float* bp = a.bias ? a.bias : a.sw;
     const int32_t* cp = a.colsum ? a.colsum : reinterpret_cast<const int32_t*>(a.sw);
+    const int nb = n0 + 4 * (lane >> 4);
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a.sw) | reinterpret_cast<uintptr_t>(bp) |
+                         reinterpret_cast<uintptr_t>(cp);
+    if (nb + 3 < a.N && (al & 15) == 0) {
+        const v4i s4 = *reinterpret_cast<const v4i*>(a.sw + nb);
+        const v4i c4 = *reinterpret_cast<const v4i*>(cp + nb);
+        const v4i b4 = *reinterpret_cast<const v4i*>(bp + nb);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int n = min(n0 + 4 * (lane >> 4) + r, a.N - 1);
-        e.sw[r] = a.sw[n];
-        e.cs[r] = cp[n];
-        e.bias[r] = bp[n];
+        for (int r = 0; r < 4; ++r) {
+            e.sw[r] = __int_as_float(s4[r]);
+            e.cs[r] = c4[r];
+            e.bias[r] = __int_as_float(b4[r]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int n = min(nb + r, a.N - 1);
+            e.sw[r] = a.sw[n];
+            e.cs[r] = cp[n];
+            e.bias[r] = bp[n];
+        }
     }
     return e;
 }
@@ -87,6 +103,9 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
                                                  const EpiOps (&e)[NG], int n0, int mbase,
                                                  v4i (&red)[4][NG * NMB][64]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // vector stores need 8-byte aligned y row pieces (16-byte for acc)
+    const bool y_vec = (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 && a.ldy % 4 == 0;
+    const bool acc_vec = (reinterpret_cast<uintptr_t>(a.acc_out) & 15) == 0 && a.N % 4 == 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -100,21 +119,35 @@ __device__ __forceinline__ void reduce_and_store(const DecodeArgs& a, const v4i 
         const v4i tot = red[0][blk][lane] + red[1][blk][lane] + red[2][blk][lane] + red[3][blk][lane];
         const int m = mbase + mb * 16 + (lane & 15);
         if (m >= a.M) continue;
+        // this lane's outputs: row m, the 4 consecutive channels nb .. nb + 3
+        const int nb = n0 + 16 * g + 4 * (lane >> 4);
+        float y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int n = n0 + 16 * g + 4 * (lane >> 4) + r;
-            if (n < a.N) {
-                const int raw = tot[r];
-                if (a.acc_out) a.acc_out[(size_t)m * a.N + n] = raw;
-                // per-token: (S_x[m] * S_w[n]) * (acc [- Z_x[m] colsum[n]]);
-                // static: (S * S_w[n]) * (acc - Z colsum[n])
-                const int corr = a.za ? raw - a.za[m] * e[g].cs[r] : (a.sa ? raw : raw - a.z * e[g].cs[r]);
-                const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e[g].sw[r]);
-                float y = __fmul_rn(t, (float)corr);
-                if (a.bias) y = __fadd_rn(y, e[g].bias[r]);
-                a.y[(size_t)m * a.ldy + n] = f32_to_bf16(y);
-            }
+            const int raw = tot[r];
+            // per-token: (S_x[m] * S_w[n]) * (acc [- Z_x[m] colsum[n]]);
+            // static: (S * S_w[n]) * (acc - Z colsum[n])
+            const int corr = a.za ? raw - a.za[m] * e[g].cs[r] : (a.sa ? raw : raw - a.z * e[g].cs[r]);
+            const float t = __fmul_rn(a.sa ? a.sa[m] : a.s, e[g].sw[r]);
+            y[r] = __fmul_rn(t, (float)corr);
+            if (a.bias) y[r] = __fadd_rn(y[r], e[g].bias[r]);
         }
+        // One store per lane and output (8 bytes of y, 16 of acc) where the row
+        // piece is aligned and inside N: four 2-byte stores per lane made the
+        // stores the longest part of the kernel's tail.
+        const bool whole = nb + 3 < a.N;
+        if (a.acc_out) {
+            int32_t* ap = a.acc_out + (size_t)m * a.N + nb;
+            if (whole && acc_vec)
+                *reinterpret_cast<v4i*>(ap) = tot;
+            else
+                for (int r = 0; r < 4 && nb + r < a.N; ++r) ap[r] = tot[r];
+        }
+        uint16_t* yp = a.y + (size_t)m * a.ldy + nb;
+        if (whole && y_vec)
+            *reinterpret_cast<uint2*>(yp) = make_uint2(f32x2_to_16<kBF16>(y[0], y[1]), f32x2_to_16<kBF16>(y[2], y[3]));
+        else
+            for (int r = 0; r < 4 && nb + r < a.N; ++r) yp[r] = f32_to_bf16(y[r]);
     }
 }
 
