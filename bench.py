@@ -408,6 +408,60 @@ def bench_decode(args, torch, pdq, synth):
                 gpu_out=gpu_out)
 
 
+DECODE_SWEEP_N = (4096, 16384, 65536, 131072)  # K = 4096: 16.8 .. 537 MB of INT8 weight
+
+
+def bench_decode_weights(args, torch, pdq, synth, s, z):
+    """The static decode linear at M = 1 (the one-launch call, and the GEMV on
+    its codes) for INT8 weights of 16.8 to 537 MB (K = 4096, N = 4096 ..
+    131072), with the calibrated S and Z of the decode workload: HIP-graph
+    replays over weight copies rotated through at least 1 GB, so that every
+    call streams its weight from HBM.  Weights N(0, 0.02) drawn on the device
+    from a seeded generator (the host generator would take seconds at this
+    size); the activation row is the decode recipe's."""
+    c = synth.Decode()
+    K = c.K
+    x = torch.from_numpy(c.x(1)).to(torch.bfloat16).cuda()
+    xq = torch.empty(pdq.act_bytes(1, K), dtype=torch.int8, device="cuda")
+    pdq.quantize_static(x, s, z, xq=xq)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(901)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for n in DECODE_SWEEP_N:
+        w = (torch.randn((n, K), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        wq0, ws, cs = pdq.quantize_weight(w)
+        del w
+        copies = max(2, -(-(1 << 30) // wq0.numel()))
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        y = torch.empty((1, n), dtype=torch.bfloat16, device="cuda")
+
+        def call(i):
+            pdq._call("pdq_linear_decode", pdq._p(x), pdq.BF16, 1, K, K, s, z, pdq._p(wqs[i % copies]),
+                      pdq._p(ws), pdq._p(cs), None, n, pdq._p(xq), pdq._p(y), n, None, None, pdq._stream(x.device))
+
+        def gemv(i):
+            pdq._call("pdq_gemm_static", pdq._p(xq), 1, K, s, z, pdq._p(wqs[i % copies]), pdq._p(ws), pdq._p(cs),
+                      None, n, pdq._p(y), n, None, pdq._stream(x.device))
+
+        replays = max(10, 256 // copies)
+        settle(call, stream)
+        ms_call = graph_timed(call, copies, replays, stream)
+        ms_gemv = graph_timed(gemv, copies, replays, stream)
+        call_bytes = n * K + 2 * K + 2 * n + 8 * n
+        gemv_bytes = n * K + K + 2 * n + 8 * n
+        res[str(n)] = dict(weight_MB=round(n * K / 1e6, 1), copies=copies,
+                           us_call=round(ms_call * 1e3, 2),
+                           call_GBps=round(call_bytes / (ms_call * 1e-3) / 1e9, 1),
+                           call_frac=round(call_bytes / (ms_call * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           us_gemv=round(ms_gemv * 1e3, 2),
+                           gemv_GBps=round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
+                           gemv_frac=round(gemv_bytes / (ms_gemv * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        del wqs, wq0, ws, cs, y
+        torch.cuda.empty_cache()
+    return res
+
+
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
 
 
@@ -970,7 +1024,7 @@ def main():
         log(f"[prefill] hipBLASLt INT8 GEMM (torch._int_mm, INT32 out) {pre['ms_lib']*1e3:.1f} us")
     log(f"[prefill asym] step {pre['ms_step_asym']*1e3:.1f} us (quant {pre['ms_quant_asym']*1e3:.1f} us, "
         f"GEMM {pre['ms_gemm_asym']*1e3:.1f} us)")
-    dec = llm = blk = smq = None
+    dec = llm = blk = smq = dws = None
     if args.only == "all":
         dec = bench_decode(args, torch, pdq, synth)
         for m, r in dec["per_batch"].items():
@@ -979,6 +1033,11 @@ def main():
                 f"({r['call_graph_GBps']:.0f} GB/s), GEMV {r['us_gemv_graph']:.2f} us "
                 f"({r['gemv_graph_GBps']:.0f} GB/s); saturated {r['saturated']}; static symmetric call "
                 f"{r['us_call_static_sym_graph']:.2f} us, zero-point call {r['us_call_zeropoint_graph']:.2f} us")
+        dws = bench_decode_weights(args, torch, pdq, synth, dec["S"], dec["Z"])
+        for n, r in dws.items():
+            log(f"[decode M=1, 4096 -> {n}, {r['weight_MB']} MB] call {r['us_call']:.2f} us = "
+                f"{r['call_GBps']:.0f} GB/s ({100 * r['call_frac']:.1f}%), GEMV {r['us_gemv']:.2f} us = "
+                f"{r['gemv_GBps']:.0f} GB/s ({100 * r['gemv_frac']:.1f}%)")
         llm = bench_llm_int8(args, torch, pdq, synth)
         log(f"[llm.int8] {llm['ms']*1e3:.1f} us, {llm['int8_tops']:.0f} TOPS, |O|={llm['n_outlier']}")
         blk = bench_block(args, torch, pdq, synth)
@@ -1039,6 +1098,12 @@ def main():
                          "S_zeropoint": dec["S_zp"], "Z_zeropoint": dec["Z_zp"],
                          "per_batch": {m: {k: round(v, 5) if isinstance(v, float) else v
                                            for k, v in r.items()} for m, r in dec["per_batch"].items()}}
+        if dws:
+            out["decode_weight_sweep"] = {
+                "workload": "static decode linear at M = 1, K = 4096, N = 4096 .. 131072 (16.8 .. 537 MB of INT8 "
+                            "weight), HIP-graph replays over copies rotated through >= 1 GB; the one-launch call "
+                            "and the GEMV on its codes",
+                "unit": "GB/s", "peak": PEAK_HBM_GBS, "per_N": dws}
         out["cs_cg"] = {"workload": "decode linear 4096 -> 4096, bf16 activations: quantizer cost C_s and "
                                     "GEMM cost C_g (us, HIP-graph replays over 16 weight copies), per-token "
                                     "dynamic vs per-tensor static",
