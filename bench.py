@@ -736,6 +736,28 @@ def bench_llm_int8(args, torch, pdq, synth):
                 side_flops=2.0 * M * N * n_out)
 
 
+def run_env(torch) -> dict:
+    """Versions and device of the run: PyTorch and its HIP runtime, the GPU's
+    name, architecture and compute units, the library's build (hash of its
+    kernel sources)."""
+    props = torch.cuda.get_device_properties(0)
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "device": props.name,
+           "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+           "memory_GB": round(props.total_memory / 1e9, 1)}
+    try:
+        import glob
+
+        h = hashlib.sha256()
+        for f in sorted(glob.glob(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                               "w8a8_int8_quantized_absmax_amd", "csrc", "*"))):
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+        env["kernel_sources_sha256"] = h.hexdigest()[:16]
+    except OSError:
+        pass
+    return env
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -1073,6 +1095,7 @@ def main():
                      "kernel": "k_gemm_i8 (INT8 MFMA GEMM + bf16 epilogue)",
                      "us_per_launch": round(pre["ms_gemm"] * 1e3, 2),
                      "sclk_during_gemm": pre["sclk"]},
+        "env": run_env(torch),
         "settle": {"ms_before_each_timed_region": SETTLE_MS,
                    "why": "the first ~35 ms of launches after the GPU has idled (input generation on the host) "
                           "run up to 30% slower while the clock ramps up; each timed region is preceded by "
