@@ -74,6 +74,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"libpdq link failed:\n{_quiet(res.stdout + res.stderr)}")
+    # the library must load (every symbol resolved) before it replaces the
+    # previous one: a kernel whose host stub the compiler did not emit only
+    # shows up here (loaded in a child process, which makes no HIP call)
+    chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"], capture_output=True,
+                         text=True)
+    if chk.returncode != 0:
+        raise RuntimeError(f"libpdq does not load:\n{chk.stderr.strip()[-2000:]}")
     os.replace(tmp, LIB)
     return LIB
 

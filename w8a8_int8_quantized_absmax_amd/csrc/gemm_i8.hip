@@ -108,9 +108,9 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 
 // MI: 32-row MFMA blocks per wave.  4: the 256x256 tile.  2: half of it,
 // rows [128 h, 128 h + 128) of the 256-row tile at m0 (h from the tile
-// index), computed by the 4 waves as 2x2 blocks of 64x128; the K tiles move
-// exactly as for the whole tile (same loads, same waits), the MFMAs and the A
-// fragment reads halve.  Used for a last round of at most 128 tiles, so that
+// index), computed by the 4 waves as 2x2 blocks of 64x128; only those 128 A
+// rows of each K tile are loaded (6 loads per wave and K tile instead of 8),
+// and the MFMAs and the A fragment reads halve.  Used for a last round of at most 128 tiles, so that
 // it fills the 256 CUs with half the work each instead of leaving half of
 // them idle.
 template <int OUT, bool SIDE, int ZP, int MI>
@@ -180,25 +180,44 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // Global -> LDS without registers: one global_load_lds_dwordx4 moves 64
     // lanes x 16 bytes into 1 KB of LDS, lane l's 16 bytes at 16 l: one packed
     // block, which already is the swizzled image of its 16 rows.  Wave w fills
-    // rows [64w, 64w + 64) of both the A and the B tile, four 16-row groups
-    // each: 4 + 4 instructions per K tile.  Groups past the last (of A or B)
-    // are clamped onto it: they only feed outputs that are never stored.
-    const int8_t* pa[4];
+    // rows [64w, 64w + 64) of the B tile, four 16-row groups, and of the A tile
+    // the rows the workgroup multiplies: [64w, 64w + 64) of a whole tile (four
+    // groups), [mh + 32w, mh + 32w + 32) of a half tile (two), each at its row
+    // of the 256-row LDS image: 4 + 4 or 2 + 4 instructions per K tile.  Groups
+    // past the last (of A or B) are clamped onto it: they only feed outputs
+    // that are never stored.
+    constexpr int kLA = MI == 4 ? 4 : 2;  // A loads per wave and K tile
+    constexpr int kLoads = kLA + 4;       // loads per wave and K tile
+    const int8_t* pa[4];  // the first kLA used (an array of kLA elements drops the host stubs)
     const int8_t* pb[4];
     const int lastga = (M - 1) / kWGroup, lastgb = (N - 1) / kWGroup;
+    [[maybe_unused]] const int arow0 = mh + wave * 32;  // half tile: this wave's first A row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        pa[i] = a.A + wpack_block(min(m0 / kWGroup + wave * 4 + i, lastga), 0, nkt) + lane * 16;
+        if constexpr (MI == 4)
+            pa[i] = a.A + wpack_block(min(m0 / kWGroup + wave * 4 + i, lastga), 0, nkt) + lane * 16;
+        else if (i < kLA)
+            pa[i] = a.A + wpack_block(min((m0 + arow0) / kWGroup + i, lastga), 0, nkt) + lane * 16;
         pb[i] = a.B + wpack_block(min(n0 / kWGroup + wave * 4 + i, lastgb), 0, nkt) + lane * 16;
     }
-    // Load number `i` (0..7: A groups, then B groups) of K tile kt into `buf`.
+    // Load number `i` (0 .. kLoads - 1: A groups, then B groups) of K tile kt into `buf`.
     auto issue_one = [&](uint8_t* buf, int kt, int i) {
         uint8_t* la = buf + wave * 64 * BK;
-        if (i < 4)
-            __builtin_amdgcn_global_load_lds(pa[i] + (size_t)kt * kWBlock, (lds_ptr_t)(la + i * 16 * BK), 16, 0, 0);
-        else
-            __builtin_amdgcn_global_load_lds(pb[i - 4] + (size_t)kt * kWBlock,
-                                             (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK), 16, 0, 0);
+        if constexpr (MI == 4) {
+            if (i < 4)
+                __builtin_amdgcn_global_load_lds(pa[i] + (size_t)kt * kWBlock, (lds_ptr_t)(la + i * 16 * BK), 16, 0,
+                                                 0);
+            else
+                __builtin_amdgcn_global_load_lds(pb[i - 4] + (size_t)kt * kWBlock,
+                                                 (lds_ptr_t)(la + BM * BK + (i - 4) * 16 * BK), 16, 0, 0);
+        } else {
+            if (i < kLA)
+                __builtin_amdgcn_global_load_lds(pa[i] + (size_t)kt * kWBlock,
+                                                 (lds_ptr_t)(buf + (arow0 + i * 16) * BK), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(pb[i - kLA] + (size_t)kt * kWBlock,
+                                                 (lds_ptr_t)(la + BM * BK + (i - kLA) * 16 * BK), 16, 0, 0);
+        }
     };
     // Fragments of one 32-wide K step: lane l reads row (l%32) of each 32-row
     // block, chunk 2*s + l/32 (16 bytes = 16 K values).
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     // kt+1 have landed, so step 0 of tile kt+1 is read during the remaining 15
     // MFMAs.  One barrier per tile, and no LDS latency exposed between tiles.
     //
-    // Every tile issues exactly 8 loads per wave, also past the last tile
+    // Every tile issues exactly kLoads loads per wave, also past the last tile
     // (those re-load the last tile into a buffer nobody reads again), so the
     // number of loads in flight is the same on every path and each wait below
     // -- and each wait the compiler derives for the LDS reads -- is exact.
@@ -233,12 +252,12 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
     auto issue_tile = [&](uint8_t* buf, int t, int i) { issue_one(buf, min(t, nkt - 1), i); };
     if (nkt > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue_tile(st0, 0, i);
+        for (int i = 0; i < kLoads; ++i) issue_tile(st0, 0, i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue_tile(st1, 1, i);
+        for (int i = 0; i < kLoads; ++i) issue_tile(st1, 1, i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue_tile(st2, 2, i);
-        wait_loads_and_sync<16>();
+        for (int i = 0; i < kLoads; ++i) issue_tile(st2, 2, i);
+        wait_loads_and_sync<2 * kLoads>();
         read_frags(st0, 0, f0a, f0b);
         auto body = [&](auto S, int kt) {
             constexpr int s0 = decltype(S)::value;
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
                     if constexpr (MI == 4) {
                         if (j & 1) issue_tile(sd, next, 2 * i + (j >> 1));
                     } else {
-                        issue_tile(sd, next, 4 * i + j);  // 8 MFMAs, the same 8 loads
+                        if (4 * i + j < kLoads) issue_tile(sd, next, 4 * i + j);  // 8 MFMAs, 6 loads
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
             // Loads issued after tile kt+1's: tiles kt+2 and kt+3.  Also after
             // the last tile (tile kt+1 then re-loads the last one), so that the
             // wait is on every path and the compiler's count stays exact.
-            wait_loads_and_sync<16>();
+            wait_loads_and_sync<2 * kLoads>();
             read_frags(sn, 0, f0a, f0b);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
