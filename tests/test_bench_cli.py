@@ -1,7 +1,9 @@
 """bench.py's parts that hold without a GPU: it measures one GPU and refuses a
 multi-GPU request (an argument or a launcher's WORLD_SIZE) with a message and
-exit status 2, before touching any device; and the parity record of its JSON
-line counts every difference between a run's outputs and the oracle's."""
+exit status 2, before touching any device; the parity record of its JSON
+line counts every difference between a run's outputs and the oracle's; and
+its roofline traffic figure is the committed counter summary of the current
+GEMM source, or null."""
 import os
 import subprocess
 import sys
@@ -83,3 +85,36 @@ def test_parity_record_counts_planted_mismatches():
     g8["acc"][0, 0] += 7
     bad8 = b._parity_llm_int8(O, g8, r8)
     assert not bad8["outlier_columns_equal"] and bad8["acc_mismatches"] == 1
+
+
+def test_traffic_summary_is_for_the_current_gemm_and_adds_up(tmp_path):
+    """roofline.traffic comes from the committed counter summary only while it
+    was taken on the current GEMM source: its bytes are the two counters scaled
+    by the copy-kernel calibration, and any code change to the GEMM source (not
+    a comment) makes the bench line report null instead."""
+    import json
+
+    b = _bench_module()
+    with open(b.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    cal = t["calibration"]
+    # a 1 GiB copy reads and writes 1 GiB: the scales follow from its counters
+    assert cal["fetch_scale"] == round(1048576.0 / cal["copy_FETCH_SIZE_KiB"], 2)
+    assert cal["write_scale"] == round(1048576.0 / cal["copy_WRITE_SIZE_KiB"], 2)
+    fetch = t["FETCH_SIZE_KiB_per_launch"] * 1024 * cal["fetch_scale"]
+    write = t["WRITE_SIZE_KiB_per_launch"] * 1024 * cal["write_scale"]
+    assert (fetch, write) == (t["fetch_bytes_per_launch"], t["write_bytes_per_launch"])
+    assert t["bytes_per_launch"] == fetch + write
+    # the written bytes are the bf16 output of the 4096 x 11008 product
+    assert t["write_bytes_per_launch"] == 4096 * 11008 * 2
+    assert t["bytes_per_launch"] >= t["algorithmic_bytes_per_launch"]
+    assert b.traffic_for(0) == t["bytes_per_launch"], "counters were taken on another GEMM source"
+
+    with open(b.GEMM_SRC) as f:
+        src = f.read()
+    edited = tmp_path / "gemm_i8.hip"
+    edited.write_text(src + "\n// a comment only\n")
+    b.GEMM_SRC = str(edited)
+    assert b.traffic_for(0) == t["bytes_per_launch"]
+    edited.write_text(src + "\nstatic int unused_probe;\n")
+    assert b.traffic_for(0) is None
